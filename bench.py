@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA NF4 linear on one MI355X.
+
+A step is one training step of the frozen-base linear on the Llama-7B-shaped
+q_proj workload: W0 4096 x 4096 stored as NF4 (blocks of 64) with
+double-quantised absmax (8-bit, groups of 256), 2048 tokens (batch 4 x
+sequence 512), LoRA r = 16, alpha = 32: the forward pass (LoRA down
+projection H = X A^T, fused dequant-GEMM with the LoRA epilogue) and the
+backward pass (G and dB from one pass over dY, dA, fused dequant-GEMM for
+dX). Inputs are seeded synthetic tensors already resident in HBM. The weight
+is quantised once before timing (a frozen base is quantised at load time).
+
+Printed: one JSON line with the step throughput in TFLOP/s (algorithmic
+flops 4Mdk + 6Mr(d+k) per step), the roofline of the dominant kernel timed
+with HIP events inside the timed region, the CPU oracle timed on the host,
+and per-row measurements of every other kernel of the path (quantise,
+dequantise, decode-shaped GEMV, merge) on inputs rotated through more than
+the 256 MB last-level cache.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QLoRA linear fwd+bwd TFLOP/s & dequant/GEMV HBM GB/s (% roofline), 1×MI355X"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+D = K = 4096
+M = 2048
+R = 16
+ALPHA = 32.0
+
+
+def step_flops(M, d, k, r):
+    return 4 * M * d * k + 6 * M * r * (d + k)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bit_nf4_quantized_19_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = data.get("kernels", {}).get(kernel)
+    if not e or e.get("source_digest") != digest:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--rows", choices=["on", "off"], default="on")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path runs on a single MI355X "
+              "(the multi-GPU sharding is a design note, not a measured mode).")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from bit_nf4_quantized_19_amd import ops, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops.lib()
+    log(f"[bench] device {torch.cuda.get_device_name(0)}")
+
+    inp = synth.linear_inputs(D, K, M, R, idx=0)
+    W0 = synth.to_device_bf16(inp["W0"], dev)
+    X, A, B, dY = (synth.to_device_bf16(inp[n], dev) for n in ("X", "A", "B", "dY"))
+    w = ops.quantize(W0, double_quant=True)
+    Y = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    H = torch.empty(M, R, dtype=torch.float32, device=dev)
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    dA = torch.empty(R, K, dtype=torch.bfloat16, device=dev)
+    dB = torch.empty(D, R, dtype=torch.bfloat16, device=dev)
+
+    def ws(op):
+        n = ops.workspace_bytes(op, D, K, M, R, True)
+        t = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+        off = (-t.data_ptr()) % 256
+        return t[off:off + n]
+    ws_f, ws_b = ws(ops.OP_FWD), ws(ops.OP_BWD)
+
+    def step():
+        ops.linear_fwd(w, X, A, B, ALPHA, save_h=True, Y=Y, H=H, ws=ws_f)
+        ops.linear_bwd(w, X, A, B, ALPHA, dY, H=H, dX=dX, dA=dA, dB=dB, ws=ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+    ops.profile_begin(64 * max(1, args.steps))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ops.profile_end()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    flops = step_flops(M, D, K, R)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    log(f"[bench] {ms_step:.3f} ms/step, {tflops:.1f} TFLOP/s")
+
+    kern = {}
+    for name in ops.KERNELS:
+        cnt, tot = ops.profile_query(name)
+        if cnt:
+            kern[name] = {"launches": cnt, "avg_us": 1e3 * tot / cnt}
+    fwd_gemm_flops = 2 * M * D * K + 2 * M * R * D
+    dx_gemm_flops = 2 * M * D * K + 2 * M * R * K
+    cand = [("gemm_fwd", fwd_gemm_flops, "gemm.hip"), ("gemm_dx", dx_gemm_flops, "gemm.hip")]
+    dom = max(cand, key=lambda c: kern.get(c[0], {"avg_us": 0})["avg_us"])
+    avg_s = kern[dom[0]]["avg_us"] * 1e-6
+    achieved = dom[1] / avg_s / 1e12
+    digest = source_digest(dom[2], "common.h")
+    roofline = {"kernel": dom[0], "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for(dom[0], digest),
+                "algorithmic_flops_per_launch": dom[1], "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    rows = measure_rows(ops, synth, torch, dev) if args.rows == "on" else None
+    cpu = cpu_baseline(inp, flops) if args.cpu_baseline == "on" else None
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normal: W0 ~ N(0,0.02), X, dY ~ N(0,1), A, B ~ N(0,0.01))",
+        "config": {"workload": "llama7b_q_proj_nf4_dq_4096x4096_tokens2048_r16_fwd_bwd",
+                   "d": D, "k": K, "tokens": M, "r": R, "lora_alpha": ALPHA,
+                   "blocksize": 64, "double_quant": True, "dq_blocksize": 256,
+                   "parallelism": "single_gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
+        "rows": rows,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _rotated(fn, n_sets, iters):
+    """Average milliseconds of fn(i % n_sets) over iters calls, events on the
+    current stream."""
+    import torch
+    for i in range(n_sets):
+        fn(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(iters):
+        fn(i % n_sets)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def measure_rows(ops, synth, torch, dev):
+    """Per-row measurements (quantise, dequantise, GEMV, merge, fwd, bwd)."""
+    out = {}
+    # quantise / dequantise: 12 distinct 4096x4096 weights (403 MB bf16)
+    nset = 12
+    Ws = [synth.normal_bf16_device((D, K), 0.02, 9000 + i, device=dev) for i in range(nset)]
+    qs = [ops.NF4Weight.empty(D, K, True, dev) for _ in range(nset)]
+    wsq = torch.empty(ops.workspace_bytes(ops.OP_QUANTIZE, D, K, 0, 0, True) + 256,
+                      dtype=torch.uint8, device=dev)
+    off = (-wsq.data_ptr()) % 256
+    wsq = wsq[off:off + ops.workspace_bytes(ops.OP_QUANTIZE, D, K, 0, 0, True)]
+    ops.profile_begin(4096)
+    ms_q = _rotated(lambda i: ops.quantize(Ws[i], True, out=qs[i], ws=wsq), nset, 48)
+    ops.profile_end()
+    c, t = ops.profile_query("quantize")
+    n = D * K
+    qbytes = 2 * n + ops.storage_bytes(D, K, True)
+    out["quantize"] = {"shape": [D, K], "double_quant": True, "ms_call": round(ms_q, 4),
+                       "kernel_us": round(1e3 * t / c, 2),
+                       "GB_s": round(qbytes / (t / c * 1e-3) / 1e9, 1),
+                       "algorithmic_bytes": qbytes}
+    out["quantize"]["frac_hbm"] = round(out["quantize"]["GB_s"] / PEAK_HBM_GBS, 4)
+    outs = [torch.empty(D, K, dtype=torch.bfloat16, device=dev) for _ in range(nset)]
+    ops.profile_begin(4096)
+    ms_d = _rotated(lambda i: ops.dequantize(qs[i], out=outs[i]), nset, 48)
+    ops.profile_end()
+    c, t = ops.profile_query("dequantize")
+    dbytes = ops.storage_bytes(D, K, True) + 2 * n
+    out["dequantize"] = {"shape": [D, K], "kernel_us": round(1e3 * t / c, 2),
+                         "GB_s": round(dbytes / (t / c * 1e-3) / 1e9, 1),
+                         "algorithmic_bytes": dbytes}
+    out["dequantize"]["frac_hbm"] = round(out["dequantize"]["GB_s"] / PEAK_HBM_GBS, 4)
+    # merge (r = 16)
+    Ad = synth.normal_bf16_device((R, K), 0.01, 31, device=dev)
+    Bd = synth.normal_bf16_device((D, R), 0.01, 32, device=dev)
+    ops.profile_begin(4096)
+    _rotated(lambda i: ops.merge(qs[i], Ad, Bd, ALPHA, out=outs[i]), nset, 48)
+    ops.profile_end()
+    c, t = ops.profile_query("merge")
+    mbytes = ops.storage_bytes(D, K, True) + 2 * n + 2 * R * (D + K)
+    out["merge"] = {"shape": [D, K], "r": R, "kernel_us": round(1e3 * t / c, 2),
+                    "GB_s": round(mbytes / (t / c * 1e-3) / 1e9, 1), "algorithmic_bytes": mbytes}
+    out["merge"]["frac_hbm"] = round(out["merge"]["GB_s"] / PEAK_HBM_GBS, 4)
+    del Ws, outs, qs
+    torch.cuda.empty_cache()
+    # decode-shaped GEMV: gate/up 4096 -> 11008 and down 11008 -> 4096, 16
+    # distinct weights each (372 MB of NF4 per shape)
+    out["gemv"] = {}
+    for (d, k) in ((11008, 4096), (4096, 11008)):
+        nset = 16
+        gq = []
+        for i in range(nset):
+            Wt = synth.normal_bf16_device((d, k), 0.02, 9100 + i, device=dev)
+            gq.append(ops.quantize(Wt, True))
+            del Wt
+        Ag = synth.normal_bf16_device((R, k), 0.01, 41, device=dev)
+        Bg = synth.normal_bf16_device((d, R), 0.01, 42, device=dev)
+        for Mt in (1, 4, 16):
+            Xg = synth.normal_bf16_device((Mt, k), 1.0, 43, device=dev)
+            Yg = torch.empty(Mt, d, dtype=torch.bfloat16, device=dev)
+            wsn = ops.workspace_bytes(ops.OP_FWD, d, k, Mt, R, True)
+            wst = torch.empty(wsn + 256, dtype=torch.uint8, device=dev)
+            o2 = (-wst.data_ptr()) % 256
+            wst = wst[o2:o2 + wsn]
+            ops.profile_begin(8192)
+            ms_call = _rotated(lambda i: ops.linear_fwd(gq[i], Xg, Ag, Bg, ALPHA, save_h=False,
+                                                        Y=Yg, ws=wst), nset, 96)
+            ops.profile_end()
+            c, t = ops.profile_query("gemv")
+            gbytes = (ops.storage_bytes(d, k, True) + 2 * R * (d + k) + 2 * Mt * k + 2 * Mt * d)
+            key = f"{d}x{k}_M{Mt}"
+            out["gemv"][key] = {"kernel_us": round(1e3 * t / c, 2), "call_us": round(1e3 * ms_call, 2),
+                                "GB_s_kernel": round(gbytes / (t / c * 1e-3) / 1e9, 1),
+                                "GB_s_call": round(gbytes / (ms_call * 1e-3) / 1e9, 1),
+                                "algorithmic_bytes": gbytes}
+            out["gemv"][key]["frac_hbm_kernel"] = round(out["gemv"][key]["GB_s_kernel"] / PEAK_HBM_GBS, 4)
+            out["gemv"][key]["frac_hbm_call"] = round(out["gemv"][key]["GB_s_call"] / PEAK_HBM_GBS, 4)
+        del gq
+        torch.cuda.empty_cache()
+    log(f"[bench] rows: {json.dumps(out)}")
+    return out
+
+
+def cpu_baseline(inp, flops):
+    """The CPU oracle (as it stands) on the host cores: one full step of the
+    workload (oracle dequantisation of W0 plus float64 forward and backward on
+    all 2048 tokens), median of 3 runs; the quantised record is prepared once,
+    untimed."""
+    import numpy as np
+    from oracle import lora as olora
+    from oracle import nf4 as onf4
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    log(f"[bench] cpu oracle baseline on {cores} threads")
+    qw = onf4.quantize_weight(inp["W0"], True)
+    s = olora.lora_scale(ALPHA, R)
+    widen = lambda b: onf4.bf16_bits_to_f32(b).astype(np.float64)
+    X, A, B, dY = (widen(inp[n]) for n in ("X", "A", "B", "dY"))
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        Wd = widen(onf4.dequantize_weight(qw)).reshape(D, K)
+        Yo, Ho = olora.forward(Wd, X, A, B, s)
+        olora.backward(Wd, X, A, B, s, dY)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": round(flops / t / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": "one full step of the workload (oracle dequantise + float64 forward "
+                      f"and backward, 2048 tokens), median of 3 runs: {t:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

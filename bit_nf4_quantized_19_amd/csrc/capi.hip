@@ -1,0 +1,352 @@
+// C ABI of libqlora_nf4: argument checks, workspace layout and dispatch to
+// the gfx950 kernels. Every check runs on the host before anything is
+// enqueued; no HIP call is made for an invalid argument.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by all entry points.
+qlora_status check_weight_shape(int64_t d, int64_t k) {
+  if (d < 1 || k < 1) return QLORA_ERR_INVALID_ARG;
+  if (k % 64 != 0 || d % 8 != 0) return QLORA_ERR_UNSUPPORTED;
+  if (d > (int64_t(1) << 31) || k > (int64_t(1) << 31)) return QLORA_ERR_UNSUPPORTED;
+  const int64_t n = d * k;
+  if (n / 64 >= (int64_t(1) << 32)) return QLORA_ERR_UNSUPPORTED;
+  return QLORA_OK;
+}
+
+qlora_status check_weight(const qlora_nf4_weight *w, bool need_outputs_only) {
+  (void)need_outputs_only;
+  if (!w) return QLORA_ERR_INVALID_ARG;
+  qlora_status s = check_weight_shape(w->d, w->k);
+  if (s != QLORA_OK) return s;
+  if (w->blocksize != 64) return QLORA_ERR_UNSUPPORTED;
+  if (w->double_quant != 0 && w->double_quant != 1) return QLORA_ERR_INVALID_ARG;
+  if (w->double_quant && w->dq_blocksize != 256) return QLORA_ERR_UNSUPPORTED;
+  if (!w->codes || !aligned16(w->codes)) return QLORA_ERR_INVALID_ARG;
+  if (w->double_quant) {
+    if (!w->absmax_q || !w->absmax_scale || !w->absmax_offset) return QLORA_ERR_INVALID_ARG;
+    if (((uintptr_t)w->absmax_scale & 3u) || ((uintptr_t)w->absmax_offset & 3u))
+      return QLORA_ERR_INVALID_ARG;
+  } else {
+    if (!w->absmax || ((uintptr_t)w->absmax & 3u)) return QLORA_ERR_INVALID_ARG;
+  }
+  return QLORA_OK;
+}
+
+ql::ScaleSrc scale_src(const qlora_nf4_weight *w) {
+  return ql::ScaleSrc{w->absmax, w->absmax_q, w->absmax_scale, w->absmax_offset,
+                      w->double_quant};
+}
+
+// Bump allocator over the caller's workspace (also used to size it).
+struct Carve {
+  char *base;
+  int64_t off = 0;
+  template <class T>
+  T *take(int64_t bytes) {
+    T *p = base ? (T *)(base + off) : nullptr;
+    off += ql_rup(bytes > 0 ? bytes : 0, kAlign);
+    return p;
+  }
+};
+
+struct FwdWs {
+  uint16_t *Ap, *Bp, *Hs_hi, *Hs_lo;
+  float *Hpart, *H, *gpart;
+  int64_t bytes;
+};
+
+FwdWs fwd_layout(char *base, int64_t d, int64_t k, int64_t M, int r) {
+  const int rp = (int)ql_rup(r, 16);
+  Carve c{base};
+  FwdWs L{};
+  L.Ap = (r % 16) ? c.take<uint16_t>((int64_t)rp * k * 2) : nullptr;
+  L.Bp = (r % 16) ? c.take<uint16_t>(d * rp * 2) : nullptr;
+  L.Hpart = c.take<float>((int64_t)skinny_part_bytes(M, k, rp));
+  L.H = c.take<float>(M * rp * 4);
+  if (M > 16) {
+    L.Hs_hi = c.take<uint16_t>(M * rp * 2);
+    L.Hs_lo = c.take<uint16_t>(M * rp * 2);
+    L.gpart = nullptr;
+  } else {
+    L.Hs_hi = L.Hs_lo = nullptr;
+    L.gpart = c.take<float>((int64_t)gemv_part_bytes(d, k, M));
+  }
+  L.bytes = c.off;
+  return L;
+}
+
+struct BwdWs {
+  uint16_t *Ap, *Bt, *At, *Gs_hi, *Gs_lo;
+  float *Hpart, *H, *Gpart, *G, *cpart;
+  int64_t bytes;
+};
+
+BwdWs bwd_layout(char *base, int64_t d, int64_t k, int64_t M, int r, bool need_h, bool need_dx) {
+  const int rp = (int)ql_rup(r, 16);
+  Carve c{base};
+  BwdWs L{};
+  L.Ap = (need_h && (r % 16)) ? c.take<uint16_t>((int64_t)rp * k * 2) : nullptr;
+  L.Hpart = need_h ? c.take<float>((int64_t)skinny_part_bytes(M, k, rp)) : nullptr;
+  L.H = need_h ? c.take<float>(M * rp * 4) : nullptr;
+  L.Bt = c.take<uint16_t>((int64_t)rp * d * 2);
+  L.Gpart = c.take<float>((int64_t)skinny_part_bytes(M, d, rp));
+  L.G = c.take<float>(M * rp * 4);
+  L.Gs_hi = need_dx ? c.take<uint16_t>(M * rp * 2) : nullptr;
+  L.Gs_lo = need_dx ? c.take<uint16_t>(M * rp * 2) : nullptr;
+  L.At = need_dx ? c.take<uint16_t>(k * rp * 2) : nullptr;
+  const int64_t cp = (int64_t)std::max(colacc_part_bytes(M, d, rp), colacc_part_bytes(M, k, rp));
+  L.cpart = c.take<float>(cp);
+  L.bytes = c.off;
+  return L;
+}
+
+bool ws_ok(const void *ws, size_t ws_bytes, int64_t need) {
+  if (need == 0) return true;
+  return ws && (((uintptr_t)ws & (kAlign - 1)) == 0) && (int64_t)ws_bytes >= need;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qlora_status_string(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_INVALID_ARG: return "invalid argument";
+    case QLORA_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case QLORA_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case QLORA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t qlora_nf4_storage_bytes(int64_t d, int64_t k, int32_t double_quant) {
+  if (check_weight_shape(d, k) != QLORA_OK) return 0;
+  const int64_t n = d * k, nb = n / 64;
+  if (!double_quant) return (size_t)(n / 2 + 4 * nb);
+  return (size_t)(n / 2 + nb + 4 * ql_cdiv(nb, 256) + 4);
+}
+
+size_t qlora_workspace_bytes(int32_t op, int64_t d, int64_t k, int64_t M, int32_t r,
+                             int32_t double_quant) {
+  if (check_weight_shape(d, k) != QLORA_OK) return (size_t)-1;
+  if (op == QLORA_OP_QUANTIZE) return quantize_ws_bytes(d * k, double_quant);
+  if (M < 1 || r < 1 || r > 128) return (size_t)-1;
+  if (op == QLORA_OP_FWD) return (size_t)fwd_layout(nullptr, d, k, M, r).bytes;
+  // backward: sized for the largest case (H recomputed, dX requested)
+  if (op == QLORA_OP_BWD) return (size_t)bwd_layout(nullptr, d, k, M, r, true, true).bytes;
+  return (size_t)-1;
+}
+
+qlora_status qlora_nf4_codebook(float levels[16], float thresholds[15]) {
+  if (!levels || !thresholds) return QLORA_ERR_INVALID_ARG;
+  host_codebook(levels, thresholds);
+  return QLORA_OK;
+}
+
+qlora_status qlora_nf4_quantize(const uint16_t *W0, const qlora_nf4_weight *w, void *ws,
+                                size_t ws_bytes, void *stream) {
+  qlora_status s = check_weight(w, true);
+  if (s != QLORA_OK) return s;
+  if (!W0 || !aligned16(W0)) return QLORA_ERR_INVALID_ARG;
+  const int64_t n = w->d * w->k;
+  const int64_t need = (int64_t)quantize_ws_bytes(n, w->double_quant);
+  if (!ws_ok(ws, ws_bytes, need)) return QLORA_ERR_WORKSPACE;
+  return launch_quantize(W0, n, w->codes, w->absmax, w->double_quant, w->absmax_q,
+                         w->absmax_scale, w->absmax_offset, ws, (hipStream_t)stream);
+}
+
+qlora_status qlora_nf4_dequantize(const qlora_nf4_weight *w, uint16_t *W_out, void *stream) {
+  qlora_status s = check_weight(w, false);
+  if (s != QLORA_OK) return s;
+  if (!W_out || !aligned16(W_out)) return QLORA_ERR_INVALID_ARG;
+  return launch_dequantize(w->codes, scale_src(w), w->d * w->k, W_out, (hipStream_t)stream);
+}
+
+static qlora_status check_lora(const uint16_t *A, const uint16_t *B, int32_t r, float alpha) {
+  if (!A || !B || !aligned16(A) || !aligned16(B)) return QLORA_ERR_INVALID_ARG;
+  if (r < 1) return QLORA_ERR_INVALID_ARG;
+  if (r > 128) return QLORA_ERR_UNSUPPORTED;
+  if (!isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+  return QLORA_OK;
+}
+
+qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
+                              const uint16_t *A, const uint16_t *B, int32_t r, float lora_alpha,
+                              uint16_t *Y, float *H_save, void *ws, size_t ws_bytes,
+                              void *stream) {
+  qlora_status s = check_weight(w, false);
+  if (s != QLORA_OK) return s;
+  if ((s = check_lora(A, B, r, lora_alpha)) != QLORA_OK) return s;
+  if (!X || !Y || !aligned16(X) || !aligned16(Y) || M < 1) return QLORA_ERR_INVALID_ARG;
+  if (H_save && ((uintptr_t)H_save & 3u)) return QLORA_ERR_INVALID_ARG;
+  const int64_t d = w->d, k = w->k;
+  const FwdWs need = fwd_layout(nullptr, d, k, M, r);
+  if (!ws_ok(ws, ws_bytes, need.bytes)) return QLORA_ERR_WORKSPACE;
+  const FwdWs L = fwd_layout((char *)ws, d, k, M, r);
+  hipStream_t st = (hipStream_t)stream;
+  const int rp = (int)ql_rup(r, 16);
+  const float sc = lora_alpha / (float)r;
+  const ql::ScaleSrc src = scale_src(w);
+
+  const uint16_t *Ap = A, *Bp = B;
+  if (r % 16) {
+    if ((s = launch_pad_copy(A, r, k, L.Ap, rp, k, 0, st)) != QLORA_OK) return s;
+    if ((s = launch_pad_copy(B, d, r, L.Bp, d, rp, 0, st)) != QLORA_OK) return s;
+    Ap = L.Ap;
+    Bp = L.Bp;
+  }
+  // H = X A^T (float32, M x rp); H_save gets the M x r copy
+  if ((s = launch_skinny(X, M, k, Ap, rp, L.Hpart, L.H, rp, H_save, r, sc, L.Hs_hi, L.Hs_lo,
+                         st)) != QLORA_OK)
+    return s;
+  if (M <= 16)
+    return launch_gemv_fwd(w->codes, src, d, k, X, M, Bp, L.H, rp, sc, L.gpart, Y, st);
+  return launch_gemm_fwd(w->codes, src, d, k, X, M, Bp, L.Hs_hi, L.Hs_lo, rp, Y, st);
+}
+
+qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
+                              const uint16_t *A, const uint16_t *B, int32_t r, float lora_alpha,
+                              const uint16_t *dY, const float *H, uint16_t *dX, uint16_t *dA,
+                              uint16_t *dB, void *ws, size_t ws_bytes, void *stream) {
+  qlora_status s = check_weight(w, false);
+  if (s != QLORA_OK) return s;
+  if ((s = check_lora(A, B, r, lora_alpha)) != QLORA_OK) return s;
+  if (!X || !dY || !dA || !dB || M < 1) return QLORA_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(dA) || !aligned16(dB))
+    return QLORA_ERR_INVALID_ARG;
+  if (dX && !aligned16(dX)) return QLORA_ERR_INVALID_ARG;
+  if (H && ((uintptr_t)H & 3u)) return QLORA_ERR_INVALID_ARG;
+  const int64_t d = w->d, k = w->k;
+  const bool need_h = (H == nullptr) || (r % 16 != 0);
+  const bool need_dx = dX != nullptr;
+  const BwdWs need = bwd_layout(nullptr, d, k, M, r, need_h, need_dx);
+  if (!ws_ok(ws, ws_bytes, need.bytes)) return QLORA_ERR_WORKSPACE;
+  const BwdWs L = bwd_layout((char *)ws, d, k, M, r, need_h, need_dx);
+  hipStream_t st = (hipStream_t)stream;
+  const int rp = (int)ql_rup(r, 16);
+  const float sc = lora_alpha / (float)r;
+
+  const float *Hq = H;  // M x rp
+  if (need_h) {
+    const uint16_t *Ap = A;
+    if (r % 16) {
+      if ((s = launch_pad_copy(A, r, k, L.Ap, rp, k, 0, st)) != QLORA_OK) return s;
+      Ap = L.Ap;
+    }
+    if ((s = launch_skinny(X, M, k, Ap, rp, L.Hpart, L.H, rp, nullptr, 0, sc, nullptr, nullptr,
+                           st)) != QLORA_OK)
+      return s;
+    Hq = L.H;
+  }
+  // G = dY B (float32, M x rp) and s*G as bf16 hi/lo for the dX epilogue
+  if ((s = launch_pad_copy(B, d, r, L.Bt, rp, d, 1, st)) != QLORA_OK) return s;
+  if ((s = launch_skinny(dY, M, d, L.Bt, rp, L.Gpart, L.G, rp, nullptr, 0, sc, L.Gs_hi, L.Gs_lo,
+                         st)) != QLORA_OK)
+    return s;
+  // dB = s dY^T H (d x r) ; dA = s G^T X (r x k)
+  if ((s = launch_colacc(dY, M, d, Hq, rp, r, sc, L.cpart, dB, 0, st)) != QLORA_OK) return s;
+  if ((s = launch_colacc(X, M, k, L.G, rp, r, sc, L.cpart, dA, 1, st)) != QLORA_OK) return s;
+  if (need_dx) {
+    if ((s = launch_pad_copy(A, r, k, L.At, k, rp, 1, st)) != QLORA_OK) return s;
+    if ((s = launch_gemm_dx(w->codes, scale_src(w), d, k, dY, M, L.At, L.Gs_hi, L.Gs_lo, rp, dX,
+                            st)) != QLORA_OK)
+      return s;
+  }
+  return QLORA_OK;
+}
+
+qlora_status qlora_merge(const qlora_nf4_weight *w, const uint16_t *A, const uint16_t *B,
+                         int32_t r, float lora_alpha, uint16_t *W_merged, void *stream) {
+  qlora_status s = check_weight(w, false);
+  if (s != QLORA_OK) return s;
+  if ((s = check_lora(A, B, r, lora_alpha)) != QLORA_OK) return s;
+  if (!W_merged || !aligned16(W_merged)) return QLORA_ERR_INVALID_ARG;
+  const float sc = lora_alpha / (float)r;
+  return launch_merge(w->codes, scale_src(w), w->d, w->k, A, B, r, sc, W_merged,
+                      (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---- kernel timing hooks ------------------------------------------------------
+namespace {
+struct ProfState {
+  bool on = false;
+  int cap = 0, n = 0;
+  hipEvent_t *ev = nullptr;
+  int *kid = nullptr;
+};
+ProfState g_prof;
+}  // namespace
+
+int ql_prof_begin(int kernel_id, hipStream_t st) {
+  if (!g_prof.on || g_prof.n >= g_prof.cap) return -1;
+  const int s = g_prof.n++;
+  g_prof.kid[s] = kernel_id;
+  hipEventRecord(g_prof.ev[2 * s], st);
+  return s;
+}
+
+void ql_prof_end(int slot, hipStream_t st) {
+  if (slot >= 0) hipEventRecord(g_prof.ev[2 * slot + 1], st);
+}
+
+extern "C" {
+
+qlora_status qlora_profile_release(void) {
+  for (int i = 0; i < 2 * g_prof.cap; ++i) hipEventDestroy(g_prof.ev[i]);
+  delete[] g_prof.ev;
+  delete[] g_prof.kid;
+  g_prof = ProfState{};
+  return QLORA_OK;
+}
+
+qlora_status qlora_profile_begin(int32_t cap) {
+  if (cap < 1) return QLORA_ERR_INVALID_ARG;
+  if (g_prof.cap != cap) {
+    qlora_profile_release();
+    g_prof.ev = new hipEvent_t[2 * cap];
+    g_prof.kid = new int[cap];
+    for (int i = 0; i < 2 * cap; ++i)
+      if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) return QLORA_ERR_HIP;
+    g_prof.cap = cap;
+  }
+  g_prof.n = 0;
+  g_prof.on = true;
+  return QLORA_OK;
+}
+
+qlora_status qlora_profile_end(void) {
+  g_prof.on = false;
+  return QLORA_OK;
+}
+
+qlora_status qlora_profile_query(int32_t kernel_id, int32_t *count, double *total_ms) {
+  if (!count || !total_ms) return QLORA_ERR_INVALID_ARG;
+  *count = 0;
+  *total_ms = 0.0;
+  for (int s = 0; s < g_prof.n; ++s) {
+    if (g_prof.kid[s] != kernel_id) continue;
+    if (hipEventSynchronize(g_prof.ev[2 * s + 1]) != hipSuccess) return QLORA_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, g_prof.ev[2 * s], g_prof.ev[2 * s + 1]) != hipSuccess)
+      return QLORA_ERR_HIP;
+    *count += 1;
+    *total_ms += ms;
+  }
+  return QLORA_OK;
+}
+
+}  // extern "C"

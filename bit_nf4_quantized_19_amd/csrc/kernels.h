@@ -1,0 +1,73 @@
+// Host launchers of the gfx950 kernels (internal; the C ABI in capi.hip
+// validates arguments and calls these).
+#pragma once
+
+#include "common.h"
+
+// quantize.hip
+qlora_status launch_quantize(const uint16_t *W0, int64_t n, uint8_t *codes,
+                             float *absmax_out, int dq, int8_t *q, float *s2,
+                             float *mu, void *ws, hipStream_t st);
+size_t quantize_ws_bytes(int64_t n, int dq);
+
+// dequant.hip
+qlora_status launch_dequantize(const uint8_t *codes, ql::ScaleSrc sc, int64_t n,
+                               uint16_t *out, hipStream_t st);
+
+// lora_small.hip : small LoRA contractions and layout helpers
+// P = pad/transposed bf16 copies; see the definitions for layouts.
+qlora_status launch_pad_copy(const uint16_t *src, int64_t rows, int64_t cols,
+                             uint16_t *dst, int64_t drows, int64_t dcols,
+                             int transpose, hipStream_t st);
+// out[m][t] (fp32, M x rp) = sum_c In[m][c] * P[t][c]; In M x C, P rp x C.
+// out2 (optional) receives the first out2_ld columns with leading dim out2_ld.
+// Also writes s*out split into bf16 hi/lo (M x rp each) when hi != NULL.
+qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C,
+                           const uint16_t *P, int rp, float *part, float *out,
+                           int64_t out_ld, float *out2, int out2_ld, float s,
+                           uint16_t *hi, uint16_t *lo, hipStream_t st);
+size_t skinny_part_bytes(int64_t M, int64_t C, int rp);
+// out = s * sum_m In[m][c] * Q[m][t] rounded to bf16; In M x C, Q M x rp fp32.
+// transpose_out == 0: out is C x r (ld r); == 1: out is r x C (ld C).
+qlora_status launch_colacc(const uint16_t *In, int64_t M, int64_t C,
+                           const float *Q, int rp, int r, float s, float *part,
+                           uint16_t *out, int transpose_out, hipStream_t st);
+size_t colacc_part_bytes(int64_t M, int64_t C, int rp);
+
+// gemm.hip : fused dequant-GEMM, forward (Y) and input-gradient (dX) forms
+qlora_status launch_gemm_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
+                             int64_t k, const uint16_t *X, int64_t M,
+                             const uint16_t *Bp, const uint16_t *Hs_hi,
+                             const uint16_t *Hs_lo, int rp, uint16_t *Y,
+                             hipStream_t st);
+qlora_status launch_gemm_dx(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
+                            int64_t k, const uint16_t *dY, int64_t M,
+                            const uint16_t *At, const uint16_t *Gs_hi,
+                            const uint16_t *Gs_lo, int rp, uint16_t *dX,
+                            hipStream_t st);
+
+// gemv.hip : memory-bound forward for M <= 16
+qlora_status launch_gemv_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
+                             int64_t k, const uint16_t *X, int64_t M,
+                             const uint16_t *Bp, const float *H, int rp,
+                             float s, float *part, uint16_t *Y, hipStream_t st);
+size_t gemv_part_bytes(int64_t d, int64_t k, int64_t M);
+
+// merge.hip
+qlora_status launch_merge(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
+                          int64_t k, const uint16_t *A, const uint16_t *B,
+                          int r, float s, uint16_t *Wm, hipStream_t st);
+
+// tables (quantize.hip)
+void host_codebook(float levels[16], float thresholds[15]);
+
+// Event bracketing of kernel launches (capi.hip). prof_begin returns a slot
+// (or -1 when profiling is off/full); prof_end records the closing event.
+int ql_prof_begin(int kernel_id, hipStream_t st);
+void ql_prof_end(int slot, hipStream_t st);
+struct QlProf {
+  int slot;
+  hipStream_t st;
+  QlProf(int kid, hipStream_t s) : slot(ql_prof_begin(kid, s)), st(s) {}
+  ~QlProf() { ql_prof_end(slot, st); }
+};

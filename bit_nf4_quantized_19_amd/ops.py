@@ -1,0 +1,289 @@
+"""Python binding of libqlora_nf4 (argument marshalling only).
+
+Every function here forwards torch device tensors (as raw pointers) and the
+current HIP stream to the C ABI declared in ``include/qlora_nf4.h``; all
+arithmetic runs in the library's gfx950 kernels. There is no fallback: if the
+shared library is missing or fails to load, the first call raises.
+
+bf16 tensors are ``torch.bfloat16`` (passed as their uint16 bit patterns).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
+
+QLORA_OK, QLORA_ERR_INVALID_ARG, QLORA_ERR_UNSUPPORTED, QLORA_ERR_WORKSPACE, QLORA_ERR_HIP = (
+    0, -1, -2, -3, -4)
+OP_QUANTIZE, OP_FWD, OP_BWD = 0, 1, 2
+
+
+class QLoRAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class NF4WeightC(ctypes.Structure):
+    _fields_ = [
+        ("d", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("blocksize", ctypes.c_int32), ("double_quant", ctypes.c_int32),
+        ("dq_blocksize", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
+        ("absmax_q", ctypes.c_void_p), ("absmax_scale", ctypes.c_void_p),
+        ("absmax_offset", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+_vp, _i64, _i32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                              ctypes.c_float, ctypes.c_size_t)
+_PW = ctypes.POINTER(NF4WeightC)
+
+#: exported symbol -> (restype, argtypes); mirrors include/qlora_nf4.h
+SIGNATURES = {
+    "qlora_nf4_quantize": (ctypes.c_int, [_vp, _PW, _vp, _sz, _vp]),
+    "qlora_nf4_dequantize": (ctypes.c_int, [_PW, _vp, _vp]),
+    "qlora_linear_fwd": (ctypes.c_int, [_PW, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp,
+                                        _vp, _sz, _vp]),
+    "qlora_linear_bwd": (ctypes.c_int, [_PW, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp,
+                                        _vp, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_merge": (ctypes.c_int, [_PW, _vp, _vp, _i32, _f32, _vp, _vp]),
+    "qlora_nf4_storage_bytes": (_sz, [_i64, _i64, _i32]),
+    "qlora_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64, _i32, _i32]),
+    "qlora_nf4_codebook": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float),
+                                          ctypes.POINTER(ctypes.c_float)]),
+    "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "qlora_profile_begin": (ctypes.c_int, [_i32]),
+    "qlora_profile_end": (ctypes.c_int, []),
+    "qlora_profile_query": (ctypes.c_int, [_i32, ctypes.POINTER(ctypes.c_int32),
+                                           ctypes.POINTER(ctypes.c_double)]),
+    "qlora_profile_release": (ctypes.c_int, []),
+}
+
+#: kernel ids of the timing hooks (QLORA_K_* in the header)
+KERNELS = ["quantize", "double_quant", "dequantize", "gemm_fwd", "gemm_dx", "gemv",
+           "gemv_epilogue", "lora_down", "lora_reduce", "lora_colacc", "lora_colacc_reduce",
+           "merge", "layout"]
+
+
+def lib() -> ctypes.CDLL:
+    """Load the shared library (once). Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with "
+                              "`python -m bit_nf4_quantized_19_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().qlora_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != QLORA_OK:
+        raise QLoRAError(status, what)
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dev_bf16(t: torch.Tensor, name: str):
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor")
+
+
+# ---------------------------------------------------------------------------
+@dataclass
+class NF4Weight:
+    """Quantised weight: packed codes plus absmax or its double-quantised form."""
+    d: int
+    k: int
+    double_quant: bool
+    codes: torch.Tensor                      # uint8 [d*k/2]
+    absmax: torch.Tensor | None = None       # float32 [nb]
+    absmax_q: torch.Tensor | None = None     # int8 [nb]
+    absmax_scale: torch.Tensor | None = None  # float32 [ceil(nb/256)]
+    absmax_offset: torch.Tensor | None = None  # float32 [1]
+
+    def c_struct(self) -> NF4WeightC:
+        return NF4WeightC(self.d, self.k, 64, int(self.double_quant), 256, 0,
+                          _ptr(self.codes), _ptr(self.absmax), _ptr(self.absmax_q),
+                          _ptr(self.absmax_scale), _ptr(self.absmax_offset))
+
+    @staticmethod
+    def empty(d: int, k: int, double_quant: bool, device="cuda") -> "NF4Weight":
+        n = d * k
+        nb = n // 64
+        w = NF4Weight(d, k, double_quant, torch.empty(n // 2, dtype=torch.uint8, device=device))
+        if double_quant:
+            w.absmax_q = torch.empty(nb, dtype=torch.int8, device=device)
+            w.absmax_scale = torch.empty(-(-nb // 256), dtype=torch.float32, device=device)
+            w.absmax_offset = torch.empty(1, dtype=torch.float32, device=device)
+        else:
+            w.absmax = torch.empty(nb, dtype=torch.float32, device=device)
+        return w
+
+
+def storage_bytes(d: int, k: int, double_quant: bool) -> int:
+    return int(lib().qlora_nf4_storage_bytes(d, k, int(double_quant)))
+
+
+def workspace_bytes(op: int, d: int, k: int, M: int = 0, r: int = 0,
+                    double_quant: bool = True) -> int:
+    n = lib().qlora_workspace_bytes(op, d, k, M, r, int(double_quant))
+    if n == ctypes.c_size_t(-1).value:
+        raise QLoRAError(QLORA_ERR_UNSUPPORTED, "workspace_bytes")
+    return int(n)
+
+
+def codebook():
+    lv = (ctypes.c_float * 16)()
+    th = (ctypes.c_float * 15)()
+    _check(lib().qlora_nf4_codebook(lv, th), "codebook")
+    return list(lv), list(th)
+
+
+def _workspace(nbytes: int, device, ws: torch.Tensor | None):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None:
+        return ws, ws.numel() * ws.element_size()
+    t = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-t.data_ptr()) % 256
+    return t[off:off + nbytes], nbytes
+
+
+def quantize(W0: torch.Tensor, double_quant: bool = True, out: NF4Weight | None = None,
+             ws: torch.Tensor | None = None, stream=None) -> NF4Weight:
+    _dev_bf16(W0, "W0")
+    d, k = W0.shape
+    w = out if out is not None else NF4Weight.empty(d, k, double_quant, W0.device)
+    wsb = workspace_bytes(OP_QUANTIZE, d, k, 0, 0, double_quant)
+    wst, wsn = _workspace(wsb, W0.device, ws)
+    cw = w.c_struct()
+    _check(lib().qlora_nf4_quantize(W0.data_ptr(), ctypes.byref(cw), _ptr(wst), wsn,
+                                    _stream(stream)), "qlora_nf4_quantize")
+    return w
+
+
+def dequantize(w: NF4Weight, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    Y = out if out is not None else torch.empty(w.d, w.k, dtype=torch.bfloat16,
+                                                device=w.codes.device)
+    cw = w.c_struct()
+    _check(lib().qlora_nf4_dequantize(ctypes.byref(cw), Y.data_ptr(), _stream(stream)),
+           "qlora_nf4_dequantize")
+    return Y
+
+
+def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+               lora_alpha: float, save_h: bool = True, Y: torch.Tensor | None = None,
+               H: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+    """Y = X W'^T + (alpha/r) (X A^T) B^T. Returns (Y, H or None)."""
+    for t, nm in ((X, "X"), (A, "A"), (B, "B")):
+        _dev_bf16(t, nm)
+    M = X.shape[0]
+    r = A.shape[0]
+    if Y is None:
+        Y = torch.empty(M, w.d, dtype=torch.bfloat16, device=X.device)
+    if save_h and H is None:
+        H = torch.empty(M, r, dtype=torch.float32, device=X.device)
+    wsb = workspace_bytes(OP_FWD, w.d, w.k, M, r, w.double_quant)
+    wst, wsn = _workspace(wsb, X.device, ws)
+    cw = w.c_struct()
+    _check(lib().qlora_linear_fwd(ctypes.byref(cw), X.data_ptr(), M, A.data_ptr(),
+                                  B.data_ptr(), r, float(lora_alpha), Y.data_ptr(),
+                                  _ptr(H) if save_h else None, _ptr(wst), wsn,
+                                  _stream(stream)), "qlora_linear_fwd")
+    return Y, (H if save_h else None)
+
+
+def linear_bwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+               lora_alpha: float, dY: torch.Tensor, H: torch.Tensor | None = None,
+               need_dx: bool = True, dX=None, dA=None, dB=None,
+               ws: torch.Tensor | None = None, stream=None):
+    """Returns (dX or None, dA, dB)."""
+    for t, nm in ((X, "X"), (A, "A"), (B, "B"), (dY, "dY")):
+        _dev_bf16(t, nm)
+    M = X.shape[0]
+    r = A.shape[0]
+    dev = X.device
+    if need_dx and dX is None:
+        dX = torch.empty(M, w.k, dtype=torch.bfloat16, device=dev)
+    if dA is None:
+        dA = torch.empty(r, w.k, dtype=torch.bfloat16, device=dev)
+    if dB is None:
+        dB = torch.empty(w.d, r, dtype=torch.bfloat16, device=dev)
+    wsb = workspace_bytes(OP_BWD, w.d, w.k, M, r, w.double_quant)
+    wst, wsn = _workspace(wsb, dev, ws)
+    cw = w.c_struct()
+    _check(lib().qlora_linear_bwd(ctypes.byref(cw), X.data_ptr(), M, A.data_ptr(),
+                                  B.data_ptr(), r, float(lora_alpha), dY.data_ptr(), _ptr(H),
+                                  _ptr(dX) if need_dx else None, dA.data_ptr(), dB.data_ptr(),
+                                  _ptr(wst), wsn, _stream(stream)), "qlora_linear_bwd")
+    return (dX if need_dx else None), dA, dB
+
+
+def merge(w: NF4Weight, A: torch.Tensor, B: torch.Tensor, lora_alpha: float,
+          out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    _dev_bf16(A, "A")
+    _dev_bf16(B, "B")
+    r = A.shape[0]
+    Wm = out if out is not None else torch.empty(w.d, w.k, dtype=torch.bfloat16,
+                                                 device=A.device)
+    cw = w.c_struct()
+    _check(lib().qlora_merge(ctypes.byref(cw), A.data_ptr(), B.data_ptr(), r,
+                             float(lora_alpha), Wm.data_ptr(), _stream(stream)), "qlora_merge")
+    return Wm
+
+
+def profile_begin(cap: int = 4096):
+    """Start bracketing kernel launches with HIP events (see the header)."""
+    _check(lib().qlora_profile_begin(int(cap)), "qlora_profile_begin")
+
+
+def profile_end():
+    _check(lib().qlora_profile_end(), "qlora_profile_end")
+
+
+def profile_query(kernel: str):
+    """(launch count, total milliseconds) of a kernel since profile_begin."""
+    cnt = ctypes.c_int32(0)
+    ms = ctypes.c_double(0.0)
+    _check(lib().qlora_profile_query(KERNELS.index(kernel), ctypes.byref(cnt),
+                                     ctypes.byref(ms)), "qlora_profile_query")
+    return int(cnt.value), float(ms.value)
+
+
+def lora_scale(alpha: float, r: int) -> float:
+    """fl32(alpha / r), the scale the kernels apply."""
+    import numpy as np
+    return float(np.float32(np.float32(alpha) / np.float32(r)))
+
+
+__all__ = ["NF4Weight", "QLoRAError", "quantize", "dequantize", "linear_fwd", "linear_bwd",
+           "merge", "storage_bytes", "workspace_bytes", "codebook", "lib", "lora_scale",
+           "OP_QUANTIZE", "OP_FWD", "OP_BWD", "SIGNATURES", "LIB_PATH", "KERNELS",
+           "profile_begin", "profile_end", "profile_query"]
+_ = math

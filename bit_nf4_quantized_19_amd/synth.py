@@ -58,6 +58,13 @@ def linear_inputs(d: int, k: int, M: int, r: int, idx: int = 0,
     return out
 
 
+def to_device_bf16(bits: np.ndarray, device="cuda"):
+    """Copy bf16 bits (uint16 array) to a torch.bfloat16 device tensor."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
 def normal_bf16_device(shape, std: float, seed: int, device="cuda"):
     """Device-side variant for shapes too large to draw on the host: a seeded
     torch generator on ``device``, float32 normal times ``std``, rounded to

@@ -1,0 +1,196 @@
+/*
+ * qlora_nf4.h -- C ABI of the MI355X (gfx950) QLoRA frozen-base NF4 linear.
+ *
+ * The layer (QLoRA glossary, Ultralytics, "QLoRA 的工作原理"; Day-25 LoRA/QLoRA
+ * notes, sections 2.1 and 6.2): a frozen base weight W0 (d x k, row-major,
+ * out_features x in_features) is stored as 4-bit NormalFloat codes in blocks
+ * of 64 consecutive weights with one absmax per block; the absmax values may
+ * be double-quantised to 8 bits with one float32 scale per 256 blocks. The
+ * forward pass dequantises W0 to bfloat16 and computes, for M token rows X
+ * (M x k),
+ *
+ *     Y = X W'^T + s (X A^T) B^T,       s = fl32(lora_alpha / r),
+ *
+ * with LoRA matrices A (r x k) and B (d x r). The backward pass produces dX
+ * through the same dequantised W' and gradients for A and B only.
+ *
+ * Conventions shared by every entry point
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major, dense.
+ *   - Every tensor pointer is a device pointer owned by the caller, 16-byte
+ *     aligned; the weight descriptor itself is host memory. The library never
+ *     allocates, frees or keeps a pointer after a call returns.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). Calls only
+ *     enqueue work on it and never synchronise; results are valid once the
+ *     stream has reached them. Calls on different streams that write the
+ *     same buffers race.
+ *   - Arguments are checked on the host before anything is enqueued; on any
+ *     error nothing is launched. A launch failure returns QLORA_ERR_HIP.
+ *     Device faults surface at the caller's next synchronisation.
+ *   - Outputs must not alias inputs. Results are deterministic: the same
+ *     inputs give bit-identical outputs on every call.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_INVALID_ARG = -1, /* NULL/misaligned pointer, size < 1, non-finite alpha */
+  QLORA_ERR_UNSUPPORTED = -2, /* blocksize != 64, dq_blocksize != 256, k % 64 != 0,
+                                 d % 8 != 0, d*k/64 >= 2^32, r > 128 */
+  QLORA_ERR_WORKSPACE = -3,   /* workspace smaller than qlora_workspace_bytes() */
+  QLORA_ERR_HIP = -4          /* a kernel launch failed */
+} qlora_status;
+
+/*
+ * Quantised weight (QLoRA glossary, "QLoRA 的工作原理", NF4 and
+ * double-quantisation bullets; LLM tutorial ch. 3, "双重量化").
+ *
+ *   codes         [d*k/2] bytes; element 2j of the row-major weight is the
+ *                 high nibble of byte j, element 2j+1 the low nibble. A code
+ *                 indexes the 16 ascending NF4 levels (code 7 is exactly 0).
+ *   absmax        [d*k/64] float32, one per block       (double_quant == 0)
+ *   absmax_q      [d*k/64] int8 codes of (absmax - mu)  (double_quant == 1)
+ *   absmax_scale  [ceil(d*k/64/256)] float32 scales s2  (double_quant == 1)
+ *   absmax_offset [1] float32 mean mu                   (double_quant == 1)
+ * The dequantised block scale is a' = fl(fl(q * s2) + mu) (or absmax) and a
+ * weight dequantises to w' = bf16_rne(fl(level[code] * a')).
+ * Pointers unused by the chosen mode may be NULL.
+ */
+typedef struct qlora_nf4_weight {
+  int64_t d;             /* rows (out_features), multiple of 8 */
+  int64_t k;             /* columns (in_features), multiple of 64 */
+  int32_t blocksize;     /* must be 64 */
+  int32_t double_quant;  /* 0 or 1 */
+  int32_t dq_blocksize;  /* must be 256 when double_quant == 1 */
+  int32_t reserved;      /* set to 0 */
+  uint8_t *codes;
+  float *absmax;
+  int8_t *absmax_q;
+  float *absmax_scale;
+  float *absmax_offset;
+} qlora_nf4_weight;
+
+/* Operation ids for qlora_workspace_bytes. */
+enum { QLORA_OP_QUANTIZE = 0, QLORA_OP_FWD = 1, QLORA_OP_BWD = 2 };
+
+/*
+ * Quantise a bf16 weight W0 (d x k) into `w` (all of w's pointers are
+ * outputs; d, k, blocksize, double_quant, dq_blocksize are inputs).
+ * Per block of 64: a = max|w|; each weight gets the code of the level nearest
+ * to fl32(w / a) (float32 distance, lower code on equal distances); an
+ * all-zero block gets code 7 and absmax 0 (QLoRA glossary, "QLoRA 的工作原理",
+ * snippet). With double quantisation (same page, double-quantisation bullet;
+ * Day-25 notes 3.3: constants are quantised after the weights):
+ * mu = exact mean of all absmax values rounded once to float32; per group of
+ * 256 blocks s2 = fl(max|fl(a - mu)| / 127) and
+ * q = clamp(rne(fl(fl(a - mu) / s2)), -127, 127) (q = 0 when s2 == 0).
+ * Workspace: qlora_workspace_bytes(QLORA_OP_QUANTIZE, d, k, 0, 0, dq) bytes
+ * of device memory (0 without double quantisation; ws may then be NULL).
+ * Non-finite weights are outside the method's domain; their codes are
+ * unspecified.
+ */
+qlora_status qlora_nf4_quantize(const uint16_t *W0, const qlora_nf4_weight *w,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Dequantise `w` to bf16 W_out (d x k): w' = bf16(fl(level[code] * a'))
+ * (QLoRA glossary, "QLoRA 的工作原理": weights are dequantised to bfloat16
+ * before the matrix product; LLM tutorial ch. 3, 3.8: dequantise to bf16
+ * before merging). Bit-exact.
+ */
+qlora_status qlora_nf4_dequantize(const qlora_nf4_weight *w, uint16_t *W_out,
+                                  void *stream);
+
+/*
+ * Forward: Y (M x d, bf16) = bf16(X W'^T + s H B^T), H = X A^T (Day-25 notes
+ * 2.1 and 6.2; QLoRA glossary forward paragraph). X is M x k, A is r x k,
+ * B is d x r, all bf16; accumulation is float32. If H_save is non-NULL the
+ * float32 H (M x r) is written there for the backward pass. M <= 16 uses the
+ * memory-bound GEMV kernel, larger M the fused dequant-GEMM.
+ * Workspace: qlora_workspace_bytes(QLORA_OP_FWD, d, k, M, r, dq) bytes.
+ */
+qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X,
+                              int64_t M, const uint16_t *A, const uint16_t *B,
+                              int32_t r, float lora_alpha, uint16_t *Y,
+                              float *H_save, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/*
+ * Backward of the forward above for upstream gradient dY (M x d, bf16)
+ * (chain rule; QLoRA glossary forward paragraph: gradients pass through the
+ * dequantised weight, only A and B are updated):
+ *   G  = dY B                    (float32, M x r, workspace)
+ *   dX = bf16(dY W' + s G A)     (M x k; skipped when dX == NULL)
+ *   dA = bf16(s G^T X)           (r x k)
+ *   dB = bf16(s dY^T H)          (d x r)
+ * H is the float32 X A^T saved by the forward, or NULL to recompute it.
+ * Workspace: qlora_workspace_bytes(QLORA_OP_BWD, d, k, M, r, dq) bytes.
+ */
+qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X,
+                              int64_t M, const uint16_t *A, const uint16_t *B,
+                              int32_t r, float lora_alpha, const uint16_t *dY,
+                              const float *H, uint16_t *dX, uint16_t *dA,
+                              uint16_t *dB, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/*
+ * Merge: W_merged (d x k, bf16) = bf16(float(w') + s (B A)) with B A summed
+ * in float32 (Day-25 notes 2.6 and 6.2; LLM tutorial ch. 3, 3.8: a 4-bit base
+ * is dequantised to bf16 and then merged).
+ */
+qlora_status qlora_merge(const qlora_nf4_weight *w, const uint16_t *A,
+                         const uint16_t *B, int32_t r, float lora_alpha,
+                         uint16_t *W_merged, void *stream);
+
+/* Bytes of the quantised record for d x k: d*k/2 + 4*nb (no double quant)
+ * or d*k/2 + nb + 4*ceil(nb/256) + 4 (double quant), nb = d*k/64.
+ * Returns 0 for an unsupported shape. */
+size_t qlora_nf4_storage_bytes(int64_t d, int64_t k, int32_t double_quant);
+
+/* Device workspace in bytes for `op` (QLORA_OP_*); 0 means none needed.
+ * Returns (size_t)-1 for an unsupported shape. */
+size_t qlora_workspace_bytes(int32_t op, int64_t d, int64_t k, int64_t M,
+                             int32_t r, int32_t double_quant);
+
+/* Host copy of the constant tables compiled into the kernels: the 16 NF4
+ * levels (ascending) and the 15 code thresholds T_i (code = #{i: x > T_i}).
+ * Touches no device; for inspection and tests. Returns QLORA_OK. */
+qlora_status qlora_nf4_codebook(float levels[16], float thresholds[15]);
+
+/* Static text for a status code. */
+const char *qlora_status_string(int status);
+
+/*
+ * Kernel timing with HIP events (measurement support; not part of the
+ * method). Between qlora_profile_begin(cap) and qlora_profile_end(), every
+ * launch of the library's main kernels is bracketed by two hipEvents
+ * recorded on the launch stream, up to `cap` launches. qlora_profile_query
+ * waits for the recorded events and returns the number of launches of
+ * kernel `kernel_id` (QLORA_K_*) and their summed duration in milliseconds.
+ * Not thread-safe; intended for one benchmarking thread. begin() creates the
+ * events (host call, may allocate); release() destroys them.
+ */
+enum {
+  QLORA_K_QUANTIZE = 0, QLORA_K_DOUBLE_QUANT = 1, QLORA_K_DEQUANTIZE = 2,
+  QLORA_K_GEMM_FWD = 3, QLORA_K_GEMM_DX = 4, QLORA_K_GEMV = 5, QLORA_K_GEMV_EPILOGUE = 6,
+  QLORA_K_LORA_DOWN = 7, QLORA_K_LORA_REDUCE = 8, QLORA_K_LORA_COLACC = 9,
+  QLORA_K_LORA_COLACC_REDUCE = 10, QLORA_K_MERGE = 11, QLORA_K_LAYOUT = 12,
+  QLORA_K_COUNT = 13
+};
+qlora_status qlora_profile_begin(int32_t cap);
+qlora_status qlora_profile_end(void);
+qlora_status qlora_profile_query(int32_t kernel_id, int32_t *count, double *total_ms);
+qlora_status qlora_profile_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

@@ -27,7 +27,7 @@ Readings where the pages are silent (each listed in the design doc)
 -------------------------------------------------------------
 * Levels: the quantiles are evaluated in float64 at the literal decimal
   probabilities and rounded once to float32 (the snippet's float32 evaluation
-  lands within 4 ulp; the tests check that).
+  lands within 8 ulp; the tests check that).
 * Tie-break of the nearest-level search: lowest index (the snippet's argmin).
 * All-zero block (absmax 0, ``0/0`` undefined): every code is the zero level.
 * Code packing: element ``2j`` in the high nibble of byte ``j``.
@@ -104,6 +104,15 @@ def nearest_level(x: np.ndarray, levels: np.ndarray) -> np.ndarray:
     return out
 
 
+def block_absmax(w: np.ndarray, blocksize: int = BLOCKSIZE) -> np.ndarray:
+    """``a = max |w|`` over each block of ``blocksize`` consecutive weights
+    (QLoRA glossary, "QLoRA 的工作原理": one absmax scale per 64 weights)."""
+    w = np.asarray(w, dtype=np.float32).reshape(-1)
+    if w.size % blocksize:
+        raise ValueError("length must be a multiple of the blocksize")
+    return np.abs(w.reshape(-1, blocksize)).max(axis=1)
+
+
 def quantize_blocks(w: np.ndarray, levels: np.ndarray | None = None,
                     blocksize: int = BLOCKSIZE):
     """Blockwise absmax quantisation of a flat float32 array.
@@ -115,10 +124,8 @@ def quantize_blocks(w: np.ndarray, levels: np.ndarray | None = None,
     """
     lv = nf4_levels() if levels is None else np.asarray(levels, np.float32)
     w = np.asarray(w, dtype=np.float32).reshape(-1)
-    if w.size % blocksize:
-        raise ValueError("length must be a multiple of the blocksize")
+    absmax = block_absmax(w, blocksize)
     wb = w.reshape(-1, blocksize)
-    absmax = np.abs(wb).max(axis=1)
     with np.errstate(invalid="ignore", divide="ignore"):
         x = wb / absmax[:, None]  # IEEE float32 division, correctly rounded
     codes = nearest_level(x, lv)
