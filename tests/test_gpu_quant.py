@@ -95,7 +95,7 @@ def _sweep_weight():
     extra[2, :] = 0x8000
     extra[3, 0] = 0x0001                         # smallest subnormal alone
     blocks = np.concatenate([blocks, extra])
-    nblk = -(-blocks.shape[0] // 8) * 8
+    nblk = -(-blocks.shape[0] // 64) * 64          # rows of 512: d % 8 == 0
     blocks = np.concatenate([blocks, np.zeros((nblk - blocks.shape[0], 64), np.uint16)])
     return blocks.reshape(-1, 512)
 
