@@ -23,7 +23,7 @@ Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against values the pages print, closed forms, invariants or brute force,
 except the 8-bit format of the double-quantised absmax (symmetric int8 with
 one float32 scale per 256 blocks and one global mean), which the pages do not
-define; that format is the reading documented in the design doc and its code
+define; that format is the plainest reading of "8-bit" and its code
 format is "parity unpinned" beyond the invariants tested (error bound,
 equal-value special case, exact mean).
 """

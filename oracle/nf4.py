@@ -23,8 +23,8 @@ Pages followed
 * LLM-train tutorial ch. 3 (jwzheng96.github.io), section "双重量化": one
   float32 absmax per 64-element block costs 32/64 = 0.5 bit per parameter.
 
-Readings where the pages are silent (each listed in the design doc)
--------------------------------------------------------------
+Readings where the pages are silent
+----------------------------------
 * Levels: the quantiles are evaluated in float64 at the literal decimal
   probabilities and rounded once to float32 (the snippet's float32 evaluation
   lands within 8 ulp; the tests check that).
