@@ -105,8 +105,7 @@ BwdWs bwd_layout(char *base, int64_t d, int64_t k, int64_t M, int r, bool need_h
   L.Gs_hi = need_dx ? c.take<uint16_t>(M * rp * 2) : nullptr;
   L.Gs_lo = need_dx ? c.take<uint16_t>(M * rp * 2) : nullptr;
   L.At = need_dx ? c.take<uint16_t>(k * rp * 2) : nullptr;
-  const int64_t cp = (int64_t)std::max(colacc_part_bytes(M, d, rp), colacc_part_bytes(M, k, rp));
-  L.cpart = c.take<float>(cp);
+  L.cpart = c.take<float>((int64_t)colacc_part_bytes(M, d, k, rp));
   L.bytes = c.off;
   return L;
 }
@@ -202,8 +201,8 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int6
 
   const uint16_t *Ap = A, *Bp = B;
   if (r % 16) {
-    if ((s = launch_pad_copy(A, r, k, L.Ap, rp, k, 0, st)) != QLORA_OK) return s;
-    if ((s = launch_pad_copy(B, d, r, L.Bp, d, rp, 0, st)) != QLORA_OK) return s;
+    const LayoutReq req[2] = {{A, r, k, L.Ap, rp, k, 0}, {B, d, r, L.Bp, d, rp, 0}};
+    if ((s = launch_layout(req, 2, st)) != QLORA_OK) return s;
     Ap = L.Ap;
     Bp = L.Bp;
   }
@@ -238,28 +237,30 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, int6
   const int rp = (int)ql_rup(r, 16);
   const float sc = lora_alpha / (float)r;
 
+  // layouts: A padded (for H), B^T (for G), A^T (for the dX epilogue)
+  {
+    const LayoutReq req[3] = {{A, r, k, (need_h && (r % 16)) ? L.Ap : nullptr, rp, k, 0},
+                              {B, d, r, L.Bt, rp, d, 1},
+                              {A, r, k, need_dx ? L.At : nullptr, k, rp, 1}};
+    if ((s = launch_layout(req, 3, st)) != QLORA_OK) return s;
+  }
   const float *Hq = H;  // M x rp
   if (need_h) {
-    const uint16_t *Ap = A;
-    if (r % 16) {
-      if ((s = launch_pad_copy(A, r, k, L.Ap, rp, k, 0, st)) != QLORA_OK) return s;
-      Ap = L.Ap;
-    }
+    const uint16_t *Ap = (r % 16) ? L.Ap : A;
     if ((s = launch_skinny(X, M, k, Ap, rp, L.Hpart, L.H, rp, nullptr, 0, sc, nullptr, nullptr,
                            st)) != QLORA_OK)
       return s;
     Hq = L.H;
   }
   // G = dY B (float32, M x rp) and s*G as bf16 hi/lo for the dX epilogue
-  if ((s = launch_pad_copy(B, d, r, L.Bt, rp, d, 1, st)) != QLORA_OK) return s;
   if ((s = launch_skinny(dY, M, d, L.Bt, rp, L.Gpart, L.G, rp, nullptr, 0, sc, L.Gs_hi, L.Gs_lo,
                          st)) != QLORA_OK)
     return s;
-  // dB = s dY^T H (d x r) ; dA = s G^T X (r x k)
-  if ((s = launch_colacc(dY, M, d, Hq, rp, r, sc, L.cpart, dB, 0, st)) != QLORA_OK) return s;
-  if ((s = launch_colacc(X, M, k, L.G, rp, r, sc, L.cpart, dA, 1, st)) != QLORA_OK) return s;
+  // dB = s dY^T H (d x r) and dA = s G^T X (r x k), one launch
+  if ((s = launch_colacc2(ColaccReq{dY, d, Hq, dB, 0}, ColaccReq{X, k, L.G, dA, 1}, M, rp, r, sc,
+                          L.cpart, st)) != QLORA_OK)
+    return s;
   if (need_dx) {
-    if ((s = launch_pad_copy(A, r, k, L.At, k, rp, 1, st)) != QLORA_OK) return s;
     if ((s = launch_gemm_dx(w->codes, scale_src(w), d, k, dY, M, L.At, L.Gs_hi, L.Gs_lo, rp, dX,
                             st)) != QLORA_OK)
       return s;
@@ -285,6 +286,7 @@ namespace {
 struct ProfState {
   bool on = false;
   int cap = 0, n = 0;
+  uint32_t mask = 0xFFFFFFFFu;
   hipEvent_t *ev = nullptr;
   int *kid = nullptr;
 };
@@ -292,28 +294,28 @@ ProfState g_prof;
 }  // namespace
 
 int ql_prof_begin(int kernel_id, hipStream_t st) {
-  if (!g_prof.on || g_prof.n >= g_prof.cap) return -1;
+  if (!g_prof.on || g_prof.n >= g_prof.cap || !((g_prof.mask >> kernel_id) & 1u)) return -1;
   const int s = g_prof.n++;
   g_prof.kid[s] = kernel_id;
-  hipEventRecord(g_prof.ev[2 * s], st);
+  (void)hipEventRecord(g_prof.ev[2 * s], st);
   return s;
 }
 
 void ql_prof_end(int slot, hipStream_t st) {
-  if (slot >= 0) hipEventRecord(g_prof.ev[2 * slot + 1], st);
+  if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot + 1], st);
 }
 
 extern "C" {
 
 qlora_status qlora_profile_release(void) {
-  for (int i = 0; i < 2 * g_prof.cap; ++i) hipEventDestroy(g_prof.ev[i]);
+  for (int i = 0; i < 2 * g_prof.cap; ++i) (void)hipEventDestroy(g_prof.ev[i]);
   delete[] g_prof.ev;
   delete[] g_prof.kid;
   g_prof = ProfState{};
   return QLORA_OK;
 }
 
-qlora_status qlora_profile_begin(int32_t cap) {
+qlora_status qlora_profile_begin(int32_t cap, uint32_t mask) {
   if (cap < 1) return QLORA_ERR_INVALID_ARG;
   if (g_prof.cap != cap) {
     qlora_profile_release();
@@ -324,6 +326,7 @@ qlora_status qlora_profile_begin(int32_t cap) {
     g_prof.cap = cap;
   }
   g_prof.n = 0;
+  g_prof.mask = mask ? mask : 0xFFFFFFFFu;
   g_prof.on = true;
   return QLORA_OK;
 }

@@ -15,10 +15,17 @@ qlora_status launch_dequantize(const uint8_t *codes, ql::ScaleSrc sc, int64_t n,
                                uint16_t *out, hipStream_t st);
 
 // lora_small.hip : small LoRA contractions and layout helpers
-// P = pad/transposed bf16 copies; see the definitions for layouts.
-qlora_status launch_pad_copy(const uint16_t *src, int64_t rows, int64_t cols,
-                             uint16_t *dst, int64_t drows, int64_t dcols,
-                             int transpose, hipStream_t st);
+// Up to four zero-padded / transposed bf16 copies in one launch:
+// dst (drows x dcols) [i][j] = src[i][j] (or src[j][i] when transpose), zero
+// outside src (rows x cols). Requests with dst == NULL are skipped.
+struct LayoutReq {
+  const uint16_t *src;
+  int64_t rows, cols;
+  uint16_t *dst;
+  int64_t drows, dcols;
+  int transpose;
+};
+qlora_status launch_layout(const LayoutReq *req, int nreq, hipStream_t st);
 // out[m][t] (fp32, M x rp) = sum_c In[m][c] * P[t][c]; In M x C, P rp x C.
 // out2 (optional) receives the first out2_ld columns with leading dim out2_ld.
 // Also writes s*out split into bf16 hi/lo (M x rp each) when hi != NULL.
@@ -27,12 +34,19 @@ qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C,
                            int64_t out_ld, float *out2, int out2_ld, float s,
                            uint16_t *hi, uint16_t *lo, hipStream_t st);
 size_t skinny_part_bytes(int64_t M, int64_t C, int rp);
-// out = s * sum_m In[m][c] * Q[m][t] rounded to bf16; In M x C, Q M x rp fp32.
+// Two problems out = s * sum_m In[m][c] * Q[m][t] rounded to bf16 (In M x C,
+// Q M x rp fp32) in one launch plus one reduction launch.
 // transpose_out == 0: out is C x r (ld r); == 1: out is r x C (ld C).
-qlora_status launch_colacc(const uint16_t *In, int64_t M, int64_t C,
-                           const float *Q, int rp, int r, float s, float *part,
-                           uint16_t *out, int transpose_out, hipStream_t st);
-size_t colacc_part_bytes(int64_t M, int64_t C, int rp);
+struct ColaccReq {
+  const uint16_t *In;
+  int64_t C;
+  const float *Q;
+  uint16_t *out;
+  int transpose_out;
+};
+qlora_status launch_colacc2(const ColaccReq &a, const ColaccReq &b, int64_t M, int rp,
+                            int r, float s, float *part, hipStream_t st);
+size_t colacc_part_bytes(int64_t M, int64_t C0, int64_t C1, int rp);
 
 // gemm.hip : fused dequant-GEMM, forward (Y) and input-gradient (dX) forms
 qlora_status launch_gemm_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,

@@ -61,7 +61,7 @@ SIGNATURES = {
     "qlora_nf4_codebook": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float),
                                           ctypes.POINTER(ctypes.c_float)]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
-    "qlora_profile_begin": (ctypes.c_int, [_i32]),
+    "qlora_profile_begin": (ctypes.c_int, [_i32, ctypes.c_uint32]),
     "qlora_profile_end": (ctypes.c_int, []),
     "qlora_profile_query": (ctypes.c_int, [_i32, ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_double)]),
@@ -258,9 +258,13 @@ def merge(w: NF4Weight, A: torch.Tensor, B: torch.Tensor, lora_alpha: float,
     return Wm
 
 
-def profile_begin(cap: int = 4096):
-    """Start bracketing kernel launches with HIP events (see the header)."""
-    _check(lib().qlora_profile_begin(int(cap)), "qlora_profile_begin")
+def profile_begin(cap: int = 4096, kernels=None):
+    """Start bracketing kernel launches with HIP events (see the header);
+    ``kernels`` (names from KERNELS) limits the bracketing to those kernels."""
+    mask = 0
+    for name in kernels or ():
+        mask |= 1 << KERNELS.index(name)
+    _check(lib().qlora_profile_begin(int(cap), mask), "qlora_profile_begin")
 
 
 def profile_end():

@@ -169,9 +169,10 @@ const char *qlora_status_string(int status);
 
 /*
  * Kernel timing with HIP events (measurement support; not part of the
- * method). Between qlora_profile_begin(cap) and qlora_profile_end(), every
- * launch of the library's main kernels is bracketed by two hipEvents
- * recorded on the launch stream, up to `cap` launches. qlora_profile_query
+ * method). Between qlora_profile_begin(cap, mask) and qlora_profile_end(),
+ * every launch of a kernel whose id bit is set in `mask` (bit QLORA_K_* ;
+ * 0 = all) is bracketed by two hipEvents recorded on the launch stream, up
+ * to `cap` launches; other launches get no events. qlora_profile_query
  * waits for the recorded events and returns the number of launches of
  * kernel `kernel_id` (QLORA_K_*) and their summed duration in milliseconds.
  * Not thread-safe; intended for one benchmarking thread. begin() creates the
@@ -184,7 +185,7 @@ enum {
   QLORA_K_LORA_COLACC_REDUCE = 10, QLORA_K_MERGE = 11, QLORA_K_LAYOUT = 12,
   QLORA_K_COUNT = 13
 };
-qlora_status qlora_profile_begin(int32_t cap);
+qlora_status qlora_profile_begin(int32_t cap, uint32_t mask);
 qlora_status qlora_profile_end(void);
 qlora_status qlora_profile_query(int32_t kernel_id, int32_t *count, double *total_ms);
 qlora_status qlora_profile_release(void);
