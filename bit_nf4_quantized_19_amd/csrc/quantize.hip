@@ -9,7 +9,8 @@
 //
 // Kernel design
 //  * quantize_kernel: one lane per 16-byte chunk (8 weights), 8 lanes per
-//    block, coalesced 16-byte loads and 4-byte code stores. The block absmax
+//    block, coalesced 16-byte loads and 4-byte code stores; each lane takes
+//    QU chunks 256 lanes apart and issues their loads together. The block absmax
 //    is a DPP max over the 8 lanes on the bf16 magnitude bits. The code
 //    decision is division-free and bit-exact: the chunk's x is located in
 //    one of 65 cells (approximate reciprocal), the cell's single candidate
@@ -21,10 +22,16 @@
 //  * With double quantisation the kernel also accumulates an exact integer
 //    histogram of the bf16 absmax values by exponent (sum of 8-bit
 //    significands per exponent): the exact sum of all absmax values, needed
-//    for the mean, independent of summation order.
-//  * dq_mean_kernel turns the histogram into mu = round_f32(sum / nb) with a
-//    384-bit integer division (one lane; the kernel is tiny).
-//  * dq_encode_kernel: one workgroup per group of 256 blocks.
+//    for the mean, independent of summation order. Each wave first adds the
+//    significands of its blocks per distinct exponent (few: the absmax values
+//    of one tensor span few octaves), so the LDS atomics are per wave, not
+//    per block; each workgroup then adds its histogram to one of NHC global
+//    copies (spreading the atomics over more addresses).
+//  * dq_mean_kernel (one workgroup) adds the histogram copies, places them
+//    into 384-bit limb sums with LDS atomics (one lane per exponent) and
+//    turns the sum into mu = round_f32(sum / nb) by exact long division.
+//  * dq_encode_kernel: one workgroup per group of 256 blocks: s2 and the
+//    int8 codes of its group.
 #include <cstring>
 
 #include <algorithm>
@@ -35,7 +42,8 @@
 namespace {
 
 constexpr int QT = 256;
-constexpr int kMaxQuantGrid = 2048;
+constexpr int QU = 8;      // chunks per lane
+constexpr int NHC = 64;    // global histogram copies (workgroup b adds to copy b % NHC)
 
 struct __align__(16) Cell {
   float T, H;
@@ -64,7 +72,9 @@ QL_DEV uint32_t encode8(const uint32_t u[4], float a, const Cell *cell) {
     aa = a * 0x1p100f;
     sw = 0x1p100f;
   }
-  const float r32 = 32.0f * __builtin_amdgcn_rcpf(aa);
+  // 32 / aa as the reciprocal of aa / 32 (exact scaling), which stays a
+  // normal float32 for aa up to the largest bf16
+  const float r32 = __builtin_amdgcn_rcpf(aa * 0x1p-5f);
   uint32_t packed = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -89,7 +99,10 @@ __global__ __launch_bounds__(QT) void quantize_kernel(
     float *__restrict__ absmax_out, unsigned long long *__restrict__ hist,
     int64_t nchunks) {
   __shared__ Cell cell[NF4_NCELL];
-  __shared__ unsigned long long lhist[256];
+  // 8 private 32-bit copies of the histogram, one per block-leader slot of a
+  // wave (lanes 0, 8, .., 56), so the LDS atomics rarely collide; a copy
+  // receives at most 16 significands (< 2^12) per workgroup
+  __shared__ uint32_t lh8[8][256];
   const int tid = threadIdx.x;
   if (tid < NF4_NCELL) {
     const int j = c_cell[tid];
@@ -98,41 +111,49 @@ __global__ __launch_bounds__(QT) void quantize_kernel(
     cell[tid].base = (uint32_t)j;
     cell[tid].pad = 0;
   }
-  if (DQ) lhist[tid] = 0;
-  __syncthreads();
-
-  const int64_t stride = (int64_t)gridDim.x * QT;
-  for (int64_t base = (int64_t)blockIdx.x * QT; base < nchunks; base += stride) {
-    const int64_t ch = base + tid;
-    if (ch < nchunks) {  // n % 64 == 0: the 8 lanes of a block agree
-      const uint4 v = W[ch];
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-      uint32_t m = 0;
+  if (DQ)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        m = max(m, max(u[i] & 0x7fffu, (u[i] >> 16) & 0x7fffu));
-      const uint32_t mb = max8_dpp(m);
-      const float a = __uint_as_float(mb << 16);
-      uint32_t packed;
-      if (__builtin_expect(__any(a < 0x1p-90f && a > 0.0f), 0))
-        packed = encode8<true>(u, a, cell);
-      else
-        packed = encode8<false>(u, a, cell);
-      codes[ch] = packed;
-      if ((ch & 7) == 0) {
-        absmax_out[ch >> 3] = a;
-        if (DQ) {
-          const uint32_t t = mb >> 7, man = mb & 0x7fu;
-          const uint32_t sig = t ? (man | 0x80u) : man;
-          if (sig) atomicAdd(&lhist[t ? t : 1], (unsigned long long)sig);
-        }
-      }
+    for (int i = 0; i < 8; ++i) lh8[i][tid] = 0u;
+  const int64_t base = (int64_t)blockIdx.x * (QT * QU) + tid;
+  // the QU chunks of this lane, loads first; n % 64 == 0, so the 8 lanes of
+  // a block agree on validity
+  uint4 v[QU];
+#pragma unroll
+  for (int u = 0; u < QU; ++u) {
+    const int64_t ch = base + u * QT;
+    v[u] = ch < nchunks ? W[ch] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < QU; ++u) {
+    const int64_t ch = base + u * QT;
+    const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, max(w4[i] & 0x7fffu, (w4[i] >> 16) & 0x7fffu));
+    const uint32_t mb = max8_dpp(m);
+    const float a = __uint_as_float(mb << 16);
+    uint32_t packed;
+    if (__builtin_expect(__any(a < 0x1p-90f && a > 0.0f), 0))
+      packed = encode8<true>(w4, a, cell);
+    else
+      packed = encode8<false>(w4, a, cell);
+    const bool ok = ch < nchunks;
+    if (ok) codes[ch] = packed;
+    const bool leader = ok && (ch & 7) == 0;
+    if (leader) absmax_out[ch >> 3] = a;
+    if (DQ) {
+      const uint32_t t = mb >> 7, man = mb & 0x7fu;
+      const uint32_t sig = t ? (man | 0x80u) : man;
+      if (leader && sig) atomicAdd(&lh8[(tid >> 3) & 7][t ? t : 1u], sig);
     }
   }
   if (DQ) {
     __syncthreads();
-    const unsigned long long h = lhist[tid];
-    if (h) atomicAdd(&hist[tid], h);
+    unsigned long long h = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h += lh8[i][tid];
+    if (h) atomicAdd(&hist[(blockIdx.x % NHC) * 256 + tid], h);
   }
 }
 
@@ -140,59 +161,59 @@ __global__ void zero_u64_kernel(unsigned long long *p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0ull;
 }
 
-// mu = nearest float32 (ties to even) of sum_t hist[t] * 2^(t-134) / nb.
-__global__ void dq_mean_kernel(const unsigned long long *__restrict__ hist,
-                               uint32_t nb, float *__restrict__ mu_out) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  // numerator N * 2^64 in 2^-197 units, 384 bits in 32-bit limbs
+// mu = nearest float32 (ties to even) of N / nb, N the numerator in units of
+// 2^-197 scaled by 2^64, held as 12 32-bit limbs whose sums `limb` still lack
+// their carries. Executed by one lane. The long division goes 16 bits at a
+// time in fp64: each partial dividend r * 2^16 + d (r < nb < 2^32) is below
+// 2^48 and exact, the quotient is below 2^16, and an integer quotient k - e
+// (e >= 1/nb) sits more than 2^-48 relatively below k, so the correctly
+// rounded fp64 quotient never reaches k: its floor is the integer quotient.
+QL_DEV float mean_from_limbs(const unsigned long long *limb, uint32_t *sq, uint32_t nb) {
   uint32_t N[12];
-  for (int i = 0; i < 12; ++i) N[i] = 0u;
-  for (int t = 1; t < 256; ++t) {
-    const unsigned long long h = hist[t];
-    if (!h) continue;
-    const int sh = t - 1 + 64;
-    int li = sh >> 5;
-    const int bit = sh & 31;
-    // h < 2^48; h << bit spans at most 3 limbs
-    unsigned long long lo = h << bit;
-    uint32_t part[3] = {(uint32_t)lo, (uint32_t)(lo >> 32),
-                        (uint32_t)(bit ? (h >> (64 - bit)) : 0ull)};
-    unsigned long long carry = 0;
-    for (int j = 0; li + j < 12; ++j) {
-      const unsigned long long add = (j < 3 ? part[j] : 0u);
-      if (j >= 3 && carry == 0) break;
-      const unsigned long long s = (unsigned long long)N[li + j] + add + carry;
-      N[li + j] = (uint32_t)s;
-      carry = s >> 32;
-    }
-  }
+  unsigned long long carry = 0;
   bool nonzero = false;
-  for (int i = 0; i < 12; ++i) nonzero |= (N[i] != 0u);
-  if (!nonzero || nb == 0) {
-    mu_out[0] = 0.0f;
-    return;
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    const unsigned long long s = limb[i] + carry;
+    N[i] = (uint32_t)s;
+    carry = s >> 32;
+    nonzero |= N[i] != 0u;
   }
+  if (!nonzero || nb == 0) return 0.0f;
+  const double dn = (double)nb;
   uint32_t Q[12];
   unsigned long long rem = 0;
+#pragma unroll
   for (int i = 11; i >= 0; --i) {
-    const unsigned long long cur = (rem << 32) | N[i];
-    Q[i] = (uint32_t)(cur / nb);
-    rem = cur % nb;
+    uint32_t qw = 0;
+    if (rem != 0 || N[i] != 0u) {
+      const double c1 = (double)((rem << 16) | (N[i] >> 16));
+      const double q1 = floor(c1 / dn);
+      const double c2 = (c1 - q1 * dn) * 65536.0 + (double)(N[i] & 0xFFFFu);
+      const double q2 = floor(c2 / dn);
+      rem = (unsigned long long)(c2 - q2 * dn);
+      qw = ((uint32_t)q1 << 16) | (uint32_t)q2;
+    }
+    Q[i] = qw;
+    sq[i] = qw;
   }
-  int p = -1;
-  for (int i = 11; i >= 0 && p < 0; --i)
-    if (Q[i]) p = 32 * i + 31 - __builtin_clz(Q[i]);
+  int top = 0;
+#pragma unroll
+  for (int i = 1; i < 12; ++i) if (Q[i]) top = i;
+  const int p = 32 * top + 31 - __builtin_clz(sq[top]);
   const int E = p - 197;
   int e_eff = E < -126 ? -126 : E;
-  const int sh = e_eff - 23 + 197;  // bit of Q holding the float32 ulp (>= 9)
-  auto bit_at = [&](int b) -> uint32_t { return (Q[b >> 5] >> (b & 31)) & 1u; };
+  const int sh = e_eff - 23 + 197;  // bit of Q holding the float32 ulp (>= 48)
   const int li = sh >> 5, lb = sh & 31;
-  unsigned long long win = (unsigned long long)Q[li] |
-                           ((li + 1 < 12) ? ((unsigned long long)Q[li + 1] << 32) : 0ull);
+  const unsigned long long win = (unsigned long long)sq[li] |
+                                 ((unsigned long long)sq[li + 1] << 32);  // li <= 10
   uint32_t mant = (uint32_t)((win >> lb) & 0xFFFFFFull);
-  const uint32_t guard = bit_at(sh - 1);
-  bool sticky = rem != 0;
-  for (int b = 0; b < sh - 1 && !sticky; ++b) sticky = bit_at(b) != 0u;
+  const int g = sh - 1, gl = g >> 5, gb = g & 31;
+  const uint32_t gw = sq[gl];
+  const uint32_t guard = (gw >> gb) & 1u;
+  bool sticky = rem != 0 || (gw & ((1u << gb) - 1u)) != 0u;
+#pragma unroll
+  for (int i = 0; i < 12; ++i) sticky |= (i < gl) && Q[i] != 0u;
   if (guard && (sticky || (mant & 1u))) ++mant;
   uint32_t bits;
   if (E >= -126) {
@@ -205,7 +226,35 @@ __global__ void dq_mean_kernel(const unsigned long long *__restrict__ hist,
   } else {
     bits = mant;  // subnormal (or the smallest normal after rounding up)
   }
-  mu_out[0] = __uint_as_float(bits);
+  return __uint_as_float(bits);
+}
+
+// One workgroup: lane t adds the NHC copies of bucket t (sum of 8-bit
+// significands of the absmax values with bf16 exponent field t, subnormals in
+// bucket 1) and adds h * 2^(t-1+64) into the limb sums with LDS atomics.
+__global__ __launch_bounds__(256) void dq_mean_kernel(const unsigned long long *__restrict__ hist,
+                                                     uint32_t nb, float *__restrict__ mu_out) {
+  __shared__ unsigned long long limb[12];
+  __shared__ uint32_t sq[12];
+  const int tid = threadIdx.x;
+  if (tid < 12) limb[tid] = 0ull;
+  unsigned long long hc[NHC];
+#pragma unroll
+  for (int c = 0; c < NHC; ++c) hc[c] = hist[c * 256 + tid];
+  unsigned long long h = 0;
+#pragma unroll
+  for (int c = 0; c < NHC; ++c) h += hc[c];
+  __syncthreads();
+  if (tid >= 1 && h != 0ull) {
+    // h < 2^48, shift <= 318: three limbs, the last one <= 11
+    const int sh = tid - 1 + 64, li = sh >> 5, bit = sh & 31;
+    const unsigned long long lo = h << bit;
+    atomicAdd(&limb[li], lo & 0xFFFFFFFFull);
+    atomicAdd(&limb[li + 1], lo >> 32);
+    if (bit) atomicAdd(&limb[li + 2], h >> (64 - bit));
+  }
+  __syncthreads();
+  if (tid == 0) mu_out[0] = mean_from_limbs(limb, sq, nb);
 }
 
 __global__ __launch_bounds__(256) void dq_encode_kernel(
@@ -240,32 +289,32 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(
 size_t quantize_ws_bytes(int64_t n, int dq) {
   if (!dq) return 0;
   const int64_t nb = n / 64;
-  return (size_t)(ql_rup(4 * nb, 256) + 256 * 8);
+  return (size_t)(ql_rup(4 * nb, 256) + NHC * 256 * 8);
 }
 
 qlora_status launch_quantize(const uint16_t *W0, int64_t n, uint8_t *codes,
                              float *absmax_out, int dq, int8_t *q, float *s2,
                              float *mu, void *ws, hipStream_t st) {
   const int64_t nchunks = n / 8, nb = n / 64;
-  const int grid = (int)std::min<int64_t>(ql_cdiv(nchunks, QT), kMaxQuantGrid);
+  const int64_t grid = ql_cdiv(nchunks, QT * QU);
   if (!dq) {
     QlProf prof(QLORA_K_QUANTIZE, st);
-    quantize_kernel<false><<<grid, QT, 0, st>>>((const uint4 *)W0, (uint32_t *)codes,
+    quantize_kernel<false><<<(unsigned)grid, QT, 0, st>>>((const uint4 *)W0, (uint32_t *)codes,
                                                  absmax_out, nullptr, nchunks);
     QL_LAUNCH_CHECK();
     return QLORA_OK;
   }
   float *amax = (float *)ws;
   unsigned long long *hist = (unsigned long long *)((char *)ws + ql_rup(4 * nb, 256));
-  zero_u64_kernel<<<1, 256, 0, st>>>(hist, 256);
+  zero_u64_kernel<<<1, 256, 0, st>>>(hist, NHC * 256);
   {
     QlProf prof(QLORA_K_QUANTIZE, st);
-    quantize_kernel<true><<<grid, QT, 0, st>>>((const uint4 *)W0, (uint32_t *)codes, amax,
+    quantize_kernel<true><<<(unsigned)grid, QT, 0, st>>>((const uint4 *)W0, (uint32_t *)codes, amax,
                                                 hist, nchunks);
   }
   {
     QlProf prof(QLORA_K_DOUBLE_QUANT, st);
-    dq_mean_kernel<<<1, 64, 0, st>>>(hist, (uint32_t)nb, mu);
+    dq_mean_kernel<<<1, 256, 0, st>>>(hist, (uint32_t)nb, mu);
     dq_encode_kernel<<<(unsigned)ql_cdiv(nb, 256), 256, 0, st>>>(amax, nb, mu, q, s2);
   }
   QL_LAUNCH_CHECK();

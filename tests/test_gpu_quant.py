@@ -71,6 +71,22 @@ def test_quantize_ragged_group_count(ops):
     _check_exact(ops, synth.normal_bf16((72, 192), 0.02, 77), True)
 
 
+def _scaled_bf16(shape, scale, seed):
+    w = synth.normal_bf16(shape, 1.0, seed)
+    f = onf4.bf16_bits_to_f32(w) * np.float32(scale)
+    return onf4.f32_to_bf16_bits(f.astype(np.float32))
+
+
+def test_quantize_dq_subnormal_mean(ops):
+    # every absmax is a bf16 subnormal or just above: the mean is subnormal
+    _check_exact(ops, _scaled_bf16((256, 512), 2.0 ** -130, 91), True)
+
+
+def test_quantize_dq_huge_mean(ops):
+    # absmax values near 2^126: the mean's numerator uses the top limbs
+    _check_exact(ops, _scaled_bf16((256, 512), 2.0 ** 124, 92), True)
+
+
 def _sweep_weight():
     """Every bf16 pattern with |w| <= a, for absmax values spanning normal,
     subnormal, tiny and huge magnitudes; the first element of each block is a
