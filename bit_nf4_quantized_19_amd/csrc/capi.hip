@@ -35,6 +35,7 @@ qlora_status check_weight(const qlora_nf4_weight *w, bool need_outputs_only) {
   if (!w->codes || !aligned16(w->codes)) return QLORA_ERR_INVALID_ARG;
   if (w->double_quant) {
     if (!w->absmax_q || !w->absmax_scale || !w->absmax_offset) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(w->absmax_q)) return QLORA_ERR_INVALID_ARG;  // read as dwords
     if (((uintptr_t)w->absmax_scale & 3u) || ((uintptr_t)w->absmax_offset & 3u))
       return QLORA_ERR_INVALID_ARG;
   } else {

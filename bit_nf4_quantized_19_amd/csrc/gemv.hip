@@ -2,18 +2,39 @@
 //
 // Same layer as the fused GEMM (QLoRA glossary, Ultralytics, "QLoRA 的工作原理",
 // forward paragraph): Y = X W'^T + s H B^T. With M <= 16 the time is the HBM
-// read of the packed codes (0.5 byte per weight), so the kernel moves as few
-// bytes and issues as few VALU operations per weight as it can:
+// read of the packed codes (0.5 byte per weight), so the kernel reads them in
+// whole 128-byte lines, keeps all of a wave's loads in flight at once, and
+// spends little VALU per weight:
 //   * The per-block scale is factored out of each 64-wide partial sum,
-//     sum_b a'_b * sum_{c in b} level[code_c] x_c; the 64-term inner sums run
-//     on MFMA (16x16x32 bf16, tokens padded to 16) with the levels as bf16
-//     operands looked up two at a time from a 256-entry byte -> (level, level)
-//     LDS table. This equals X W'^T up to float32/bf16 rounding (the weights
-//     are rounded to bf16 at the level instead of after the product).
-//   * Each wave streams 16 weight rows; a workgroup covers 64 rows and one of
-//     S contraction splits; partial sums go to a small float32 buffer and a
-//     second kernel adds the splits in a fixed order, the rank-r LoRA term in
-//     float32, and rounds to bf16.
+//     sum_b a'_b * sum_{c in b} level[code_c] x_c. The 64-term inner sums run
+//     on MFMA (16x16x32 bf16). This equals X W'^T up to float32/bf16 rounding
+//     (the weights are rounded to bf16 at the level instead of after the
+//     product).
+//   * Operand layout: lane (n, q) of a wave (n = lane % 16, q = lane / 16)
+//     holds whole blocks 4c + q (c = 0..3) of weight row n, 32 bytes each,
+//     read as two 16-byte loads; a pair of load instructions thus covers
+//     full 128-byte lines of 16 rows. At MFMA step s the lane supplies codes
+//     8s..8s+7 of its block as the B operand (column n). A row m = 4g + t
+//     carries token 4 tp + t on the k-slots of lane group g only (zeros
+//     elsewhere), so D[4q + t][n] is the partial sum of block 4c + q for that
+//     token, held by the lane that owns the block and its scale. The four
+//     lane groups of a row are added once at the end.
+//   * Decoding: one code byte gives two bf16 levels through a 256-entry LDS
+//     table replicated 32 times (entry e, copy c at byte e*256 + 4c). One
+//     byte permute builds the address (code byte in bits 8-15, 4*(lane%32)
+//     in bits 0-7), and each 32-lane half of a read hits 32 distinct banks.
+//   * The X slice (up to 16 tokens x 1024 columns) lives in the upper halves
+//     of the table rows, placed so that a lane's A operand for chunk c, step s
+//     is at a per-lane base plus an immediate offset; lanes outside their
+//     token group read a zero region at the same offsets. No VALU is spent on
+//     A addresses.
+//   * Work unit: 16 weight rows x one slice of 16 blocks (1024 columns).
+//     About one workgroup of 8 waves per compute unit; each workgroup serves
+//     one slice (table and X slice built once) and each wave takes up to two
+//     units, whose loads are all issued before the table is built and whose
+//     MFMA chains are interleaved. Partial sums per slice go to a float32
+//     buffer; a second kernel adds the slices in a fixed order, the rank-r
+//     LoRA term in float32, and rounds to bf16.
 #include <algorithm>
 
 #include "kernels.h"
@@ -21,7 +42,15 @@
 
 namespace {
 
-constexpr int GT = 256;
+constexpr int GW = 8;            // waves per workgroup, one row group of 16 rows each
+constexpr int GT = 64 * GW;
+constexpr int GX = 2048 / GT;    // X chunks (16 tokens x 16 blocks x 8) per thread
+constexpr int GB = 16;           // blocks per slice (1024 columns)
+// LDS: 256 rows of 256 bytes (table copies in bytes 0-127, X in 128-255),
+// then the zero region read by lanes outside their token group
+constexpr uint32_t ZBASE = 65536 + 64;
+constexpr uint32_t ZBYTES = 15 * 256 + 64 + 16;
+constexpr int LDS_BYTES = (int)(ZBASE + ZBYTES);
 __constant__ uint32_t c_levels_v[16] = NF4_LEVEL_BITS;
 
 struct GemvArgs {
@@ -30,95 +59,226 @@ struct GemvArgs {
   int64_t d, k;
   const uint16_t *X;
   int64_t M;
-  int64_t blocks_per_split;
-  float *part;  // [S][M][d]
+  int64_t nb;      // blocks of the weight (d k / 64)
+  int64_t ngroups; // row groups of 16 rows
+  int G;           // workgroups per slice
+  int rpw;         // row groups per workgroup, <= 2 GW (the last ones may be past the end)
+  float *part;     // [S][M][d]
 };
 
-__global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
-  __shared__ uint32_t lut[256];
-  {
-    const int b = threadIdx.x;
-    const float hi = __uint_as_float(c_levels_v[b >> 4]);
-    const float lo = __uint_as_float(c_levels_v[b & 15]);
-    lut[b] = ql::pack_bf16x2(hi, lo);  // element 2j (high nibble) first
-  }
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t j0 = (int64_t)blockIdx.x * 64 + 16 * wave;
-  const int64_t split = blockIdx.y;
-  const int64_t nbr = g.k >> 6;  // blocks per row
-  const int64_t b_lo = split * g.blocks_per_split;
-  const int64_t b_hi = min(nbr, b_lo + g.blocks_per_split);
-  if (j0 >= g.d) return;  // whole wave idle (d % 16 == 0)
+// LDS byte offset of X[token 4 tp + t][slice block 4c + g][8s .. 8s+7]: row
+// tp*64 + g*16 + c*4 + s/2, upper half, 16-byte slot (s%2)*4 + t
+QL_DEV constexpr uint32_t xa_base(int tp, int g, int t) {
+  return (uint32_t)((tp * 64 + g * 16) * 256 + 128 + t * 16);
+}
+QL_DEV constexpr uint32_t xa_imm(int c, int s) {
+  return (uint32_t)((c * 4 + (s >> 1)) * 256 + (s & 1) * 64);
+}
 
-  const int r16 = lane & 15, kq = lane >> 4;
-  const int64_t arow = j0 + r16;            // weight row this lane feeds (A operand)
-  const bool arow_ok = arow < g.d;
-  const int64_t xrow = r16;                 // token row this lane feeds (B operand)
-  const bool xrow_ok = xrow < g.M;
-  // rows of the accumulator this lane holds: j0 + 4*kq + i
-  const float mu = g.sc.dq ? g.sc.mu[0] : 0.0f;
-  int64_t grow[4];
-  float s2lo[4], s2hi[4];
-  int64_t glo[4];
+// Registers of one work unit (16 rows x one slice) of a wave.
+struct GUnit {
+  uint4 cw[4][2];   // lane (n, q): blocks 4c + q of row n, 32 bytes each
+  uint32_t qw[5];   // int8 scale codes of the row's slice (aligned dwords)
+  float araw[4];    // absmax of blocks 4c + q (no double quantisation)
+  float s2lo, s2hi;
+  int64_t blk0;     // first block of the row's slice
+  int64_t row0;     // first row of the unit
+};
+
+template <bool DQ, bool FULL>
+QL_DEV void unit_load(const GemvArgs &g, GUnit &u, int64_t rg, int64_t b0, int nblk, int n,
+                      int q) {
+  const int64_t nbr = g.k >> 6;
+  u.row0 = rg * 16;
+  const int64_t row = min(u.row0 + n, g.d - 1);
+  u.blk0 = row * nbr + b0;
+  if (DQ) {
+    u.s2lo = g.sc.s2[u.blk0 >> 8];
+    u.s2hi = g.sc.s2[(u.blk0 + nblk - 1) >> 8];
+    // the row's int8 codes from the 5 aligned dwords around them (the code
+    // array has a multiple of 8 bytes, so a clamped dword index stays in it)
+    const uint32_t *qp = (const uint32_t *)g.sc.q;
+    const int64_t w0 = u.blk0 >> 2, wlast = (g.nb >> 2) - 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    grow[i] = j0 + 4 * kq + i;
-    const int64_t r = grow[i] < g.d ? grow[i] : (g.d - 1);
-    grow[i] = r;
-    if (g.sc.dq) {
-      glo[i] = (r * nbr + b_lo) >> 8;
-      const int64_t ghi = (r * nbr + max(b_hi - 1, b_lo)) >> 8;
-      s2lo[i] = g.sc.s2[glo[i]];
-      s2hi[i] = g.sc.s2[ghi];
-    }
+    for (int j = 0; j < 5; ++j) u.qw[j] = qp[min(w0 + j, wlast)];
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      u.araw[c] = g.sc.absmax[u.blk0 + (FULL ? 4 * c + q : min(4 * c + q, nblk - 1))];
   }
+  // blocks past the end of a ragged slice re-read the last block; their X
+  // chunks are zero
+  const uint8_t *crow = g.codes + row * (g.k >> 1) + b0 * 32;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int bb = FULL ? 4 * c + q : min(4 * c + q, nblk - 1);
+    u.cw[c][0] = *(const uint4 *)(crow + 32 * bb);
+    u.cw[c][1] = *(const uint4 *)(crow + 32 * bb + 16);
+  }
+}
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+// MFMA steps of NU units of a wave (same slice, so they share the A
+// operand reads; their independent chains interleave). D[4q + t][n] = partial
+// sum of block 4c + q for token 4tp + t. Writes the units' partial sums.
+template <bool DQ, int TP, int NU>
+QL_DEV void unit_compute(const GemvArgs &g, const GUnit *const (&us)[NU],
+                         const unsigned char *smem, const uint32_t (&abase)[TP], uint32_t lcopy,
+                         float mu, int n, int q, int64_t slice) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  const uint8_t *crow = g.codes + ((arow_ok ? arow : 0) * g.k >> 1);
-  const uint16_t *xr = g.X + (xrow_ok ? xrow : 0) * g.k;
-
-#pragma unroll 4
-  for (int64_t b = b_lo; b < b_hi; ++b) {
-    const int64_t kb = b << 6;
-    uint32_t c0 = 0, c1 = 0;
-    if (arow_ok) {
-      c0 = *(const uint32_t *)(crow + ((kb + 8 * kq) >> 1));
-      c1 = *(const uint32_t *)(crow + ((kb + 32 + 8 * kq) >> 1));
-    }
-    uint4 x0 = ql::zero4(), x1 = ql::zero4();
-    if (xrow_ok) {
-      x0 = *(const uint4 *)(xr + kb + 8 * kq);
-      x1 = *(const uint4 *)(xr + kb + 32 + 8 * kq);
-    }
-    uint4 a0, a1;
-    a0.x = lut[c0 & 255]; a0.y = lut[(c0 >> 8) & 255];
-    a0.z = lut[(c0 >> 16) & 255]; a0.w = lut[c0 >> 24];
-    a1.x = lut[c1 & 255]; a1.y = lut[(c1 >> 8) & 255];
-    a1.z = lut[(c1 >> 16) & 255]; a1.w = lut[c1 >> 24];
-    f32x4 p = ql::mfma16(a0, x0, zero);
-    p = ql::mfma16(a1, x1, p);
+  f32x4 acc[NU][TP];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t blk = grow[i] * nbr + b;
-      float ap;
-      if (g.sc.dq) {
-        const float s2 = ((blk >> 8) == glo[i]) ? s2lo[i] : s2hi[i];
-        ap = (float)g.sc.q[blk] * s2 + mu;
-      } else {
-        ap = g.sc.absmax[blk];
+  for (int v = 0; v < NU; ++v)
+#pragma unroll
+    for (int tp = 0; tp < TP; ++tp) acc[v][tp] = zero;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    f32x4 p[NU][TP];
+#pragma unroll
+    for (int v = 0; v < NU; ++v)
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) p[v][tp] = zero;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      uint4 bop[NU];
+#pragma unroll
+      for (int v = 0; v < NU; ++v) {
+        const uint4 &h = us[v]->cw[c][s >> 2];
+        const uint32_t w = (s & 3) == 0 ? h.x : (s & 3) == 1 ? h.y : (s & 3) == 2 ? h.z : h.w;
+        bop[v].x = *(const uint32_t *)(smem + __builtin_amdgcn_perm(w, lcopy, 0x0C0C0400u));
+        bop[v].y = *(const uint32_t *)(smem + __builtin_amdgcn_perm(w, lcopy, 0x0C0C0500u));
+        bop[v].z = *(const uint32_t *)(smem + __builtin_amdgcn_perm(w, lcopy, 0x0C0C0600u));
+        bop[v].w = *(const uint32_t *)(smem + __builtin_amdgcn_perm(w, lcopy, 0x0C0C0700u));
       }
-      acc[i] = fmaf(ap, p[i], acc[i]);
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) {
+        const uint4 aop = *(const uint4 *)(smem + abase[tp] + xa_imm(c, s));
+#pragma unroll
+        for (int v = 0; v < NU; ++v) p[v][tp] = ql::mfma16(aop, bop[v], p[v][tp]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NU; ++v) {
+      // scale of block 4c + q of row n
+      const GUnit &u = *us[v];
+      float ap;
+      if (DQ) {
+        const float s2 = ((u.blk0 + 4 * c + q) >> 8) == (u.blk0 >> 8) ? u.s2lo : u.s2hi;
+        const uint32_t win =
+            __builtin_amdgcn_alignbyte(u.qw[c + 1], u.qw[c], (uint32_t)(u.blk0 & 3));
+        const int qv = (int)(int8_t)(win >> (8 * q));
+        ap = (float)qv * s2 + mu;
+      } else {
+        ap = u.araw[c];
+      }
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[v][tp][i] = fmaf(ap, p[v][tp][i], acc[v][tp][i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the chunks' register sets apart
+  }
+#pragma unroll
+  for (int v = 0; v < NU; ++v) {
+    // add the four lane groups (blocks 4c + q) of each row
+#pragma unroll
+    for (int tp = 0; tp < TP; ++tp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = acc[v][tp][i];
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        acc[v][tp][i] = x;
+      }
+    const int64_t row0 = us[v]->row0;
+    if (q == 0 && row0 + n < g.d) {
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 4 * tp + i;
+          if (t < g.M) g.part[(slice * g.M + t) * g.d + row0 + n] = acc[v][tp][i];
+        }
     }
   }
-  // lane holds D[4*kq + i][r16] = partial Y[token r16][row j0 + 4kq + i]
-  if (r16 < g.M) {
+}
+
+// Workgroup (x, slice) takes row groups x, x + G, x + 2G, ... (at most 2 GW
+// of them) of one slice; wave w takes the workgroup's row groups w and
+// w + GW, both loaded before the table is built, then computed together. The
+// table and the X slice are built once per workgroup.
+template <bool DQ, int TP, bool FULL>
+__global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
+  __shared__ __align__(16) unsigned char smem[LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, q = lane >> 4;
+  const int64_t nbr = g.k >> 6;
+  const int64_t slice = blockIdx.y;
+  const int64_t b0 = slice * GB;
+  const int nblk = FULL ? GB : (int)min<int64_t>(GB, nbr - b0);
+  auto rg_of = [&](int j) -> int64_t { return (int64_t)blockIdx.x + (int64_t)g.G * j; };
+
+  // Global loads in the order they are used: table entry, X slice, first unit.
+  // 1. table entry written by this lane: byte e -> (level[e >> 4], level[e & 15]);
+  //    the levels are read with uniform (scalar) loads and picked per lane,
+  //    so no vector-memory wait stands before the table is built
+  const int te = tid & 255;
+  uint32_t lv_hi = c_levels_v[0], lv_lo = c_levels_v[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t row = j0 + 4 * kq + i;
-      if (row < g.d) g.part[(split * g.M + r16) * g.d + row] = acc[i];
-    }
+  for (int i = 1; i < 16; ++i) {
+    const uint32_t v = c_levels_v[i];
+    lv_hi = (te >> 4) == i ? v : lv_hi;
+    lv_lo = (te & 15) == i ? v : lv_lo;
+  }
+  // 2. X slice: chunk idx -> token m, slice block b, 8-column chunk s
+  uint4 xv[GX];
+#pragma unroll
+  for (int i = 0; i < GX; ++i) {
+    const int idx = tid + GT * i;
+    const int m = idx >> 7, b = (idx >> 3) & 15, sc8 = idx & 7;
+    const bool ok = m < g.M && b < nblk;  // else read X[0][0..7], stored as zeros
+    xv[i] = *(const uint4 *)(g.X + (ok ? m * g.k + (b0 + b) * 64 + 8 * sc8 : 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const float mu = DQ ? g.sc.mu[0] : 0.0f;
+  // 3. the wave's two units (row groups wave and wave + GW of this
+  //    workgroup), loaded unconditionally (clamped) so every wait is exact
+  const int64_t rga = rg_of(wave), rgb = rg_of(wave + GW);
+  const bool has_a = wave < g.rpw && rga < g.ngroups;
+  const bool has_b = wave + GW < g.rpw && rgb < g.ngroups;
+  GUnit ua, ub;
+  unit_load<DQ, FULL>(g, ua, min(rga, g.ngroups - 1), b0, nblk, n, q);
+  unit_load<DQ, FULL>(g, ub, min(rgb, g.ngroups - 1), b0, nblk, n, q);
+  // 4. table (bf16 pair, even element in the low half), 32 copies per entry;
+  //    X chunks; zero region
+  {
+    const uint32_t v = ql::pack_bf16x2(__uint_as_float(lv_hi), __uint_as_float(lv_lo));
+    const uint4 v4 = make_uint4(v, v, v, v);
+    constexpr int PER = 2048 / GT;  // 16-byte stores per lane
+    unsigned char *t = smem + te * 256 + 16 * PER * (tid >> 8);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) *(uint4 *)(t + 16 * i) = v4;
+  }
+#pragma unroll
+  for (int i = 0; i < GX; ++i) {
+    const int idx = tid + GT * i;
+    const int m = idx >> 7, b = (idx >> 3) & 15, sc8 = idx & 7;
+    const bool ok = m < g.M && b < nblk;
+    *(uint4 *)(smem + xa_base(m >> 2, b & 3, m & 3) + xa_imm(b >> 2, sc8)) = ok ? xv[i] : ql::zero4();
+  }
+  if (tid < (int)(ZBYTES / 16)) *(uint4 *)(smem + ZBASE + 16 * tid) = ql::zero4();
+  __syncthreads();
+
+  const uint32_t lcopy = 4u * (uint32_t)(lane & 31);
+  const bool a_on = (n >> 2) == q;  // lane group q carries token rows 4q..4q+3
+  uint32_t abase[TP];
+#pragma unroll
+  for (int tp = 0; tp < TP; ++tp) abase[tp] = a_on ? xa_base(tp, q, n & 3) : ZBASE;
+  if (has_b) {  // has_b implies has_a
+    const GUnit *const both[2] = {&ua, &ub};
+    unit_compute<DQ, TP, 2>(g, both, smem, abase, lcopy, mu, n, q, slice);
+  } else if (has_a) {
+    const GUnit *const one[1] = {&ua};
+    unit_compute<DQ, TP, 1>(g, one, smem, abase, lcopy, mu, n, q, slice);
   }
 }
 
@@ -138,36 +298,59 @@ __global__ __launch_bounds__(256) void gemv_epilogue_kernel(
 
 }  // namespace
 
-static int64_t gemv_splits(int64_t d, int64_t k) {
-  const int64_t nbr = k >> 6;
-  const int64_t wgs = ql_cdiv(d, 64);
-  int64_t S = ql_cdiv(1024, wgs);
-  S = std::min<int64_t>(S, std::max<int64_t>(1, nbr / 8));  // >= 8 blocks per wave
-  S = std::max<int64_t>(S, ql_cdiv(nbr, 256));              // <= 256 blocks per split
-  return std::max<int64_t>(S, 1);
-}
+static int64_t gemv_splits(int64_t k) { return ql_cdiv(k >> 6, GB); }
 
 size_t gemv_part_bytes(int64_t d, int64_t k, int64_t M) {
-  return (size_t)(gemv_splits(d, k) * M * d * 4);
+  return (size_t)(gemv_splits(k) * M * d * 4);
 }
 
 qlora_status launch_gemv_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, int64_t k,
                              const uint16_t *X, int64_t M, const uint16_t *Bp,
                              const float *H, int rp, float s, float *part, uint16_t *Y,
                              hipStream_t st) {
-  const int64_t nbr = k >> 6;
-  const int64_t S = gemv_splits(d, k);
-  const int64_t bps = ql_cdiv(nbr, S);
-  GemvArgs g{codes, sc, d, k, X, M, bps, part};
-  dim3 grid((unsigned)ql_cdiv(d, 64), (unsigned)ql_cdiv(nbr, bps));
+  if (M < 1 || M > 16) return QLORA_ERR_INVALID_ARG;
+  static int ncu = 0;
+  if (ncu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        ncu < 1)
+      ncu = 256;
+  }
+  const int64_t S = gemv_splits(k);
+  const int64_t ngroups = ql_cdiv(d, 16);
+  // about one workgroup per compute unit, each slice served by G of them,
+  // and at most two row groups per wave
+  const int64_t G = std::min<int64_t>(
+      ngroups, std::max<int64_t>(std::max<int64_t>(1, ncu / S), ql_cdiv(ngroups, 2 * GW)));
+  const int64_t rpw = ql_cdiv(ngroups, G);
+  if (S > 65535 || G > (int64_t(1) << 30)) return QLORA_ERR_UNSUPPORTED;
+  GemvArgs g{codes, sc, d, k, X, M, d * (k >> 6), ngroups, (int)G, (int)rpw, part};
+  dim3 grid((unsigned)G, (unsigned)S);
   {
     QlProf prof(QLORA_K_GEMV, st);
-    nf4_gemv_kernel<<<grid, GT, 0, st>>>(g);
+    const int tp = (int)ql_cdiv(M, 4);
+    // every slice is full when k is a multiple of 1024
+    const bool full = (k % (64 * GB)) == 0;
+#define QL_GEMV3(DQV, TPV)                                              \
+  if (full)                                                             \
+    nf4_gemv_kernel<DQV, TPV, true><<<grid, GT, 0, st>>>(g);            \
+  else                                                                  \
+    nf4_gemv_kernel<DQV, TPV, false><<<grid, GT, 0, st>>>(g);
+#define QL_GEMV(TPV)                                                    \
+  if (sc.dq) {                                                          \
+    QL_GEMV3(true, TPV)                                                 \
+  } else {                                                              \
+    QL_GEMV3(false, TPV)                                                \
+  }
+    if (tp == 1) { QL_GEMV(1) } else if (tp == 2) { QL_GEMV(2) } else if (tp == 3) { QL_GEMV(3) } else { QL_GEMV(4) }
+#undef QL_GEMV
+#undef QL_GEMV3
   }
   {
     QlProf prof(QLORA_K_GEMV_EPILOGUE, st);
     gemv_epilogue_kernel<<<(unsigned)ql_cdiv(M * d, 256), 256, 0, st>>>(
-        part, (int)grid.y, M, d, Bp, H, rp, s, Y);
+        part, (int)S, M, d, Bp, H, rp, s, Y);
   }
   QL_LAUNCH_CHECK();
   return QLORA_OK;

@@ -112,6 +112,19 @@ def test_ragged_shapes(ops, d, k, M, r, alpha):
     assert rel_frob(g["H"], o["H"]) < 1e-5
 
 
+# ---- GEMV slices of 1024 columns: full, ragged last slice, absmax path ----
+@pytest.mark.parametrize("d,k,M,dq", [
+    (48, 1088, 3, False),         # one full slice + a one-block slice
+    (40, 2112, 16, True),         # two full slices + one block, ragged rows
+    (24, 2112, 7, False),         # rows < one wave of 16 + 8
+    (16, 1024, 1, False),         # exactly one slice
+    (8, 960, 16, True),           # one partial slice of 15 blocks
+])
+def test_gemv_slices(ops, d, k, M, dq):
+    g, o = _case(ops, d, k, M, 16, 32.0, dq, seed=d + k + M, bwd=False)
+    _assert_close(g, o, ["Y"])
+
+
 # ---- config 3: decode-shaped GEMV, fwd only ---------------------------------
 _GEMV_CACHE = {}
 
