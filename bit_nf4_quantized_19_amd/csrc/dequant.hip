@@ -4,9 +4,12 @@
 // bf16 before merging).
 //
 // w' = bf16_rne(fl(level[code] * a')), a' = fl(fl(q * s2) + mu) or absmax.
-// One lane per 8 codes (4 bytes in, 16 bytes out), 8 lanes per block;
-// levels come from a 16-entry LDS table. Memory-bound: 2.516 bytes moved per
-// weight (0.5 code + block scale share in, 2 out).
+// Memory-bound: 2.516 bytes moved per weight (0.5 code + block scale share in,
+// 2 out). A lane owns 4-byte code words (8 weights, one 16-byte output store);
+// a wave's load and store instructions each cover one contiguous run (256
+// bytes of codes, 1 KB of output), and every lane issues all its loads (DU
+// code words and their block-scale inputs) before the first use. Levels come
+// from a 16-entry LDS table (any lookup pattern is conflict-free).
 #include <algorithm>
 
 #include "kernels.h"
@@ -14,20 +17,44 @@
 
 namespace {
 
-constexpr int DT = 256;
+constexpr int DT = 256;  // threads per workgroup
+constexpr int DU = 8;    // code words per lane
 __constant__ uint32_t c_levels[16] = NF4_LEVEL_BITS;
 
+template <bool DQ>
 __global__ __launch_bounds__(DT) void dequant_kernel(const uint32_t *__restrict__ codes,
                                                      ql::ScaleSrc sc, int64_t nchunks,
                                                      uint4 *__restrict__ out) {
   __shared__ float lv[16];
   if (threadIdx.x < 16) lv[threadIdx.x] = __uint_as_float(c_levels[threadIdx.x]);
+  const int lane = threadIdx.x & 63;
+  const int64_t w0 = ((int64_t)blockIdx.x * (DT / 64) + (threadIdx.x >> 6)) * (64 * DU);
+  // loads: code words, then their scale inputs; indices past the end are
+  // clamped (their results are not stored)
+  uint32_t cw[DU];
+  int64_t idx[DU];
+#pragma unroll
+  for (int i = 0; i < DU; ++i) {
+    idx[i] = w0 + 64 * i + lane;
+    cw[i] = codes[min(idx[i], nchunks - 1)];
+  }
+  float sa[DU], sb[DU];
+#pragma unroll
+  for (int i = 0; i < DU; ++i) {
+    const int64_t blk = min(idx[i], nchunks - 1) >> 3;
+    if (DQ) {
+      sa[i] = (float)sc.q[blk];
+      sb[i] = sc.s2[blk >> 8];
+    } else {
+      sa[i] = sc.absmax[blk];
+    }
+  }
+  const float mu = DQ ? sc.mu[0] : 0.0f;
   __syncthreads();
-  const float mu = sc.dq ? sc.mu[0] : 0.0f;
-  const int64_t stride = (int64_t)gridDim.x * DT;
-  for (int64_t ch = (int64_t)blockIdx.x * DT + threadIdx.x; ch < nchunks; ch += stride) {
-    const uint32_t c = codes[ch];
-    const float ap = ql::block_scale(sc, ch >> 3, mu);
+#pragma unroll
+  for (int i = 0; i < DU; ++i) {
+    const float ap = DQ ? sa[i] * sb[i] + mu : sa[i];
+    const uint32_t c = cw[i];
     float f[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -39,7 +66,7 @@ __global__ __launch_bounds__(DT) void dequant_kernel(const uint32_t *__restrict_
     o.y = ql::pack_bf16x2(f[2], f[3]);
     o.z = ql::pack_bf16x2(f[4], f[5]);
     o.w = ql::pack_bf16x2(f[6], f[7]);
-    out[ch] = o;
+    if (idx[i] < nchunks) out[idx[i]] = o;
   }
 }
 
@@ -48,9 +75,15 @@ __global__ __launch_bounds__(DT) void dequant_kernel(const uint32_t *__restrict_
 qlora_status launch_dequantize(const uint8_t *codes, ql::ScaleSrc sc, int64_t n,
                                uint16_t *out, hipStream_t st) {
   const int64_t nchunks = n / 8;
-  const int grid = (int)std::min<int64_t>(ql_cdiv(nchunks, DT), 8192);
+  const int64_t grid = ql_cdiv(nchunks, (int64_t)DT * DU);
+  if (grid > 0x7fffffff) return QLORA_ERR_UNSUPPORTED;
   QlProf prof(QLORA_K_DEQUANTIZE, st);
-  dequant_kernel<<<grid, DT, 0, st>>>((const uint32_t *)codes, sc, nchunks, (uint4 *)out);
+  if (sc.dq)
+    dequant_kernel<true><<<(unsigned)grid, DT, 0, st>>>((const uint32_t *)codes, sc, nchunks,
+                                                       (uint4 *)out);
+  else
+    dequant_kernel<false><<<(unsigned)grid, DT, 0, st>>>((const uint32_t *)codes, sc, nchunks,
+                                                        (uint4 *)out);
   QL_LAUNCH_CHECK();
   return QLORA_OK;
 }

@@ -3,67 +3,167 @@
 // Day-25 notes 2.6 (W_merged = W0 + B A) and 6.2 (scale alpha/r); LLM
 // tutorial ch. 3, 3.8 and QLoRA glossary "权衡": a 4-bit base is dequantised
 // to 16 bits before merging. Here
-//     W_m = bf16(fl(w' + fl(s * sum_t B[j][t] A[t][c])))
-// with w' the bf16 dequantised weight and the rank-r sum in float32 (FMA,
-// t ascending). Workgroup tile: 32 rows x 64 columns; the A columns and B
-// rows of the tile are staged in LDS; each lane produces 8 consecutive
-// outputs from one 4-byte code word.
+//     W_m = bf16(fl(w' + fl(s * (B A)[j][c])))
+// with w' the bf16 dequantised weight and the rank-r product summed in
+// float32 (exact bf16 products, MFMA accumulation order).
+//
+// Workgroup tile: 4 waves x 32 rows, MC = 256 columns.
+//  * A^T of the tile's columns (all ranks, zero-padded to a multiple of 16)
+//    is staged once in LDS; the column pitch (2 rp + 16 bytes, an odd number
+//    of 16-byte slots) keeps the operand reads conflict-free.
+//  * Each wave keeps the B entries of its 32 rows in registers and walks the
+//    tile in 32-column blocks: 32x32x16 bf16 MFMAs give D[c][j] = (B A)[j][c]
+//    with lane (j, h) holding columns 8g + 4h .. 8g + 4h + 3 (g = 0..3) of
+//    row j, exactly the columns whose code nibbles it reads, so the update is
+//    applied straight from the accumulators: level lookup, block scale, bf16
+//    rounding, add s (B A), round. The bf16 results pass through a per-wave
+//    LDS staging area so that the global stores are whole 128-byte lines.
+//  * All global loads of a wave (its rows' code words and block-scale
+//    inputs for the whole tile, its B rows) are issued before the barrier.
+// HBM traffic per weight: 0.5 code byte + scale share in, 2 bytes out; A is
+// read once per 128 rows.
 #include "kernels.h"
 #include "nf4_tables.h"
 
 namespace {
 
-constexpr int MR = 32, MC = 64, MAXR = 128;
+constexpr int MC = 256, MT = 256, MNB = MC / 32;  // tile columns, threads, column blocks
+constexpr int MAXRP = 128;
 __constant__ uint32_t c_levels_m[16] = NF4_LEVEL_BITS;
 
-__global__ __launch_bounds__(256) void merge_kernel(const uint8_t *__restrict__ codes,
-                                                    ql::ScaleSrc sc, int64_t d, int64_t k,
-                                                    const uint16_t *__restrict__ A,
-                                                    const uint16_t *__restrict__ B, int r,
-                                                    float s, uint16_t *__restrict__ Wm) {
-  __shared__ float As[MAXR][MC];  // A[t][c0..c0+63]
-  __shared__ float Bs[MR][MAXR];  // B[j0..j0+31][t]
-  __shared__ float lv[16];
-  const int tid = threadIdx.x;
-  const int64_t j0 = (int64_t)blockIdx.y * MR, c0 = (int64_t)blockIdx.x * MC;
-  if (tid < 16) lv[tid] = __uint_as_float(c_levels_m[tid]);
-  for (int e = tid; e < r * MC; e += 256) {
-    const int t = e / MC, c = e % MC;
-    As[t][c] = (c0 + c < k) ? ql::bf16_to_f(A[(int64_t)t * k + c0 + c]) : 0.0f;
+struct MergeArgs {
+  const uint8_t *codes;
+  ql::ScaleSrc sc;
+  int64_t d, k;
+  const uint16_t *A, *B;
+  int r, rp;
+  float s;
+  uint16_t *Wm;
+};
+
+template <bool DQ, int NCH>
+__global__ __launch_bounds__(MT) void merge_kernel(MergeArgs g) {
+  constexpr int RP = 16 * NCH;            // padded rank
+  constexpr int PITCH = 2 * RP + 16;      // bytes per A^T column
+  __shared__ __align__(16) unsigned char s_at[MC * PITCH];
+  __shared__ __align__(16) unsigned char s_stg[4 * 32 * 128];  // per-wave output staging
+  __shared__ float s_lv[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t c0 = (int64_t)blockIdx.x * MC;
+  const int64_t j = (int64_t)blockIdx.y * 128 + 32 * wave + l32;  // this lane's row
+  const int64_t jc = min(j, g.d - 1);
+  if (tid < 16) s_lv[tid] = __uint_as_float(c_levels_m[tid]);
+
+  // 1. A^T chunk loads: thread (t = tid % 16, 16-column segment tid / 16),
+  //    one 16-rank chunk per pass
+  uint4 av[NCH][2];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    const int t = 16 * ch + (tid & 15);
+    const int64_t col = c0 + 16 * (tid >> 4);
+    av[ch][0] = ql::zero4();
+    av[ch][1] = ql::zero4();
+    if (t < g.r && col < g.k) {  // k % 64 == 0: the 16 columns are all in range
+      const uint16_t *src = g.A + (int64_t)t * g.k + col;
+      av[ch][0] = *(const uint4 *)src;
+      av[ch][1] = *(const uint4 *)(src + 8);
+    }
   }
-  for (int e = tid; e < MR * r; e += 256) {
-    const int jj = e / r, t = e % r;
-    Bs[jj][t] = (j0 + jj < d) ? ql::bf16_to_f(B[(j0 + jj) * r + t]) : 0.0f;
+  // 2. this lane's code words: row j, 32-column block b = 16 bytes (clamped
+  //    in range; results of rows past d or columns past k are not stored)
+  const int64_t kb = g.k >> 1;  // code bytes per row
+  uint4 cw[MNB];
+#pragma unroll
+  for (int b = 0; b < MNB; ++b)
+    cw[b] = *(const uint4 *)(g.codes + jc * kb + min(c0 / 2 + 16 * b, kb - 16));
+  // block scales: 32-column block b lies in 64-column block (c0 + 32 b) / 64
+  float sa[MNB / 2], sb[MNB / 2];
+  const int64_t nbr = g.k >> 6;
+#pragma unroll
+  for (int b2 = 0; b2 < MNB / 2; ++b2) {
+    const int64_t blk = jc * nbr + min(c0 / 64 + b2, nbr - 1);
+    if (DQ) {
+      sa[b2] = (float)g.sc.q[blk];
+      sb[b2] = g.sc.s2[blk >> 8];
+    } else {
+      sa[b2] = g.sc.absmax[blk];
+    }
+  }
+  const float mu = DQ ? g.sc.mu[0] : 0.0f;
+  // B entries of row j, ranks 16 ch + 8h .. +7 (ranks past r are zero)
+  uint32_t bw[NCH][4];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * ch + 8 * h + 2 * i;
+      uint32_t lo = 0, hi = 0;
+      if (t < g.r) lo = g.B[jc * g.r + t];
+      if (t + 1 < g.r) hi = g.B[jc * g.r + t + 1];
+      bw[ch][i] = lo | (hi << 16);
+    }
+  // 3. A^T to LDS: column c at c * PITCH, rank t at byte 2t
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    const int t = 16 * ch + (tid & 15), seg = tid >> 4;
+    const uint32_t v[8] = {av[ch][0].x, av[ch][0].y, av[ch][0].z, av[ch][0].w,
+                           av[ch][1].x, av[ch][1].y, av[ch][1].z, av[ch][1].w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *(uint16_t *)(s_at + (16 * seg + i) * PITCH + 2 * t) = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
   }
   __syncthreads();
-  const int jj = tid >> 3, cg = (tid & 7) * 8;
-  const int64_t j = j0 + jj, c = c0 + cg;
-  if (j >= d || c >= k) return;
-  const float mu = sc.dq ? sc.mu[0] : 0.0f;
-  const int64_t e0 = j * k + c;
-  const uint32_t cw = *(const uint32_t *)(codes + (e0 >> 1));
-  const float ap = ql::block_scale(sc, e0 >> 6, mu);
-  float ba[8];
+
+  // 4. per pair of 32-column blocks: D[c][j] on MFMA, the merged outputs into
+  //    the wave's staging rows (16-byte chunks XOR-swizzled by row), then
+  //    read back as whole rows and stored 16 bytes per lane (a wave store =
+  //    8 rows x 128 bytes). LDS accesses of a wave execute in order, so the
+  //    staging needs no barrier.
+  unsigned char *stg = s_stg + wave * (32 * 128);
+  const int64_t jw = (int64_t)blockIdx.y * 128 + 32 * wave;  // first row of the wave
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ba[i] = 0.0f;
-  for (int t = 0; t < r; ++t) {
-    const float bv = Bs[jj][t];
+  for (int pb = 0; pb < MNB / 2; ++pb) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ba[i] = fmaf(bv, As[t][cg + i], ba[i]);
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = 2 * pb + bb;
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        // A operand: A^T[c = 32 b + l32][ranks 16 ch + 8h ..]; B operand: B[j][same ranks]
+        const uint4 aop = *(const uint4 *)(s_at + (32 * b + l32) * PITCH + 32 * ch + 16 * h);
+        const uint4 bop = make_uint4(bw[ch][0], bw[ch][1], bw[ch][2], bw[ch][3]);
+        acc = ql::mfma32(aop, bop, acc);
+      }
+      // lane (row l32, h) holds D[8 gq + 4h + e][l32], columns 32 b + 8 gq + 4h + e
+      const float ap = DQ ? sa[pb] * sb[pb] + mu : sa[pb];
+      const uint32_t cwords[4] = {cw[b].x, cw[b].y, cw[b].z, cw[b].w};
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        // code bytes 4 gq + 2h, +1: columns 8 gq + 4h .. +3 (even element high nibble)
+        const uint32_t c16 = (cwords[gq] >> (16 * h)) & 0xFFFFu;
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int sh = 8 * (e >> 1) + ((e & 1) ? 0 : 4);
+          const float wq = ql::bf16_to_f(ql::f_to_bf16(s_lv[(c16 >> sh) & 15u] * ap));
+          o[e] = wq + g.s * acc[4 * gq + e];
+        }
+        const int chunk = (4 * bb + gq) ^ (l32 & 7);
+        *(uint2 *)(stg + l32 * 128 + 16 * chunk + 8 * h) =
+            make_uint2(ql::pack_bf16x2(o[0], o[1]), ql::pack_bf16x2(o[2], o[3]));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 8 * i + (lane >> 3), c = lane & 7;
+      const uint4 v = *(const uint4 *)(stg + rr * 128 + 16 * (c ^ (rr & 7)));
+      const int64_t row = jw + rr, col = c0 + 64 * pb + 8 * c;
+      if (row < g.d && col < g.k) *(uint4 *)(g.Wm + row * g.k + col) = v;
+    }
   }
-  float o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int sh = 8 * (i >> 1) + ((i & 1) ? 0 : 4);
-    const float wq = ql::bf16_to_f(ql::f_to_bf16(lv[(cw >> sh) & 15u] * ap));
-    o[i] = wq + s * ba[i];
-  }
-  uint4 out;
-  out.x = ql::pack_bf16x2(o[0], o[1]);
-  out.y = ql::pack_bf16x2(o[2], o[3]);
-  out.z = ql::pack_bf16x2(o[4], o[5]);
-  out.w = ql::pack_bf16x2(o[6], o[7]);
-  *(uint4 *)(Wm + e0) = out;
 }
 
 }  // namespace
@@ -71,9 +171,29 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint8_t *__restrict__ 
 qlora_status launch_merge(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, int64_t k,
                           const uint16_t *A, const uint16_t *B, int r, float s, uint16_t *Wm,
                           hipStream_t st) {
-  dim3 grid((unsigned)ql_cdiv(k, MC), (unsigned)ql_cdiv(d, MR));
+  const int nch = (r + 15) / 16;
+  if (nch < 1 || 16 * nch > MAXRP) return QLORA_ERR_UNSUPPORTED;
+  const int64_t gx = ql_cdiv(k, MC), gy = ql_cdiv(d, 128);
+  if (gy > 65535 || gx > 0x7fffffff) return QLORA_ERR_UNSUPPORTED;
+  MergeArgs g{codes, sc, d, k, A, B, r, 16 * nch, s, Wm};
+  dim3 grid((unsigned)gx, (unsigned)gy);
   QlProf prof(QLORA_K_MERGE, st);
-  merge_kernel<<<grid, 256, 0, st>>>(codes, sc, d, k, A, B, r, s, Wm);
+#define QL_MERGE(NCHV)                                                 \
+  if (sc.dq)                                                           \
+    merge_kernel<true, NCHV><<<grid, MT, 0, st>>>(g);                  \
+  else                                                                 \
+    merge_kernel<false, NCHV><<<grid, MT, 0, st>>>(g);
+  switch (nch) {
+    case 1: QL_MERGE(1) break;
+    case 2: QL_MERGE(2) break;
+    case 3: QL_MERGE(3) break;
+    case 4: QL_MERGE(4) break;
+    case 5: QL_MERGE(5) break;
+    case 6: QL_MERGE(6) break;
+    case 7: QL_MERGE(7) break;
+    default: QL_MERGE(8) break;
+  }
+#undef QL_MERGE
   QL_LAUNCH_CHECK();
   return QLORA_OK;
 }

@@ -153,7 +153,9 @@ def test_config3_gemv(ops, d, k, M):
 # ---- merge -------------------------------------------------------------------
 @pytest.mark.parametrize("d,k,r,alpha,dq", [(4096, 4096, 16, 32.0, True),
                                             (256, 256, 8, 16.0, False),
-                                            (200, 320, 3, 6.0, True)])
+                                            (200, 320, 3, 6.0, True),
+                                            (40, 704, 40, 16.0, True),   # 3 rank chunks, ragged tiles
+                                            (8, 64, 128, 64.0, False)])  # r = 128, one block
 def test_merge(ops, d, k, r, alpha, dq):
     inp = synth.linear_inputs(d, k, 1, r, idx=3, with_dy=False)
     w = ops.quantize(to_dev(inp["W0"]), double_quant=dq)
