@@ -212,8 +212,72 @@ def _rotated(fn, n_sets, iters):
     return s.elapsed_time(e) / iters
 
 
+def _graphed(fn, n_sets, iters):
+    """Average milliseconds per call of fn(i) when the n_sets calls are
+    captured once in a HIP graph and replayed (launch overhead of the Python
+    binding excluded); None if the capture fails."""
+    import torch
+    try:
+        for i in range(n_sets):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(n_sets):
+                    fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        reps = max(1, iters // n_sets)
+        g.replay()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / (reps * n_sets)
+    except Exception as ex:  # noqa: BLE001 - report and fall back to eager timing
+        log(f"[bench] graph capture failed ({ex}); eager timing")
+        return None
+
+
+def _call_ms(fn, n_sets, iters):
+    ms = _graphed(fn, n_sets, iters)
+    return ms if ms is not None else _rotated(fn, n_sets, iters)
+
+
+def _row(nbytes, call_ms, kernel_us):
+    """Row record: whole-call time (all kernels of the call, replayed from a
+    HIP graph, no per-kernel events) and the main kernel's event-bracketed
+    time, each as HBM GB/s."""
+    call_us = 1e3 * call_ms
+    out = {"call_us": round(call_us, 2), "kernel_us": round(kernel_us, 2),
+           "algorithmic_bytes": nbytes,
+           "GB_s_call": round(nbytes / (call_us * 1e-6) / 1e9, 1),
+           "GB_s_kernel": round(nbytes / (kernel_us * 1e-6) / 1e9, 1)}
+    out["frac_hbm_call"] = round(out["GB_s_call"] / PEAK_HBM_GBS, 4)
+    out["frac_hbm_kernel"] = round(out["GB_s_kernel"] / PEAK_HBM_GBS, 4)
+    return out
+
+
+def _kernel_us(ops, name, fn, n_sets, iters):
+    """Average event-bracketed duration of library kernel `name` over iters
+    calls of fn (a separate pass from the call timing)."""
+    ops.profile_begin(64 * iters, kernels=(name,))
+    _rotated(fn, n_sets, iters)
+    ops.profile_end()
+    c, t = ops.profile_query(name)
+    return 1e3 * t / c if c else float("nan")
+
+
 def measure_rows(ops, synth, torch, dev):
-    """Per-row measurements (quantise, dequantise, GEMV, merge, fwd, bwd)."""
+    """Per-row measurements (quantise, dequantise, GEMV, merge): call time of
+    back-to-back calls on inputs rotated through more than the last-level
+    cache, and the main kernel's event-bracketed time from a separate pass."""
     out = {}
     # quantise / dequantise: 12 distinct 4096x4096 weights (403 MB bf16)
     nset = 12
@@ -223,42 +287,30 @@ def measure_rows(ops, synth, torch, dev):
                       dtype=torch.uint8, device=dev)
     off = (-wsq.data_ptr()) % 256
     wsq = wsq[off:off + ops.workspace_bytes(ops.OP_QUANTIZE, D, K, 0, 0, True)]
-    ops.profile_begin(4096)
-    ms_q = _rotated(lambda i: ops.quantize(Ws[i], True, out=qs[i], ws=wsq), nset, 48)
-    ops.profile_end()
-    c, t = ops.profile_query("quantize")
     n = D * K
+    fq = lambda i: ops.quantize(Ws[i], True, out=qs[i], ws=wsq)
+    ms_q = _call_ms(fq, nset, 48)
     qbytes = 2 * n + ops.storage_bytes(D, K, True)
-    out["quantize"] = {"shape": [D, K], "double_quant": True, "ms_call": round(ms_q, 4),
-                       "kernel_us": round(1e3 * t / c, 2),
-                       "GB_s": round(qbytes / (t / c * 1e-3) / 1e9, 1),
-                       "algorithmic_bytes": qbytes}
-    out["quantize"]["frac_hbm"] = round(out["quantize"]["GB_s"] / PEAK_HBM_GBS, 4)
+    out["quantize"] = {"shape": [D, K], "double_quant": True,
+                       **_row(qbytes, ms_q, _kernel_us(ops, "quantize", fq, nset, 48)),
+                       "double_quant_kernel_us": round(_kernel_us(ops, "double_quant", fq, nset, 48), 2)}
     outs = [torch.empty(D, K, dtype=torch.bfloat16, device=dev) for _ in range(nset)]
-    ops.profile_begin(4096)
-    ms_d = _rotated(lambda i: ops.dequantize(qs[i], out=outs[i]), nset, 48)
-    ops.profile_end()
-    c, t = ops.profile_query("dequantize")
+    fd = lambda i: ops.dequantize(qs[i], out=outs[i])
+    ms_d = _call_ms(fd, nset, 48)
     dbytes = ops.storage_bytes(D, K, True) + 2 * n
-    out["dequantize"] = {"shape": [D, K], "kernel_us": round(1e3 * t / c, 2),
-                         "GB_s": round(dbytes / (t / c * 1e-3) / 1e9, 1),
-                         "algorithmic_bytes": dbytes}
-    out["dequantize"]["frac_hbm"] = round(out["dequantize"]["GB_s"] / PEAK_HBM_GBS, 4)
+    out["dequantize"] = {"shape": [D, K], **_row(dbytes, ms_d, _kernel_us(ops, "dequantize", fd, nset, 48))}
     # merge (r = 16)
     Ad = synth.normal_bf16_device((R, K), 0.01, 31, device=dev)
     Bd = synth.normal_bf16_device((D, R), 0.01, 32, device=dev)
-    ops.profile_begin(4096)
-    _rotated(lambda i: ops.merge(qs[i], Ad, Bd, ALPHA, out=outs[i]), nset, 48)
-    ops.profile_end()
-    c, t = ops.profile_query("merge")
+    fm = lambda i: ops.merge(qs[i], Ad, Bd, ALPHA, out=outs[i])
+    ms_m = _call_ms(fm, nset, 48)
     mbytes = ops.storage_bytes(D, K, True) + 2 * n + 2 * R * (D + K)
-    out["merge"] = {"shape": [D, K], "r": R, "kernel_us": round(1e3 * t / c, 2),
-                    "GB_s": round(mbytes / (t / c * 1e-3) / 1e9, 1), "algorithmic_bytes": mbytes}
-    out["merge"]["frac_hbm"] = round(out["merge"]["GB_s"] / PEAK_HBM_GBS, 4)
+    out["merge"] = {"shape": [D, K], "r": R, **_row(mbytes, ms_m, _kernel_us(ops, "merge", fm, nset, 48))}
     del Ws, outs, qs
     torch.cuda.empty_cache()
     # decode-shaped GEMV: gate/up 4096 -> 11008 and down 11008 -> 4096, 16
-    # distinct weights each (372 MB of NF4 per shape)
+    # distinct weights each (372 MB of NF4 per shape); the call also runs the
+    # LoRA down projection and the split/LoRA epilogue
     out["gemv"] = {}
     for (d, k) in ((11008, 4096), (4096, 11008)):
         nset = 16
@@ -276,19 +328,10 @@ def measure_rows(ops, synth, torch, dev):
             wst = torch.empty(wsn + 256, dtype=torch.uint8, device=dev)
             o2 = (-wst.data_ptr()) % 256
             wst = wst[o2:o2 + wsn]
-            ops.profile_begin(8192)
-            ms_call = _rotated(lambda i: ops.linear_fwd(gq[i], Xg, Ag, Bg, ALPHA, save_h=False,
-                                                        Y=Yg, ws=wst), nset, 96)
-            ops.profile_end()
-            c, t = ops.profile_query("gemv")
+            fg = lambda i: ops.linear_fwd(gq[i], Xg, Ag, Bg, ALPHA, save_h=False, Y=Yg, ws=wst)
+            ms_call = _call_ms(fg, nset, 96)
             gbytes = (ops.storage_bytes(d, k, True) + 2 * R * (d + k) + 2 * Mt * k + 2 * Mt * d)
-            key = f"{d}x{k}_M{Mt}"
-            out["gemv"][key] = {"kernel_us": round(1e3 * t / c, 2), "call_us": round(1e3 * ms_call, 2),
-                                "GB_s_kernel": round(gbytes / (t / c * 1e-3) / 1e9, 1),
-                                "GB_s_call": round(gbytes / (ms_call * 1e-3) / 1e9, 1),
-                                "algorithmic_bytes": gbytes}
-            out["gemv"][key]["frac_hbm_kernel"] = round(out["gemv"][key]["GB_s_kernel"] / PEAK_HBM_GBS, 4)
-            out["gemv"][key]["frac_hbm_call"] = round(out["gemv"][key]["GB_s_call"] / PEAK_HBM_GBS, 4)
+            out["gemv"][f"{d}x{k}_M{Mt}"] = _row(gbytes, ms_call, _kernel_us(ops, "gemv", fg, nset, 96))
         del gq
         torch.cuda.empty_cache()
     log(f"[bench] rows: {json.dumps(out)}")

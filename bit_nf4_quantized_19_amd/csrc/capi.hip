@@ -73,15 +73,16 @@ FwdWs fwd_layout(char *base, int64_t d, int64_t k, int64_t M, int r) {
   FwdWs L{};
   L.Ap = (r % 16) ? c.take<uint16_t>((int64_t)rp * k * 2) : nullptr;
   L.Bp = (r % 16) ? c.take<uint16_t>(d * rp * 2) : nullptr;
-  L.Hpart = c.take<float>((int64_t)skinny_part_bytes(M, k, rp));
-  L.H = c.take<float>(M * rp * 4);
   if (M > 16) {
+    L.Hpart = c.take<float>((int64_t)skinny_part_bytes(M, k, rp));
+    L.H = c.take<float>(M * rp * 4);
     L.Hs_hi = c.take<uint16_t>(M * rp * 2);
     L.Hs_lo = c.take<uint16_t>(M * rp * 2);
     L.gpart = nullptr;
-  } else {
+  } else {  // the GEMV computes H itself
+    L.Hpart = L.H = nullptr;
     L.Hs_hi = L.Hs_lo = nullptr;
-    L.gpart = c.take<float>((int64_t)gemv_part_bytes(d, k, M));
+    L.gpart = c.take<float>((int64_t)gemv_part_bytes(d, k, M, rp));
   }
   L.bytes = c.off;
   return L;
@@ -207,12 +208,12 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int6
     Ap = L.Ap;
     Bp = L.Bp;
   }
+  if (M <= 16)  // H = X A^T inside the GEMV; H_save gets the M x r copy
+    return launch_gemv_fwd(w->codes, src, d, k, X, M, Ap, Bp, r, rp, sc, L.gpart, H_save, Y, st);
   // H = X A^T (float32, M x rp); H_save gets the M x r copy
   if ((s = launch_skinny(X, M, k, Ap, rp, L.Hpart, L.H, rp, H_save, r, sc, L.Hs_hi, L.Hs_lo,
                          st)) != QLORA_OK)
     return s;
-  if (M <= 16)
-    return launch_gemv_fwd(w->codes, src, d, k, X, M, Bp, L.H, rp, sc, L.gpart, Y, st);
   return launch_gemm_fwd(w->codes, src, d, k, X, M, Bp, L.Hs_hi, L.Hs_lo, rp, Y, st);
 }
 

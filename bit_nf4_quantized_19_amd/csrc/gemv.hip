@@ -64,6 +64,9 @@ struct GemvArgs {
   int G;           // workgroups per slice
   int rpw;         // row groups per workgroup, <= 2 GW (the last ones may be past the end)
   float *part;     // [S][M][d]
+  const uint16_t *Ap;  // LoRA A, rp x k (ranks past r are zero rows)
+  int rp;
+  float *hpart;    // [S * GW][M][rp]: H = X A^T partial sums per slice and wave
 };
 
 // LDS byte offset of X[token 4 tp + t][slice block 4c + g][8s .. 8s+7]: row
@@ -202,6 +205,39 @@ QL_DEV void unit_compute(const GemvArgs &g, const GUnit *const (&us)[NU],
   }
 }
 
+// LoRA down projection H = X A^T (QLoRA glossary, forward paragraph), partial
+// sums over the 128 columns of this slice that wave w covers, on 16x16x32
+// MFMA: A operand = X rows (tokens), B operand = A rows (ranks 16 cb ..
+// 16 cb + 15); D[4q + i][n] = partial H[token 4q + i][rank 16 cb + n].
+QL_DEV void lora_down_partial(const GemvArgs &g, int64_t slice, int nblk, int wave, int n,
+                              int q) {
+  const int64_t c0 = slice * (64 * GB) + 128 * wave;  // first column of the wave
+  const int ncol = 64 * nblk - 128 * wave;           // valid columns of the wave (may be <= 0)
+  uint4 xa[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool ok = 32 * i + 8 * q < ncol && n < g.M;
+    xa[i] = ok ? *(const uint4 *)(g.X + n * g.k + c0 + 32 * i + 8 * q) : ql::zero4();
+  }
+  for (int cb = 0; cb < g.rp / 16; ++cb) {
+    uint4 aa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = 32 * i + 8 * q < ncol;
+      aa[i] = ok ? *(const uint4 *)(g.Ap + (int64_t)(16 * cb + n) * g.k + c0 + 32 * i + 8 * q)
+                 : ql::zero4();
+    }
+    f32x4 hacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hacc = ql::mfma16(xa[i], aa[i], hacc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * q + i;
+      if (t < g.M) g.hpart[((slice * GW + wave) * g.M + t) * g.rp + 16 * cb + n] = hacc[i];
+    }
+  }
+}
+
 // Workgroup (x, slice) takes row groups x, x + G, x + 2G, ... (at most 2 GW
 // of them) of one slice; wave w takes the workgroup's row groups w and
 // w + GW, both loaded before the table is built, then computed together. The
@@ -280,35 +316,64 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
     const GUnit *const one[1] = {&ua};
     unit_compute<DQ, TP, 1>(g, one, smem, abase, lcopy, mu, n, q, slice);
   }
+  if (blockIdx.x == gridDim.x - 1) lora_down_partial(g, slice, nblk, wave, n, q);  // fewest units
 }
 
+// Y[m][j] = bf16(sum_s part[s][m][j] + s_l * sum_t H[m][t] B[j][t]) with
+// H[m][t] = sum_p hpart[p][m][t] (fixed orders); workgroup (x, m) builds
+// H[m] in LDS (256 / rp lane groups of rp lanes, rp <= 128), workgroups with
+// x == 0 also write H_save (M x r).
 __global__ __launch_bounds__(256) void gemv_epilogue_kernel(
     const float *__restrict__ part, int S, int64_t M, int64_t d,
-    const uint16_t *__restrict__ Bp, const float *__restrict__ H, int rp, float s,
-    uint16_t *__restrict__ Y) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= M * d) return;
-  const int64_t m = idx / d, j = idx % d;
+    const uint16_t *__restrict__ Bp, const float *__restrict__ hpart, int nhp, int rp, float s,
+    uint16_t *__restrict__ Y, float *__restrict__ hsave, int r) {
+  __shared__ float hp[16][128];  // per lane-group sums of the H partials
+  __shared__ float hs[128];
+  const int64_t m = blockIdx.y;
+  const int tid = threadIdx.x;
+  // H[m][t]: lane group grp adds partials p = grp, grp + ng, ... of rank t
+  // (ng = 256 / rp groups), then rank t adds the groups in order
+  {
+    const int ng = 256 / rp, t = tid % rp, grp = tid / rp;
+    if (grp < ng) {
+      float acc = 0.0f;
+#pragma unroll 4
+      for (int p = grp; p < nhp; p += ng) acc += hpart[((int64_t)p * M + m) * rp + t];
+      hp[grp][t] = acc;
+    }
+    __syncthreads();
+    if (tid < rp) {
+      float acc = 0.0f;
+      for (int gi = 0; gi < ng; ++gi) acc += hp[gi][tid];
+      hs[tid] = acc;
+      if (hsave && blockIdx.x == 0 && tid < r) hsave[m * r + tid] = acc;
+    }
+    __syncthreads();
+  }
+  const int64_t j = (int64_t)blockIdx.x * 256 + tid;
+  if (j >= d) return;
   float acc = 0.0f;
-  for (int sp = 0; sp < S; ++sp) acc += part[(sp * M + m) * d + j];
+#pragma unroll 4
+  for (int sp = 0; sp < S; ++sp) acc += part[((int64_t)sp * M + m) * d + j];
   float l = 0.0f;
-  for (int t = 0; t < rp; ++t) l = fmaf(H[m * rp + t], ql::bf16_to_f(Bp[j * rp + t]), l);
-  Y[idx] = ql::f_to_bf16(acc + s * l);
+#pragma unroll 8
+  for (int t = 0; t < rp; ++t) l = fmaf(hs[t], ql::bf16_to_f(Bp[j * rp + t]), l);
+  Y[m * d + j] = ql::f_to_bf16(acc + s * l);
 }
 
 }  // namespace
 
 static int64_t gemv_splits(int64_t k) { return ql_cdiv(k >> 6, GB); }
 
-size_t gemv_part_bytes(int64_t d, int64_t k, int64_t M) {
-  return (size_t)(gemv_splits(k) * M * d * 4);
+size_t gemv_part_bytes(int64_t d, int64_t k, int64_t M, int rp) {
+  return (size_t)(gemv_splits(k) * M * d * 4 + gemv_splits(k) * GW * M * rp * 4);
 }
 
 qlora_status launch_gemv_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, int64_t k,
-                             const uint16_t *X, int64_t M, const uint16_t *Bp,
-                             const float *H, int rp, float s, float *part, uint16_t *Y,
-                             hipStream_t st) {
-  if (M < 1 || M > 16) return QLORA_ERR_INVALID_ARG;
+                             const uint16_t *X, int64_t M, const uint16_t *Ap,
+                             const uint16_t *Bp, int r, int rp, float s, float *part,
+                             float *H_save, uint16_t *Y, hipStream_t st) {
+  if (M < 1 || M > 16 || rp < 16 || rp > 128 || rp % 16) return QLORA_ERR_INVALID_ARG;
   static int ncu = 0;
   if (ncu == 0) {
     int dev = 0;
@@ -325,7 +390,8 @@ qlora_status launch_gemv_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, i
       ngroups, std::max<int64_t>(std::max<int64_t>(1, ncu / S), ql_cdiv(ngroups, 2 * GW)));
   const int64_t rpw = ql_cdiv(ngroups, G);
   if (S > 65535 || G > (int64_t(1) << 30)) return QLORA_ERR_UNSUPPORTED;
-  GemvArgs g{codes, sc, d, k, X, M, d * (k >> 6), ngroups, (int)G, (int)rpw, part};
+  float *hpart = part + S * M * d;
+  GemvArgs g{codes, sc, d, k, X, M, d * (k >> 6), ngroups, (int)G, (int)rpw, part, Ap, rp, hpart};
   dim3 grid((unsigned)G, (unsigned)S);
   {
     QlProf prof(QLORA_K_GEMV, st);
@@ -349,8 +415,9 @@ qlora_status launch_gemv_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, i
   }
   {
     QlProf prof(QLORA_K_GEMV_EPILOGUE, st);
-    gemv_epilogue_kernel<<<(unsigned)ql_cdiv(M * d, 256), 256, 0, st>>>(
-        part, (int)S, M, d, Bp, H, rp, s, Y);
+    dim3 eg((unsigned)ql_cdiv(d, 256), (unsigned)M);
+    gemv_epilogue_kernel<<<eg, 256, 0, st>>>(part, (int)S, M, d, Bp, hpart, (int)(S * GW), rp, s,
+                                             Y, H_save, r);
   }
   QL_LAUNCH_CHECK();
   return QLORA_OK;

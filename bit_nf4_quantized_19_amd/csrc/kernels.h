@@ -60,12 +60,14 @@ qlora_status launch_gemm_dx(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
                             const uint16_t *Gs_lo, int rp, uint16_t *dX,
                             hipStream_t st);
 
-// gemv.hip : memory-bound forward for M <= 16
+// gemv.hip : memory-bound forward for M <= 16, including the LoRA down
+// projection (Ap, Bp zero-padded to rp ranks; H_save may be NULL)
 qlora_status launch_gemv_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
                              int64_t k, const uint16_t *X, int64_t M,
-                             const uint16_t *Bp, const float *H, int rp,
-                             float s, float *part, uint16_t *Y, hipStream_t st);
-size_t gemv_part_bytes(int64_t d, int64_t k, int64_t M);
+                             const uint16_t *Ap, const uint16_t *Bp, int r, int rp,
+                             float s, float *part, float *H_save, uint16_t *Y,
+                             hipStream_t st);
+size_t gemv_part_bytes(int64_t d, int64_t k, int64_t M, int rp);
 
 // merge.hip
 qlora_status launch_merge(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
