@@ -16,18 +16,23 @@
 // ~16 significant bits.
 //
 // Tiling: workgroup tile 128 (n) x 256 (m), K-step 64 = one NF4 block per W'
-// row (forward) or per 8-row column strip (dX); one workgroup of four waves
-// per CU, one wave per SIMD, every wave doing all of:
-//   * fetching its quarter of the step's In tile (256 rows x 128 bytes) by
+// row (forward) or per 8-row column strip (dX); one workgroup of eight waves
+// per CU, two waves per SIMD (so one wave's LDS waits are covered by the
+// other's matrix work), every wave doing all of:
+//   * fetching its eighth of the step's In tile (256 rows x 128 bytes) by
 //     LDS DMA (global_load_lds, 16 bytes per lane), three stages, two steps
 //     ahead. On this part LDS DMA moves about three times the bytes per clock
 //     that loads into registers do, and the In tile is the bulk of the bytes
 //     a CU reads;
-//   * fetching codes and block scales three steps ahead, also by LDS DMA;
-//   * decoding the next step's W' tile once per workgroup (32 weights per
-//     lane) into LDS, three stages;
-//   * 32 v_mfma_f32_32x32x16_bf16 per step on its 64 (n) x 128 (m) quarter
-//     of the tile (2 x 2 waves), operands read from LDS.
+//   * fetching codes (waves 0-3) or block-scale words (waves 4-7) three
+//     steps ahead, also by LDS DMA;
+//   * decoding its share of the next step's W' tile (16 weights per lane)
+//     into LDS, three stages;
+//   * 16 v_mfma_f32_32x32x16_bf16 per step on its 64 (n) x 64 (m) eighth of
+//     the tile (2 x 4 waves), operands read from LDS.
+// Timeline probes of the four-wave form (one wave per SIMD, 64 x 128 per
+// wave) showed each wave's step dominated by its own LDS waits; with two
+// waves per SIMD the operand reads grow by a third but the waits overlap.
 // K order inside a step: MFMA K-slice c, lane half h covers K = 16c + 8h ..
 // +7 for both operands. LDS rows of 128 bytes are stored with the 16-byte
 // chunks permuted by f(row) = (row ^ row>>2) & 7 (conflict-free operand reads,
@@ -36,7 +41,7 @@
 // stage at compile time. The DMAs are issued from inline asm: the main loop
 // has no vector-memory instruction the compiler knows of, so it inserts no
 // vmcnt waits of its own; one barrier per K-step, before which each wave
-// waits (vmcnt, in-order retirement) exactly for its own DMA of the next
+// waits (vmcnt, in-order retirement) exactly for its own DMAs of the next
 // step, orders everything.
 // Workgroups are mapped XCD-aware: the 32 column tiles of one token block
 // land on the same XCD, whose L2 then holds that In block.
@@ -45,7 +50,7 @@
 
 namespace {
 
-constexpr int BN = 128, BM = 256, BK = 64, NT = 256;
+constexpr int BN = 128, BM = 256, BK = 64, NT = 512;
 __constant__ uint32_t c_levels_g[16] = NF4_LEVEL_BITS;
 
 struct GemmArgs {
@@ -122,9 +127,9 @@ QL_DEV float scale_of(uint32_t qd, float s2, int64_t blk, float mu) {
   return prod + mu;
 }
 
-// DMAs each wave issues per step: 8 for its In rows, 1 for codes, 1 for the
-// scale words.
-constexpr int kLoadsPerStep = 10;
+// DMAs each wave issues per step: 4 for its eighth of the In tile and 1 for
+// codes (waves 0-3) or scale words (waves 4-7).
+constexpr int kLoadsPerStep = 5;
 
 template <int MODE, bool DQ>
 struct Tile {
@@ -132,15 +137,15 @@ struct Tile {
   int tid, lane, wave, r32, h, wn, wm;
   int64_t m0, n0, nk;
   float mu;
-  int64_t xoff[8];    // byte offsets of this lane's 8 DMA chunks (from In + kk)
-  // forward: the decoding lane's weight row (clamped) and code half, the row
-  // of this lane's scale DMA; dX: code row/column of this lane's DMA, scale
-  // entry row / block column
-  int64_t wrow, srow64;
-  int half;
-  int crow_off, ccol, srow, sblk;
+  int64_t xoff[4];    // byte offsets of this lane's 4 In DMA chunks (from In + kk)
+  // code DMA (waves 0-3): forward weight row (clamped) and half block; dX code
+  // row inside the step and first column. Scale DMA (waves 4-7): forward
+  // weight row; dX entry row and block column. Decode: forward weight row;
+  // dX block column.
+  int64_t crow64, srow64, drow64;
+  int chalf, crow_off, ccol, srow, sblk, dcol;
 
-  f32x16 acc[2][4];
+  f32x16 acc[2][2];
 
   QL_DEV void init(const GemmArgs &ga) {
     g = ga;
@@ -160,121 +165,134 @@ struct Tile {
     n0 = tn * BN;
     nk = ql_cdiv(g.Ktot, BK);
     mu = DQ ? g.sc.mu[0] : 0.0f;
-    // In DMA: wave w fetches rows 64w .. 64w+63 in 8 groups of 8 rows; lane l
+    // In DMA: wave w fetches rows 32w .. 32w+31 in 4 groups of 8 rows; lane l
     // of a group fetches the chunk that the LDS permutation puts at slot l%8
     // of row l/8 (the DMA writes lane l's 16 bytes at group base + 16 l).
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 64 * wave + 8 * i + (lane >> 3);
+    for (int i = 0; i < 4; ++i) {
+      const int row = 32 * wave + 8 * i + (lane >> 3);
       const int chunk = (lane & 7) ^ ((row ^ (row >> 2)) & 7);
       int64_t m = m0 + row;
       m = m < g.M ? m : g.M - 1;  // rows past M: duplicate data, outputs discarded
       xoff[i] = (m * g.Ktot + 8 * chunk) * 2;
     }
+    const int p = 64 * (wave & 3) + lane;   // code DMA lane (waves 0-3)
+    const int e = 64 * (wave & 1) + lane;   // scale DMA entry (waves 4-7)
     if (MODE == 0) {
-      const int64_t row = n0 + (tid >> 1);
-      wrow = row < g.d ? row : g.d - 1;   // rows past d feed only discarded outputs
-      half = tid & 1;
-      const int64_t srw = n0 + 64 * (wave & 1) + lane;   // scale entry = tile row
-      srow64 = srw < g.d ? srw : g.d - 1;
+      const int64_t cr = n0 + (p >> 1);
+      crow64 = cr < g.d ? cr : g.d - 1;   // rows past d feed only discarded outputs
+      chalf = p & 1;
+      const int64_t sr = n0 + e;          // scale entry = tile row
+      srow64 = sr < g.d ? sr : g.d - 1;
+      const int64_t dr = n0 + (tid >> 2);
+      drow64 = dr < g.d ? dr : g.d - 1;
     } else {
-      crow_off = tid >> 2;                 // code row inside the step
-      const int64_t col = n0 + 32 * (tid & 3);
+      crow_off = p >> 2;                  // code row inside the step
+      const int64_t col = n0 + 32 * (p & 3);
       ccol = (int)(col < g.k ? col : g.k - 32);  // columns past k: discarded outputs
-      const int e = 64 * (wave & 1) + lane;       // scale entry 2r + b
-      srow = e >> 1;
+      srow = e >> 1;                      // scale entry 2r + b
       const int64_t c0 = n0 + 64 * (e & 1);
       sblk = (int)(c0 < g.k ? c0 : g.k - 64);
+      const int64_t dc = n0 + 64 * ((tid & 31) >> 4);
+      dcol = (int)(dc < g.k ? dc : g.k - 64);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
   }
 
-  // Row group i (8 rows, 1 KB) of this wave's quarter of the In tile of step
+  // Row group i (8 rows, 1 KB) of this wave's eighth of the In tile of step
   // kk into stage ST by LDS DMA (chunks past Ktot fetch the last valid chunk:
   // finite data times a zero W').
   template <int ST, bool FULL>
   QL_DEV void issue_x(int64_t kk, int i) {
     int64_t off = xoff[i];   // signed: the clamp below may step back past In + kk
     if (!FULL) {
-      const int row = 64 * wave + 8 * i + (lane >> 3);
+      const int row = 32 * wave + 8 * i + (lane >> 3);
       const int chunk = (lane & 7) ^ ((row ^ (row >> 2)) & 7);
       if (kk + 8 * chunk >= g.Ktot) off -= (kk + 8 * chunk - (g.Ktot - 8)) * 2;
     }
-    dma16((const char *)(g.In + kk) + off, lds_addr(&sX<ST>()[(64 * wave + 8 * i) * 8]));
+    dma16((const char *)(g.In + kk) + off, lds_addr(&sX<ST>()[(32 * wave + 8 * i) * 8]));
   }
   template <int ST, bool FULL>
   QL_DEV void issue_x_all(int64_t kk) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) issue_x<ST, FULL>(kk, i);
+    for (int i = 0; i < 4; ++i) issue_x<ST, FULL>(kk, i);
   }
 
-  // Codes and scale words of step kk into code stage ST (LDS DMA).
-  // Forward: lane p fetches 32 codes of tile row p/2; scale entry e (waves
-  // 0-1: int8-code dword or absmax, waves 2-3: s2 or absmax again) is tile
-  // row e. dX: lane p fetches columns 32(p%4).. of code row p/4; entry
-  // e = 2r + b is row r, block column b.
+  // Codes (waves 0-3) or scale words (waves 4-7) of step kk into code stage
+  // ST (LDS DMA). Forward: lane p fetches 32 codes of tile row p/2; scale
+  // entry e (waves 4-5: int8-code dword or absmax, waves 6-7: s2 or absmax
+  // again) is tile row e. dX: lane p fetches columns 32(p%4).. of code row
+  // p/4; entry e = 2r + b is row r, block column b.
   template <int ST>
   QL_DEV void issue_c(int64_t kk) {
     if (kk >= g.Ktot) kk = (nk - 1) * BK;   // prologue past the end: any valid step
-    int64_t blk;
-    if (MODE == 0) {
-      const int64_t e0 = wrow * g.k + kk + 32 * half;
-      dma16(g.codes + (e0 >> 1), lds_addr(&sC<ST>()[64 * wave]));
-      blk = (srow64 * g.k + kk) >> 6;
+    if (wave < 4) {
+      const void *src;
+      if (MODE == 0) {
+        src = g.codes + ((crow64 * g.k + kk + 32 * chalf) >> 1);
+      } else {
+        int64_t j = kk + crow_off;
+        j = j < g.d ? j : g.d - 1;
+        src = g.codes + ((j * g.k + ccol) >> 1);
+      }
+      dma16(src, lds_addr(&sC<ST>()[64 * wave]));
     } else {
-      int64_t j = kk + crow_off;
-      j = j < g.d ? j : g.d - 1;
-      dma16(g.codes + ((j * g.k + ccol) >> 1), lds_addr(&sC<ST>()[64 * wave]));
-      int64_t js = kk + srow;
-      js = js < g.d ? js : g.d - 1;
-      blk = (js * g.k + sblk) >> 6;
+      int64_t blk;
+      if (MODE == 0) {
+        blk = (srow64 * g.k + kk) >> 6;
+      } else {
+        int64_t js = kk + srow;
+        js = js < g.d ? js : g.d - 1;
+        blk = (js * g.k + sblk) >> 6;
+      }
+      // int8 codes: the aligned dword (nb is a multiple of 8, so in bounds)
+      const bool qw = wave < 6;
+      const void *src;
+      if (DQ)
+        src = qw ? (const void *)(g.sc.q + (blk & ~(int64_t)3))
+                 : (const void *)(g.sc.s2 + (blk >> 8));
+      else
+        src = (const void *)(g.sc.absmax + blk);
+      dma4(src, qw ? lds_addr(&sQ<ST>()[64 * (wave - 4)]) : lds_addr(&sS<ST>()[64 * (wave - 6)]));
     }
-    // int8 codes: the aligned dword (nb is a multiple of 8, so in bounds)
-    const void *src;
-    if (DQ)
-      src = wave < 2 ? (const void *)(g.sc.q + (blk & ~(int64_t)3))
-                     : (const void *)(g.sc.s2 + (blk >> 8));
-    else
-      src = (const void *)(g.sc.absmax + blk);
-    dma4(src, wave < 2 ? lds_addr(&sQ<ST>()[64 * wave]) : lds_addr(&sS<ST>()[64 * (wave - 2)]));
   }
 
-  // ---- decode: the codes of one step into a W' tile, in four parts --------
-  // Forward: lane owns 32 codes of one row (half of its block); part i turns
-  // code word i (8 weights) into one 16-byte fragment. dX: lane (jg = tid/32,
-  // kg = tid%32) owns rows 8jg..8jg+7, columns 4kg..4kg+3 of the stage's
-  // codes (row r at bytes 64r..64r+63); part i writes column 4kg+i, 8 rows.
+  // ---- decode: the codes of one step into a W' tile ----------------------
+  // Forward (two parts): thread t owns code words 2(t%2), +1 of code entry
+  // t/2, i.e. 16 weights of tile row t/4; part i turns one word (8 weights)
+  // into one 16-byte fragment. dX (four parts): thread (jg = t/32,
+  // kg = t%32) owns rows 4jg..4jg+3, columns 4kg..4kg+3 of the stage's codes
+  // (row r at bytes 64r..64r+63); part i writes column 4kg+i, 4 rows (8 bytes).
+  static constexpr int kParts = MODE == 0 ? 2 : 4;
   struct DecIn {
-    uint32_t c[8];   // forward: the 4 code words; dX: 8 rows' 2-byte code pairs
-    float a[8];      // forward: a[0] = the row's a'; dX: a' of each row
+    uint32_t c[4];   // forward: 2 code words; dX: 4 rows' 2-byte code pairs
+    float a[4];      // forward: a[0] = the row's a'; dX: a' of each row
   };
 
   template <int CS>
   QL_DEV DecIn dec_load(int64_t kk) {
     DecIn di;
     if (MODE == 0) {
-      const uint4 c = sC<CS>()[tid];
-      di.c[0] = c.x; di.c[1] = c.y; di.c[2] = c.z; di.c[3] = c.w;
-      const int64_t blk = (wrow * g.k + kk) >> 6;
-      di.a[0] = scale_of<DQ>(sQ<CS>()[tid >> 1], sS<CS>()[tid >> 1], blk, mu);
+      const uint2 c = ((const uint2 *)sC<CS>())[tid];
+      di.c[0] = c.x; di.c[1] = c.y;
+      const int64_t blk = (drow64 * g.k + kk) >> 6;
+      di.a[0] = scale_of<DQ>(sQ<CS>()[tid >> 2], sS<CS>()[tid >> 2], blk, mu);
     } else {
       const int jg = tid >> 5, kg = tid & 31, bsel = kg >> 4;
       const uint16_t *raw = (const uint16_t *)sC<CS>();
-      int64_t col = n0 + 64 * bsel;
-      col = col < g.k ? col : g.k - 64;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        di.c[i] = raw[(8 * jg + i) * 32 + kg];
-        const int64_t j = kk + 8 * jg + i;
+      for (int i = 0; i < 4; ++i) {
+        di.c[i] = raw[(4 * jg + i) * 32 + kg];
+        const int64_t j = kk + 4 * jg + i;
         const int64_t jc = j < g.d ? j : g.d - 1;
-        const int64_t blk = (jc * g.k + col) >> 6;
-        const float v = scale_of<DQ>(sQ<CS>()[16 * jg + bsel + 2 * i],
-                                     sS<CS>()[16 * jg + bsel + 2 * i], blk, mu);
+        const int64_t blk = (jc * g.k + dcol) >> 6;
+        const float v = scale_of<DQ>(sQ<CS>()[8 * jg + 2 * i + bsel],
+                                     sS<CS>()[8 * jg + 2 * i + bsel], blk, mu);
         di.a[i] = j < g.d ? v : 0.0f;  // rows past d: zero
       }
     }
@@ -283,7 +301,6 @@ struct Tile {
 
   template <int WS>
   QL_DEV void dec_part(const DecIn &di, int i) {
-    uint4 o;
     if (MODE == 0) {
       // byte b of a code word holds elements 2b (high nibble) and 2b+1 (low
       // nibble); spread them into byte lanes pre-multiplied by 4 (LDS address)
@@ -297,21 +314,21 @@ struct Tile {
         f[2 * b + 1] = *(const float *)(lvb + __builtin_amdgcn_ubfe(od4, 8 * b, 8));
       }
       const float a = di.a[0];
+      uint4 o;
       o.x = ql::pack_bf16x2(f[0] * a, f[1] * a);
       o.y = ql::pack_bf16x2(f[2] * a, f[3] * a);
       o.z = ql::pack_bf16x2(f[4] * a, f[5] * a);
       o.w = ql::pack_bf16x2(f[6] * a, f[7] * a);
-      sW<WS>()[swz(tid >> 1, 4 * half + i)] = o;
+      sW<WS>()[swz(tid >> 2, 4 * ((tid >> 1) & 1) + 2 * (tid & 1) + i)] = o;
     } else {
       // column 4kg+i: nibble at bit 4, 0, 12, 8 of the 2-byte pair
       const int sh = i == 0 ? 4 : i == 1 ? 0 : i == 2 ? 12 : 8;
       const float *lv = s_lv;
-      uint32_t w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        w[q] = ql::pack_bf16x2(lv[(di.c[2 * q] >> sh) & 15] * di.a[2 * q],
-                               lv[(di.c[2 * q + 1] >> sh) & 15] * di.a[2 * q + 1]);
-      sW<WS>()[swz(4 * (tid & 31) + i, tid >> 5)] = make_uint4(w[0], w[1], w[2], w[3]);
+      const int jg = tid >> 5;
+      uint2 o;
+      o.x = ql::pack_bf16x2(lv[(di.c[0] >> sh) & 15] * di.a[0], lv[(di.c[1] >> sh) & 15] * di.a[1]);
+      o.y = ql::pack_bf16x2(lv[(di.c[2] >> sh) & 15] * di.a[2], lv[(di.c[3] >> sh) & 15] * di.a[3]);
+      ((uint2 *)sW<WS>())[2 * swz(4 * (tid & 31) + i, jg >> 1) + (jg & 1)] = o;
     }
   }
 
@@ -319,24 +336,25 @@ struct Tile {
   QL_DEV void decode(int64_t t) {
     const DecIn di = dec_load<CS>(t * BK);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dec_part<WS>(di, i);
+    for (int i = 0; i < kParts; ++i) dec_part<WS>(di, i);
   }
 
-  // MFMA operands of K-slice c of stage ST: W' rows wn*64.., In rows wm*128..
+  // MFMA operands of K-slice c of stage ST: W' rows wn*64.., In rows wm*64..
   template <int ST>
-  QL_DEV void load_slice(int c, uint4 (&a)[2], uint4 (&b)[4]) {
+  QL_DEV void load_slice(int c, uint4 (&a)[2], uint4 (&b)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) a[i] = sW<ST>()[swz(wn * 64 + 32 * i + r32, 2 * c + h)];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = sX<ST>()[swz(wm * 128 + 32 * j + r32, 2 * c + h)];
+    for (int j = 0; j < 2; ++j) b[j] = sX<ST>()[swz(wm * 64 + 32 * j + r32, 2 * c + h)];
   }
 
   // One K-step s (ST = s % 3). Main steps (TAIL = false) have s + 3 < nk.
   // Stages: In tile, W' tile and codes of step t live in stage t % 3. The
-  // step is cut into its four K-slices; each slice group issues the next
-  // slice's operand reads, two of the In DMAs of step s+2 (the last one also
-  // the code DMAs of step s+3), its 8 MFMAs and a quarter of the decode of
-  // step s+1, so the decode and the DMA issue overlap the matrix cores.
+  // step is cut into its four K-slices; each slice issues the next slice's
+  // operand reads, one of this wave's In DMAs of step s+2 (the last one also
+  // its code or scale DMA of step s+3), its 4 MFMAs and a share of the decode
+  // of step s+1 (forward: slices 1 and 3; dX: every slice), so the decode and
+  // the DMA issue overlap the matrix cores of both waves on the SIMD.
   template <int ST, bool TAIL>
   QL_DEV void step(int64_t s) {
     constexpr int S1 = (ST + 1) % 3, S2 = (ST + 2) % 3;
@@ -344,21 +362,24 @@ struct Tile {
     const bool do_d = !TAIL || s + 1 < nk;
     DecIn di;
     if (do_d) di = dec_load<S1>((s + 1) * BK);
-    uint4 a[2][2], b[2][4];
+    uint4 a[2][2], b[2][2];
     load_slice<ST>(0, a[0], b[0]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       if (c < 3) load_slice<ST>(c + 1, a[(c + 1) & 1], b[(c + 1) & 1]);
-      if (do_x) {
-        issue_x<S2, !TAIL>((s + 2) * BK, 2 * c);
-        issue_x<S2, !TAIL>((s + 2) * BK, 2 * c + 1);
-      }
+      if (do_x) issue_x<S2, !TAIL>((s + 2) * BK, c);
       if (c == 3 && do_c) issue_c<ST>((s + 3) * BK);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = ql::mfma32(a[c & 1][i], b[c & 1][j], acc[i][j]);
-      if (do_d) dec_part<S1>(di, c);
+        for (int j = 0; j < 2; ++j) acc[i][j] = ql::mfma32(a[c & 1][i], b[c & 1][j], acc[i][j]);
+      if (do_d) {
+        if (MODE == 0) {
+          if (c & 1) dec_part<S1>(di, c >> 1);
+        } else {
+          dec_part<S1>(di, c);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // the In tile of step s+1 and the codes of step s+2 (issued last step)
@@ -406,28 +427,28 @@ struct Tile {
 #pragma unroll
       for (int part = 0; part < 2; ++part) {
         const uint16_t *S = part ? g.Slo : g.Shi;
-        uint4 a[2], b[4];
+        uint4 a[2], b[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int64_t n = n0 + wn * 64 + 32 * i + r32;
           a[i] = (n < g.Ntot) ? *(const uint4 *)(g.L + n * g.rp + t0 + 8 * h) : ql::zero4();
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t m = m0 + wm * 128 + 32 * j + r32;
+        for (int j = 0; j < 2; ++j) {
+          const int64_t m = m0 + wm * 64 + 32 * j + r32;
           b[j] = (m < g.M) ? *(const uint4 *)(S + m * g.rp + t0 + 8 * h) : ql::zero4();
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = ql::mfma32(a[i], b[j], acc[i][j]);
+          for (int j = 0; j < 2; ++j) acc[i][j] = ql::mfma32(a[i], b[j], acc[i][j]);
       }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t m = m0 + wm * 128 + 32 * j + r32;
+      for (int j = 0; j < 2; ++j) {
+        const int64_t m = m0 + wm * 64 + 32 * j + r32;
         if (m >= g.M) continue;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {

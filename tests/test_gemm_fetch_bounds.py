@@ -2,8 +2,9 @@
 
 The fused dequant-GEMM fetches its In tiles, packed codes and scale words by
 LDS DMA from addresses it computes per lane; a fetch past a buffer end is a
-GPU memory fault, not a wrong number. This model restates, for every lane,
-tile and step the kernel issues (the prologue fetches steps 0-1 of In and
+GPU memory fault, not a wrong number. This model restates, for every lane of
+the eight waves (each fetches an eighth of the In tile; waves 0-3 fetch the
+codes, waves 4-7 the scale words), tile and step the kernel issues (the prologue fetches steps 0-1 of In and
 0-2 of codes unconditionally, clamping addresses), the address arithmetic of
 csrc/gemm.hip and checks that each fetch lies inside its buffer, for the
 workload shapes, the ragged test shapes and one-step contractions (the case
@@ -24,8 +25,11 @@ def _cdiv(a, b):
 def _fetches_in_bounds(d, k, M, mode, dq):
     Ntot, Ktot = (d, k) if mode == 0 else (k, d)
     nk = _cdiv(Ktot, BK)
-    tid = np.arange(256)
+    tid = np.arange(512)
     lane, wave = tid & 63, tid >> 6
+    cw, sw = wave < 4, wave >= 4            # code and scale fetching waves
+    p = 64 * (wave & 3) + lane              # code DMA lane
+    e = 64 * (wave & 1) + lane              # scale DMA entry
     nb, ng = d * k // 64, _cdiv(d * k // 64, 256)
     x_steps = sorted({0, 1} | {s + 2 for s in range(nk) if s + 2 < nk})
     c_steps = sorted({0, 1, 2} | {s + 3 for s in range(nk) if s + 3 < nk})
@@ -35,8 +39,8 @@ def _fetches_in_bounds(d, k, M, mode, dq):
             for t in x_steps:
                 kk = t * BK
                 full = t >= 2 and kk + BK <= Ktot
-                for i in range(8):
-                    row = 64 * wave + 8 * i + (lane >> 3)
+                for i in range(4):
+                    row = 32 * wave + 8 * i + (lane >> 3)
                     chunk = (lane & 7) ^ ((row ^ (row >> 2)) & 7)
                     m = np.minimum(m0 + row, M - 1)
                     off = (m * Ktot + 8 * chunk) * 2
@@ -49,24 +53,24 @@ def _fetches_in_bounds(d, k, M, mode, dq):
             for t in c_steps:
                 kk = min(t * BK, (nk - 1) * BK)
                 if mode == 0:
-                    wrow = np.minimum(n0 + (tid >> 1), d - 1)
-                    ca = (wrow * k + kk + 32 * (tid & 1)) >> 1
-                    srow = np.minimum(n0 + 64 * (wave & 1) + lane, d - 1)
+                    wrow = np.minimum(n0 + (p >> 1), d - 1)
+                    ca = (wrow * k + kk + 32 * (p & 1)) >> 1
+                    srow = np.minimum(n0 + e, d - 1)
                     blk = (srow * k + kk) >> 6
                 else:
-                    j = np.minimum(kk + (tid >> 2), d - 1)
-                    col = n0 + 32 * (tid & 3)
+                    j = np.minimum(kk + (p >> 2), d - 1)
+                    col = n0 + 32 * (p & 3)
                     ca = (j * k + np.where(col < k, col, k - 32)) >> 1
-                    e = 64 * (wave & 1) + lane
                     c0 = n0 + 64 * (e & 1)
                     blk = (np.minimum(kk + (e >> 1), d - 1) * k + np.where(c0 < k, c0, k - 64)) >> 6
+                ca, blk = ca[cw], blk[sw]
                 if (ca < 0).any() or (ca + 16 > d * k // 2).any():
                     return f"code fetch of step {t}"
                 if dq:
-                    q = (blk & ~3)[wave < 2]
+                    q = (blk & ~3)[wave[sw] < 6]
                     if (q < 0).any() or (q + 4 > nb).any():
                         return f"int8-code fetch of step {t}"
-                    if ((blk >> 8)[wave >= 2] >= ng).any():
+                    if ((blk >> 8)[wave[sw] >= 6] >= ng).any():
                         return f"s2 fetch of step {t}"
                 elif (blk < 0).any() or (blk >= nb).any():
                     return f"absmax fetch of step {t}"
