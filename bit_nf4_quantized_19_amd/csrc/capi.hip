@@ -63,7 +63,7 @@ struct Carve {
 
 struct FwdWs {
   uint16_t *Ap, *Bp, *Hs_hi, *Hs_lo;
-  float *Hpart, *H, *gpart;
+  float *H, *gpart;
   int64_t bytes;
 };
 
@@ -71,16 +71,16 @@ FwdWs fwd_layout(char *base, int64_t d, int64_t k, int64_t M, int r) {
   const int rp = (int)ql_rup(r, 16);
   Carve c{base};
   FwdWs L{};
-  L.Ap = (r % 16) ? c.take<uint16_t>((int64_t)rp * k * 2) : nullptr;
-  L.Bp = (r % 16) ? c.take<uint16_t>(d * rp * 2) : nullptr;
   if (M > 16) {
-    L.Hpart = c.take<float>((int64_t)skinny_part_bytes(M, k, rp));
+    L.Ap = L.Bp = nullptr;
     L.H = c.take<float>(M * rp * 4);
     L.Hs_hi = c.take<uint16_t>(M * rp * 2);
     L.Hs_lo = c.take<uint16_t>(M * rp * 2);
     L.gpart = nullptr;
-  } else {  // the GEMV computes H itself
-    L.Hpart = L.H = nullptr;
+  } else {  // the GEMV computes H itself from zero-padded A and B
+    L.Ap = (r % 16) ? c.take<uint16_t>((int64_t)rp * k * 2) : nullptr;
+    L.Bp = (r % 16) ? c.take<uint16_t>(d * rp * 2) : nullptr;
+    L.H = nullptr;
     L.Hs_hi = L.Hs_lo = nullptr;
     L.gpart = c.take<float>((int64_t)gemv_part_bytes(d, k, M, rp));
   }
@@ -89,8 +89,8 @@ FwdWs fwd_layout(char *base, int64_t d, int64_t k, int64_t M, int r) {
 }
 
 struct BwdWs {
-  uint16_t *Ap, *Bt, *At, *Gs_hi, *Gs_lo;
-  float *Hpart, *H, *Gpart, *G, *cpart;
+  uint16_t *Bt, *Gs_hi, *Gs_lo;
+  float *H, *G, *cpart;
   int64_t bytes;
 };
 
@@ -98,15 +98,12 @@ BwdWs bwd_layout(char *base, int64_t d, int64_t k, int64_t M, int r, bool need_h
   const int rp = (int)ql_rup(r, 16);
   Carve c{base};
   BwdWs L{};
-  L.Ap = (need_h && (r % 16)) ? c.take<uint16_t>((int64_t)rp * k * 2) : nullptr;
-  L.Hpart = need_h ? c.take<float>((int64_t)skinny_part_bytes(M, k, rp)) : nullptr;
   L.H = need_h ? c.take<float>(M * rp * 4) : nullptr;
-  L.Bt = c.take<uint16_t>((int64_t)rp * d * 2);
-  L.Gpart = c.take<float>((int64_t)skinny_part_bytes(M, d, rp));
+  // B is read in place for G when r % 16 == 0; otherwise a zero-padded B^T
+  L.Bt = (r % 16) ? c.take<uint16_t>((int64_t)rp * d * 2) : nullptr;
   L.G = c.take<float>(M * rp * 4);
   L.Gs_hi = need_dx ? c.take<uint16_t>(M * rp * 2) : nullptr;
   L.Gs_lo = need_dx ? c.take<uint16_t>(M * rp * 2) : nullptr;
-  L.At = need_dx ? c.take<uint16_t>(k * rp * 2) : nullptr;
   L.cpart = c.take<float>((int64_t)colacc_part_bytes(M, d, k, rp));
   L.bytes = c.off;
   return L;
@@ -201,20 +198,21 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int6
   const float sc = lora_alpha / (float)r;
   const ql::ScaleSrc src = scale_src(w);
 
-  const uint16_t *Ap = A, *Bp = B;
-  if (r % 16) {
-    const LayoutReq req[2] = {{A, r, k, L.Ap, rp, k, 0}, {B, d, r, L.Bp, d, rp, 0}};
-    if ((s = launch_layout(req, 2, st)) != QLORA_OK) return s;
-    Ap = L.Ap;
-    Bp = L.Bp;
-  }
-  if (M <= 16)  // H = X A^T inside the GEMV; H_save gets the M x r copy
+  if (M <= 16) {  // H = X A^T inside the GEMV; H_save gets the M x r copy
+    const uint16_t *Ap = A, *Bp = B;
+    if (r % 16) {
+      const LayoutReq req[2] = {{A, r, k, L.Ap, rp, k, 0}, {B, d, r, L.Bp, d, rp, 0}};
+      if ((s = launch_layout(req, 2, st)) != QLORA_OK) return s;
+      Ap = L.Ap;
+      Bp = L.Bp;
+    }
     return launch_gemv_fwd(w->codes, src, d, k, X, M, Ap, Bp, r, rp, sc, L.gpart, H_save, Y, st);
-  // H = X A^T (float32, M x rp); H_save gets the M x r copy
-  if ((s = launch_skinny(X, M, k, Ap, rp, L.Hpart, L.H, rp, H_save, r, sc, L.Hs_hi, L.Hs_lo,
-                         st)) != QLORA_OK)
+  }
+  // H = X A^T (float32, M x rp) and s*H as bf16 hi/lo; H_save gets the M x r copy
+  if ((s = launch_skinny(X, M, k, A, false, r, rp, L.H, H_save, r, sc, L.Hs_hi, L.Hs_lo, st)) !=
+      QLORA_OK)
     return s;
-  return launch_gemm_fwd(w->codes, src, d, k, X, M, Bp, L.Hs_hi, L.Hs_lo, rp, Y, st);
+  return launch_gemm_fwd(w->codes, src, d, k, X, M, B, r, L.Hs_hi, L.Hs_lo, rp, Y, st);
 }
 
 qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
@@ -239,31 +237,29 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, int6
   const int rp = (int)ql_rup(r, 16);
   const float sc = lora_alpha / (float)r;
 
-  // layouts: A padded (for H), B^T (for G), A^T (for the dX epilogue)
-  {
-    const LayoutReq req[3] = {{A, r, k, (need_h && (r % 16)) ? L.Ap : nullptr, rp, k, 0},
-                              {B, d, r, L.Bt, rp, d, 1},
-                              {A, r, k, need_dx ? L.At : nullptr, k, rp, 1}};
-    if ((s = launch_layout(req, 3, st)) != QLORA_OK) return s;
-  }
   const float *Hq = H;  // M x rp
   if (need_h) {
-    const uint16_t *Ap = (r % 16) ? L.Ap : A;
-    if ((s = launch_skinny(X, M, k, Ap, rp, L.Hpart, L.H, rp, nullptr, 0, sc, nullptr, nullptr,
+    if ((s = launch_skinny(X, M, k, A, false, r, rp, L.H, nullptr, 0, sc, nullptr, nullptr,
                            st)) != QLORA_OK)
       return s;
     Hq = L.H;
   }
-  // G = dY B (float32, M x rp) and s*G as bf16 hi/lo for the dX epilogue
-  if ((s = launch_skinny(dY, M, d, L.Bt, rp, L.Gpart, L.G, rp, nullptr, 0, sc, L.Gs_hi, L.Gs_lo,
-                         st)) != QLORA_OK)
-    return s;
+  // G = dY B (float32, M x rp) and s*G as bf16 hi/lo for the dX epilogue; B
+  // is read in place unless r % 16 != 0 (then from a zero-padded B^T)
+  if (r % 16) {
+    const LayoutReq req[1] = {{B, d, r, L.Bt, rp, d, 1}};
+    if ((s = launch_layout(req, 1, st)) != QLORA_OK) return s;
+    s = launch_skinny(dY, M, d, L.Bt, false, rp, rp, L.G, nullptr, 0, sc, L.Gs_hi, L.Gs_lo, st);
+  } else {
+    s = launch_skinny(dY, M, d, B, true, r, rp, L.G, nullptr, 0, sc, L.Gs_hi, L.Gs_lo, st);
+  }
+  if (s != QLORA_OK) return s;
   // dB = s dY^T H (d x r) and dA = s G^T X (r x k), one launch
   if ((s = launch_colacc2(ColaccReq{dY, d, Hq, dB, 0}, ColaccReq{X, k, L.G, dA, 1}, M, rp, r, sc,
                           L.cpart, st)) != QLORA_OK)
     return s;
   if (need_dx) {
-    if ((s = launch_gemm_dx(w->codes, scale_src(w), d, k, dY, M, L.At, L.Gs_hi, L.Gs_lo, rp, dX,
+    if ((s = launch_gemm_dx(w->codes, scale_src(w), d, k, dY, M, A, r, L.Gs_hi, L.Gs_lo, rp, dX,
                             st)) != QLORA_OK)
       return s;
   }

@@ -60,9 +60,9 @@ struct GemmArgs {
   const uint16_t *In;    // M x Ktot
   int64_t M;
   int64_t Ntot, Ktot;    // output columns, contraction length
-  const uint16_t *L;     // Ntot x rp
+  const uint16_t *L;     // L[n][t] = L[n * r + t] (forward: B) or L[t * Ntot + n] (dX: A)
   const uint16_t *Shi, *Slo;  // M x rp
-  int rp;
+  int r, rp;
   uint16_t *Out;         // M x Ntot
 };
 
@@ -424,15 +424,50 @@ struct Tile {
   // the bf16 stores. Lane holds D[8(e/4) + 4(l/32) + e%4][l%32] = Out[m][n].
   QL_DEV void epilogue() {
     for (int t0 = 0; t0 < g.rp; t0 += 16) {
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        const uint16_t *S = part ? g.Slo : g.Shi;
-        uint4 a[2], b[2];
+      // L[n][t0 + 8h .. +7] read in place (ranks past r and n past Ntot: 0);
+      // loads from clamped addresses, the zeroing applied afterwards
+      uint4 a[2];
+      if (MODE == 0 && g.r % 8 == 0) {
+        // forward, B rows of whole 16-byte pieces: one load per operand
+        const int tq = t0 + 8 * h;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int64_t n = n0 + wn * 64 + 32 * i + r32;
-          a[i] = (n < g.Ntot) ? *(const uint4 *)(g.L + n * g.rp + t0 + 8 * h) : ql::zero4();
+          const int64_t nc = n < g.Ntot ? n : g.Ntot - 1;
+          const uint4 v = *(const uint4 *)(g.L + nc * g.r + (tq < g.r ? tq : g.r - 8));
+          a[i] = (n < g.Ntot && tq < g.r) ? v : ql::zero4();
         }
+      } else {
+        // gather: all 16 loads issued before any use
+        uint32_t e[2][8];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int64_t n = n0 + wn * 64 + 32 * i + r32;
+          const int64_t nc = n < g.Ntot ? n : g.Ntot - 1;
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int t = t0 + 8 * h + x, tc = t < g.r ? t : g.r - 1;
+            e[i][x] = g.L[MODE == 0 ? nc * g.r + tc : (int64_t)tc * g.Ntot + nc];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const bool n_ok = n0 + wn * 64 + 32 * i + r32 < g.Ntot;
+          uint32_t w[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int t = t0 + 8 * h + 2 * q;
+            const uint32_t lo = (n_ok && t < g.r) ? e[i][2 * q] : 0u;
+            const uint32_t hi = (n_ok && t + 1 < g.r) ? e[i][2 * q + 1] : 0u;
+            w[q] = lo | (hi << 16);
+          }
+          a[i] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const uint16_t *S = part ? g.Slo : g.Shi;
+        uint4 b[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int64_t m = m0 + wm * 64 + 32 * j + r32;
@@ -495,17 +530,17 @@ static qlora_status launch_gemm(int mode, GemmArgs g, hipStream_t st) {
 }
 
 qlora_status launch_gemm_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, int64_t k,
-                             const uint16_t *X, int64_t M, const uint16_t *Bp,
+                             const uint16_t *X, int64_t M, const uint16_t *B, int r,
                              const uint16_t *Hs_hi, const uint16_t *Hs_lo, int rp,
                              uint16_t *Y, hipStream_t st) {
-  GemmArgs g{codes, sc, d, k, X, M, d, k, Bp, Hs_hi, Hs_lo, rp, Y};
+  GemmArgs g{codes, sc, d, k, X, M, d, k, B, Hs_hi, Hs_lo, r, rp, Y};
   return launch_gemm(0, g, st);
 }
 
 qlora_status launch_gemm_dx(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, int64_t k,
-                            const uint16_t *dY, int64_t M, const uint16_t *At,
+                            const uint16_t *dY, int64_t M, const uint16_t *A, int r,
                             const uint16_t *Gs_hi, const uint16_t *Gs_lo, int rp,
                             uint16_t *dX, hipStream_t st) {
-  GemmArgs g{codes, sc, d, k, dY, M, k, d, At, Gs_hi, Gs_lo, rp, dX};
+  GemmArgs g{codes, sc, d, k, dY, M, k, d, A, Gs_hi, Gs_lo, r, rp, dX};
   return launch_gemm(1, g, st);
 }

@@ -26,14 +26,14 @@ struct LayoutReq {
   int transpose;
 };
 qlora_status launch_layout(const LayoutReq *req, int nreq, hipStream_t st);
-// out[m][t] (fp32, M x rp) = sum_c In[m][c] * P[t][c]; In M x C, P rp x C.
-// out2 (optional) receives the first out2_ld columns with leading dim out2_ld.
-// Also writes s*out split into bf16 hi/lo (M x rp each) when hi != NULL.
-qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C,
-                           const uint16_t *P, int rp, float *part, float *out,
-                           int64_t out_ld, float *out2, int out2_ld, float s,
-                           uint16_t *hi, uint16_t *lo, hipStream_t st);
-size_t skinny_part_bytes(int64_t M, int64_t C, int rp);
+// out[m][t] (fp32, M x rp) = sum_c In[m][c] * P[t][c] for t < r (zero for
+// r <= t < rp), one launch. P[t][c] = P[t * C + c] (p_col false: r x C) or
+// P[c * r + t] (p_col true: C x r, requires r % 16 == 0). out2 (optional)
+// receives the first out2_ld columns with leading dim out2_ld. Also writes
+// s*out split into bf16 hi/lo (M x rp each) when hi != NULL.
+qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, const uint16_t *P,
+                           bool p_col, int r, int rp, float *out, float *out2, int out2_ld,
+                           float s, uint16_t *hi, uint16_t *lo, hipStream_t st);
 // Two problems out = s * sum_m In[m][c] * Q[m][t] rounded to bf16 (In M x C,
 // Q M x rp fp32) in one launch plus one reduction launch.
 // transpose_out == 0: out is C x r (ld r); == 1: out is r x C (ld C).
@@ -48,15 +48,16 @@ qlora_status launch_colacc2(const ColaccReq &a, const ColaccReq &b, int64_t M, i
                             int r, float s, float *part, hipStream_t st);
 size_t colacc_part_bytes(int64_t M, int64_t C0, int64_t C1, int rp);
 
-// gemm.hip : fused dequant-GEMM, forward (Y) and input-gradient (dX) forms
+// gemm.hip : fused dequant-GEMM, forward (Y) and input-gradient (dX) forms.
+// The rank-r epilogue reads B (d x r) resp. A (r x k) in place.
 qlora_status launch_gemm_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
                              int64_t k, const uint16_t *X, int64_t M,
-                             const uint16_t *Bp, const uint16_t *Hs_hi,
+                             const uint16_t *B, int r, const uint16_t *Hs_hi,
                              const uint16_t *Hs_lo, int rp, uint16_t *Y,
                              hipStream_t st);
 qlora_status launch_gemm_dx(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
                             int64_t k, const uint16_t *dY, int64_t M,
-                            const uint16_t *At, const uint16_t *Gs_hi,
+                            const uint16_t *A, int r, const uint16_t *Gs_hi,
                             const uint16_t *Gs_lo, int rp, uint16_t *dX,
                             hipStream_t st);
 

@@ -7,18 +7,20 @@
 //             dA = s G^T X               (r x k, bf16)
 // Each reads one M x C activation once (X or dY) and is memory-bound; the
 // aim is to keep enough loads in flight and few launches.
-//   * skinny: out[m][t] = sum_c In[m][c] P[t][c] on MFMA 16x16x32 (the rows
-//     of In and of P are both contiguous in c). A wave owns a 16-token x
-//     16-t block over a contiguous range of c and issues the loads of eight
-//     32-wide K-slices before their MFMAs; the c range is split S ways
-//     (S <= 8) into partial sums that a second kernel adds in a fixed order,
-//     also emitting s*out as bf16 hi/lo parts for the fused GEMM epilogue.
+//   * skinny: out[m][t] = sum_c In[m][c] P[t][c] on MFMA 16x16x32, one
+//     launch: a workgroup owns a 16-token x 16-t block, its 16 waves split
+//     the c range and issue the loads of eight 32-wide K-slices before their
+//     MFMAs, and the waves' sums are added in LDS in a fixed order; it also
+//     emits s*out as bf16 hi/lo parts for the fused GEMM epilogue. P is A
+//     (rows contiguous in c) or B read in place (columns contiguous in t),
+//     transposed per K-slice through LDS.
 //   * colacc: out[c][t] = s sum_m In[m][c] Q[m][t] on float32 FMA, one lane
-//     per two columns, the Q rows of four tokens at a time read by scalar
-//     loads; eight waves per workgroup on disjoint token ranges, reduced in
-//     LDS in a fixed order; the token range is split S ways into partial sums
-//     that a second kernel adds in a fixed order. dB and dA run as two
-//     problems of one launch, and their reductions as one launch.
+//     per four columns and 16 t, rows streamed 16 tokens per batch with the
+//     next batch in flight, the batch's Q block broadcast from LDS; eight
+//     waves per workgroup on disjoint token ranges, reduced in LDS in a fixed
+//     order; the token range is split S ways into partial sums that a second
+//     kernel adds in a fixed order. dB and dA run as two problems of one
+//     launch, and their reductions as one launch.
 //   * layout: the zero-padded and transposed copies of A and B the other
 //     kernels read (A^T for the dX epilogue, B^T for G), in one launch.
 // r is padded to rp (a multiple of 16) with zero rows/columns.
@@ -62,26 +64,37 @@ __global__ __launch_bounds__(256) void layout_kernel(LayoutJobs jobs) {
 }
 
 // ---- skinny -----------------------------------------------------------------
-constexpr int SK_MAXSPLIT = 8;
+constexpr int SK_W = 16;       // waves per workgroup (column ranges of one token block)
 constexpr int SK_UNROLL = 8;   // K-slices of 32 whose loads are issued together
 
-// grid: x = wave items (m-block, t-block) / 4 per workgroup, y = split
-__global__ __launch_bounds__(256) void skinny_kernel(const uint16_t *__restrict__ In, int64_t M,
-                                                     int64_t C, const uint16_t *__restrict__ P,
-                                                     int rp, int64_t cps,
-                                                     float *__restrict__ part) {
+// out[m][t] = sum_c In[m][c] P[t][c] for the 16 tokens of block blockIdx.x and
+// t = 16 blockIdx.y + 0..15 (t < r; the rest are zero). P[t][c] is
+// Pm[t * C + c] (PCOL = false: A, r x C) or Pm[c * r + t] (PCOL = true: B,
+// C x r, r % 16 == 0). Wave w contracts columns [w cpw, (w+1) cpw) on
+// MFMA 16x16x32; for PCOL each K-slice's 8 x 16 block of B per lane group
+// is transposed through the wave's own LDS slot. The 16 waves' sums are
+// added in LDS in a fixed order and written as out (M x rp), out2 (M x r,
+// optional) and s*out as bf16 hi + lo parts (optional).
+template <bool PCOL>
+__global__ __launch_bounds__(64 * SK_W) void skinny_kernel(
+    const uint16_t *__restrict__ In, int64_t M, int64_t C, const uint16_t *__restrict__ Pm, int r,
+    int rp, int64_t cpw, float *__restrict__ out, float *__restrict__ out2, int out2_ld, float s,
+    uint16_t *__restrict__ hi, uint16_t *__restrict__ lo) {
+  constexpr int PQ = 272;   // bytes per lane group in the transposition slot (256 + pad)
+  __shared__ f32x4 red[SK_W][64];
+  __shared__ __align__(16) unsigned char pst[PCOL ? SK_W : 1][4 * PQ];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t tb = rp / 16;
-  const int64_t mb = item / tb, tbi = item % tb;
-  if (mb * 16 >= M) return;
-  const int64_t split = blockIdx.y;
-  const int64_t c_lo = split * cps, c_hi = min(C, c_lo + cps);
   const int r16 = lane & 15, kq = lane >> 4;
+  const int64_t mb = blockIdx.x;
+  const int t0 = 16 * (int)blockIdx.y;
   const int64_t m = mb * 16 + r16;
   const bool m_ok = m < M;
   const uint16_t *inr = In + (m_ok ? m : 0) * C + 8 * kq;
-  const uint16_t *pr = P + (tbi * 16 + r16) * C + 8 * kq;
+  const int64_t c_lo = wave * cpw, c_hi = min(C, c_lo + cpw);
+  const bool t_ok = t0 + r16 < r;
+  const uint16_t *prow = Pm + (t_ok ? t0 + r16 : 0) * C + 8 * kq;          // !PCOL
+  const int rho = (lane >> 1) & 7, hf = lane & 1;                           // PCOL raw piece
+  unsigned char *slot = pst[PCOL ? wave : 0];
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int64_t c = c_lo; c < c_hi; c += 32 * SK_UNROLL) {
     uint4 a[SK_UNROLL], b[SK_UNROLL];
@@ -90,62 +103,66 @@ __global__ __launch_bounds__(256) void skinny_kernel(const uint16_t *__restrict_
       const int64_t cc = c + 32 * u;
       a[u] = ql::zero4();
       b[u] = ql::zero4();
-      if (cc + 8 * kq < c_hi) {   // C % 8 == 0: a chunk is all in or all out
+      if (cc + 8 * kq < c_hi) {   // c_hi % 8 == 0: a chunk is all in or all out
         if (m_ok) a[u] = *(const uint4 *)(inr + cc);
-        b[u] = *(const uint4 *)(pr + cc);
+        if (!PCOL && t_ok) b[u] = *(const uint4 *)(prow + cc);
+      }
+      if (PCOL) {
+        const int64_t row = cc + 8 * kq + rho;   // B row, t = t0 + 8 hf .. +7
+        if (row < c_hi) b[u] = *(const uint4 *)(Pm + row * r + t0 + 8 * hf);
+      }
+    }
+    if (PCOL) {
+      // lane (t = r16, kq) needs B rows cc + 8kq .. +7 of column t: write the
+      // raw pieces (group kq, row rho, half hf) and read them back by column
+#pragma unroll
+      for (int u = 0; u < SK_UNROLL; ++u) {
+        *(uint4 *)(slot + kq * PQ + rho * 32 + hf * 16) = b[u];
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t e0 = *(const uint16_t *)(slot + kq * PQ + (2 * q) * 32 + 2 * r16);
+          const uint32_t e1 = *(const uint16_t *)(slot + kq * PQ + (2 * q + 1) * 32 + 2 * r16);
+          w[q] = e0 | (e1 << 16);
+        }
+        b[u] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
 #pragma unroll
     for (int u = 0; u < SK_UNROLL; ++u) acc = ql::mfma16(a[u], b[u], acc);
   }
-  // lane holds D[4kq + i][r16] = out[m-block row 4kq+i][t = tbi*16 + r16]
+  // lane holds D[4kq + i][r16] = out[token 4kq+i of the block][t0 + r16]
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4 v = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < SK_W; ++w) {
+    const f32x4 x = red[w][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += x[i];
+  }
+  const int t = t0 + r16;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t mm = mb * 16 + 4 * kq + i;
-    if (mm < M) part[(split * M + mm) * rp + tbi * 16 + r16] = acc[i];
-  }
-}
-
-// one thread per 4 consecutive t of one token
-__global__ __launch_bounds__(256) void skinny_reduce_kernel(
-    const float *__restrict__ part, int S, int64_t M, int rp, float *__restrict__ out,
-    float *__restrict__ out2, int out2_ld, float s, uint16_t *__restrict__ hi,
-    uint16_t *__restrict__ lo) {
-  const int64_t idx4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx4 * 4 >= M * rp) return;
-  const int64_t idx = idx4 * 4;
-  const int64_t m = idx / rp, t = idx % rp;
-  float4 p[SK_MAXSPLIT];
-#pragma unroll
-  for (int sp = 0; sp < SK_MAXSPLIT; ++sp)
-    if (sp < S) p[sp] = *(const float4 *)(part + sp * M * rp + idx);
-  float v[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int sp = 0; sp < SK_MAXSPLIT; ++sp)
-    if (sp < S) {
-      v[0] += p[sp].x;
-      v[1] += p[sp].y;
-      v[2] += p[sp].z;
-      v[3] += p[sp].w;
-    }
-  *(float4 *)(out + idx) = make_float4(v[0], v[1], v[2], v[3]);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (out2 && t + e < out2_ld) out2[m * out2_ld + t + e] = v[e];
+    if (mm >= M) continue;
+    out[mm * rp + t] = v[i];
+    if (out2 && t < out2_ld) out2[mm * out2_ld + t] = v[i];
     if (hi) {
-      const float sv = s * v[e];
+      const float sv = s * v[i];
       const uint16_t hb = ql::f_to_bf16(sv);
-      hi[idx + e] = hb;
-      lo[idx + e] = ql::f_to_bf16(sv - ql::bf16_to_f(hb));
+      hi[mm * rp + t] = hb;
+      lo[mm * rp + t] = ql::f_to_bf16(sv - ql::bf16_to_f(hb));
     }
   }
 }
 
 // ---- colacc -------------------------------------------------------------------
-constexpr int CA_COLS = 128;     // columns per wave (two per lane)
+constexpr int CA_COLS = 256;     // columns per workgroup (four per lane)
 constexpr int CA_MAXSPLIT = 16;
-constexpr int CA_TOK = 4;        // tokens per inner batch
-constexpr int CA_W = 8;          // waves per workgroup
+constexpr int CA_TOK = 16;       // tokens per batch
+constexpr int CA_W = 8;          // waves per workgroup (token ranges)
 
 struct ColaccProb {
   const uint16_t *In;  // M x C
@@ -155,11 +172,58 @@ struct ColaccProb {
   int64_t groups;      // column groups of CA_COLS
 };
 
+// Batch of CA_TOK tokens of one wave: this lane's 4 columns of each token
+// row and its float4 of the batch's Q block (token l/4, t = t0 + 4(l%4)..);
+// tokens past the wave's range read as zero.
+struct CaBatch {
+  uint2 v[CA_TOK];
+  float4 q;
+};
+
+QL_DEV void ca_load(CaBatch &b, const uint16_t *inc, int64_t C, bool c_ok, const float *Q, int rp,
+                    int t0, int64_t m, int64_t m_hi, int lane) {
+#pragma unroll
+  for (int u = 0; u < CA_TOK; ++u) {
+    const int64_t mm = m + u < m_hi ? m + u : m_hi - 1;  // clamped; not accumulated
+    b.v[u] = c_ok ? *(const uint2 *)(inc + mm * C) : make_uint2(0u, 0u);
+  }
+  const int64_t mq = m + (lane >> 2);
+  b.q = mq < m_hi ? *(const float4 *)(Q + mq * rp + t0 + 4 * (lane & 3))
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// acc[c][t] += x[token][c] * Q[token][t] over the batch's tokens (the first
+// n of them when PART)
+template <bool PART>
+QL_DEV void ca_batch(float (&acc)[4][16], const CaBatch &b, const float4 *qs, int n) {
+#pragma unroll
+  for (int u = 0; u < CA_TOK; ++u) {
+    if (PART && u >= n) continue;  // wave-uniform
+    float q[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 f = qs[4 * u + i];   // same address in every lane
+      q[4 * i] = f.x; q[4 * i + 1] = f.y; q[4 * i + 2] = f.z; q[4 * i + 3] = f.w;
+    }
+    const float x[4] = {ql::bf16lo(b.v[u].x), ql::bf16hi(b.v[u].x), ql::bf16lo(b.v[u].y),
+                        ql::bf16hi(b.v[u].y)};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) acc[c][t] = fmaf(x[c], q[t], acc[c][t]);
+  }
+}
+
 // grid: x = column groups of problem 0 then problem 1 (times rp/16 t-blocks),
-// y = token split. The waves of a workgroup split the split's tokens.
+// y = token split. The eight waves of a workgroup take the same 256 columns
+// over disjoint token ranges, each streaming its rows in batches of 16
+// tokens with the next batch's loads in flight; the Q block of a batch is
+// staged in the wave's own LDS slot and read back as broadcasts. The waves'
+// sums are added in LDS in a fixed order.
 __global__ __launch_bounds__(64 * CA_W) void colacc_kernel(ColaccProb p0, ColaccProb p1,
                                                            int64_t M, int rp, int64_t mps) {
-  __shared__ float red[CA_W - 1][64][32];
+  __shared__ float4 qst[CA_W][64];
+  __shared__ float4 red[CA_W][16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t tbs = rp / 16;
   int64_t gx = blockIdx.x;
@@ -167,70 +231,51 @@ __global__ __launch_bounds__(64 * CA_W) void colacc_kernel(ColaccProb p0, Colacc
   const ColaccProb &P = second ? p1 : p0;
   if (second) gx -= p0.groups * tbs;
   const int64_t cg = gx / tbs, tb = gx % tbs;
-  const int64_t c0 = cg * CA_COLS + 2 * lane;
+  const int64_t c0 = cg * CA_COLS + 4 * lane;
   const int t0 = (int)tb * 16;
   const int64_t split = blockIdx.y;
   const int64_t m_lo = split * mps, m_hi = min(M, m_lo + mps);
   const int64_t span = m_hi - m_lo;
   const int64_t w_lo = m_lo + (span * wave) / CA_W, w_hi = m_lo + (span * (wave + 1)) / CA_W;
-  float acc[2][16];
+  float acc[4][16];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int t = 0; t < 16; ++t) acc[c][t] = 0.0f;
-  const bool c_ok = c0 < P.C;  // C % 8 == 0, so c0 + 1 < C as well
+  const bool c_ok = c0 < P.C;  // C % 64 == 0: the 4 columns are all in or all out
   const uint16_t *inc = P.In + (c_ok ? c0 : 0);
-  int64_t m = w_lo;
-  for (; m + CA_TOK <= w_hi; m += CA_TOK) {
-    uint32_t v[CA_TOK];
-#pragma unroll
-    for (int u = 0; u < CA_TOK; ++u) v[u] = c_ok ? *(const uint32_t *)(inc + (m + u) * P.C) : 0u;
-#pragma unroll
-    for (int u = 0; u < CA_TOK; ++u) {
-      // Q row m+u is wave-uniform: scalar loads, broadcast to the FMAs
-      const float *qrow = P.Q + (m + u) * rp + t0;
-      const float x0 = ql::bf16lo(v[u]), x1 = ql::bf16hi(v[u]);
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const float qv = qrow[t];
-        acc[0][t] = fmaf(x0, qv, acc[0][t]);
-        acc[1][t] = fmaf(x1, qv, acc[1][t]);
-      }
+  if (w_lo < w_hi) {
+    CaBatch cur, nxt;
+    ca_load(nxt, inc, P.C, c_ok, P.Q, rp, t0, w_lo, w_hi, lane);
+    for (int64_t m = w_lo; m < w_hi; m += CA_TOK) {
+      cur = nxt;
+      if (m + CA_TOK < w_hi) ca_load(nxt, inc, P.C, c_ok, P.Q, rp, t0, m + CA_TOK, w_hi, lane);
+      qst[wave][lane] = cur.q;   // this wave's previous reads of the slot precede (in order)
+      if (m + CA_TOK <= w_hi)
+        ca_batch<false>(acc, cur, qst[wave], CA_TOK);
+      else
+        ca_batch<true>(acc, cur, qst[wave], (int)(w_hi - m));
     }
   }
-  for (; m < w_hi; ++m) {
-    const uint32_t v = c_ok ? *(const uint32_t *)(inc + m * P.C) : 0u;
-    const float *qrow = P.Q + m * rp + t0;
-    const float x0 = ql::bf16lo(v), x1 = ql::bf16hi(v);
+  // the waves' sums in a fixed order: ((wave 0 + 1) + 2) + ... ; thread p of
+  // the workgroup finishes float4 entries p and p + 512 of the 64 x 16 grid
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const float qv = qrow[t];
-      acc[0][t] = fmaf(x0, qv, acc[0][t]);
-      acc[1][t] = fmaf(x1, qv, acc[1][t]);
-    }
-  }
-  // reduce the waves in a fixed order: ((wave 0 + 1) + 2) + ...
-  if (wave > 0) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int t = 0; t < 16; ++t) red[wave - 1][lane][c * 16 + t] = acc[c][t];
-  }
+  for (int i = 0; i < 16; ++i)
+    red[wave][i][lane] = make_float4(acc[i >> 2][4 * (i & 3)], acc[i >> 2][4 * (i & 3) + 1],
+                                     acc[i >> 2][4 * (i & 3) + 2], acc[i >> 2][4 * (i & 3) + 3]);
   __syncthreads();
-  if (wave == 0 && c_ok) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float o[16];
+  for (int h = 0; h < 2; ++h) {
+    const int e = (int)threadIdx.x + 512 * h;
+    const int l = e & 63, i = e >> 6;
+    float4 o = red[0][i][l];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        o[t] = acc[c][t];
-#pragma unroll
-        for (int w = 0; w < CA_W - 1; ++w) o[t] += red[w][lane][c * 16 + t];
-      }
-      float *dst = P.part + (split * P.C + c0 + c) * rp + t0;
-#pragma unroll
-      for (int t = 0; t < 16; t += 4) *(float4 *)(dst + t) = make_float4(o[t], o[t + 1], o[t + 2], o[t + 3]);
+    for (int w = 1; w < CA_W; ++w) {
+      const float4 v = red[w][i][l];
+      o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
     }
+    const int64_t c = cg * CA_COLS + 4 * l + (i >> 2);
+    if (c < P.C) *(float4 *)(P.part + (split * P.C + c) * rp + t0 + 4 * (i & 3)) = o;
   }
 }
 
@@ -270,19 +315,11 @@ __global__ __launch_bounds__(256) void colacc_reduce_kernel(ColaccOut o0, Colacc
 }
 
 int64_t colacc_split(int64_t M, int64_t C, int rp) {
-  // about 256 workgroups of CA_W waves, each wave with at least 64 tokens
+  // about 256 workgroups of CA_W waves, each wave with at least 16 tokens
   const int64_t wgs = ql_cdiv(C, CA_COLS) * (rp / 16);
   int64_t S = ql_cdiv(256, wgs);
-  S = std::min<int64_t>(S, std::max<int64_t>(1, M / (64 * CA_W)));
+  S = std::min<int64_t>(S, std::max<int64_t>(1, M / (CA_TOK * CA_W)));
   return std::min<int64_t>(std::max<int64_t>(S, 1), CA_MAXSPLIT);
-}
-
-int64_t host_skinny_split(int64_t M, int64_t C, int rp) {
-  // about 2048 waves in all, each with at least 8 K-slices of 32
-  const int64_t items = ql_cdiv(M, 16) * (rp / 16);
-  int64_t S = ql_cdiv(2048, items);
-  S = std::min<int64_t>(S, std::max<int64_t>(1, C / (32 * SK_UNROLL)));
-  return std::min<int64_t>(std::max<int64_t>(S, 1), SK_MAXSPLIT);
 }
 
 }  // namespace
@@ -307,26 +344,21 @@ qlora_status launch_layout(const LayoutReq *req, int nreq, hipStream_t st) {
   return QLORA_OK;
 }
 
-size_t skinny_part_bytes(int64_t M, int64_t C, int rp) {
-  return (size_t)(host_skinny_split(M, C, rp) * M * rp * 4);
-}
-
-qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, const uint16_t *P, int rp,
-                           float *part, float *out, int64_t out_ld, float *out2, int out2_ld,
+qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, const uint16_t *P,
+                           bool p_col, int r, int rp, float *out, float *out2, int out2_ld,
                            float s, uint16_t *hi, uint16_t *lo, hipStream_t st) {
-  (void)out_ld;
-  const int64_t S0 = host_skinny_split(M, C, rp);
-  const int64_t cps = ql_rup(ql_cdiv(C, S0), 32);
-  const int64_t S = ql_cdiv(C, cps);
-  const int64_t items = ql_cdiv(M, 16) * (rp / 16);
-  dim3 grid((unsigned)ql_cdiv(items, 4), (unsigned)S);
-  {
-    QlProf prof(QLORA_K_LORA_DOWN, st);
-    skinny_kernel<<<grid, 256, 0, st>>>(In, M, C, P, rp, cps, part);
-  }
-  QlProf prof(QLORA_K_LORA_REDUCE, st);
-  skinny_reduce_kernel<<<(unsigned)ql_cdiv(M * rp / 4, 256), 256, 0, st>>>(
-      part, (int)S, M, rp, out, out2, out2_ld, s, hi, lo);
+  if (p_col && (r % 16 != 0 || r != rp)) return QLORA_ERR_UNSUPPORTED;
+  const int64_t cpw = ql_rup(ql_cdiv(C, SK_W), 32);
+  const int64_t mbs = ql_cdiv(M, 16);
+  if (mbs > 0x7fffffff || rp / 16 > 65535) return QLORA_ERR_UNSUPPORTED;
+  dim3 grid((unsigned)mbs, (unsigned)(rp / 16));
+  QlProf prof(QLORA_K_LORA_DOWN, st);
+  if (p_col)
+    skinny_kernel<true><<<grid, 64 * SK_W, 0, st>>>(In, M, C, P, r, rp, cpw, out, out2, out2_ld,
+                                                    s, hi, lo);
+  else
+    skinny_kernel<false><<<grid, 64 * SK_W, 0, st>>>(In, M, C, P, r, rp, cpw, out, out2, out2_ld,
+                                                     s, hi, lo);
   QL_LAUNCH_CHECK();
   return QLORA_OK;
 }

@@ -105,6 +105,8 @@ def test_lora_branch_alone(ops, M):
     (136, 576, 4, 64, 16.0),      # r = 64, GEMV, ragged d
     (264, 128, 513, 8, 16.0),     # m tile + 1
     (8, 64, 2, 5, 10.0),          # smallest legal weight
+    (200, 320, 100, 32, 64.0),    # GEMM path, two rank blocks, B read in place
+    (96, 128, 40, 64, 16.0),      # GEMM path, four rank blocks, ragged m tile
 ])
 def test_ragged_shapes(ops, d, k, M, r, alpha):
     g, o = _case(ops, d, k, M, r, alpha, True, seed=d + k + M + r)
