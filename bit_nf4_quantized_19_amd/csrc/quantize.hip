@@ -45,9 +45,12 @@ constexpr int QT = 256;
 constexpr int QU = 8;      // chunks per lane
 constexpr int NHC = 64;    // global histogram copies (workgroup b adds to copy b % NHC)
 
-struct __align__(16) Cell {
-  float T, H;
-  uint32_t base, pad;
+// Cell table entry: the candidate threshold T_j and the bits of H_j with j in
+// the low four mantissa bits (every H_j is a power of two, so those bits are
+// zero in H_j itself): 8 bytes, one ds_read_b64 per weight.
+struct __align__(8) Cell {
+  float T;
+  uint32_t Hj;
 };
 
 __constant__ uint32_t c_thresh[15] = NF4_THRESH_BITS;
@@ -86,8 +89,8 @@ QL_DEV uint32_t encode8(const uint32_t u[4], float a, const Cell *cell) {
     c = min(max(c, 0), NF4_NCELL - 1);
     const Cell ce = cell[c];
     const float dd = fmaf(-ce.T, aa, w);
-    const float ee = fmaf(-ce.H, aa, dd);
-    const uint32_t code = ce.base + (ee > 0.0f ? 1u : 0u);
+    const float ee = fmaf(-__uint_as_float(ce.Hj & ~15u), aa, dd);
+    const uint32_t code = (ce.Hj & 15u) + (ee > 0.0f ? 1u : 0u);
     packed |= code << (8 * (e >> 1) + ((e & 1) ? 0 : 4));
   }
   return (a == 0.0f) ? 0x77777777u : packed;
@@ -107,9 +110,7 @@ __global__ __launch_bounds__(QT) void quantize_kernel(
   if (tid < NF4_NCELL) {
     const int j = c_cell[tid];
     cell[tid].T = __uint_as_float(c_thresh[j]);
-    cell[tid].H = __uint_as_float(c_halfgap[j]);
-    cell[tid].base = (uint32_t)j;
-    cell[tid].pad = 0;
+    cell[tid].Hj = c_halfgap[j] | (uint32_t)j;
   }
   if (DQ)
 #pragma unroll
@@ -157,8 +158,10 @@ __global__ __launch_bounds__(QT) void quantize_kernel(
   }
 }
 
+// one thread per word
 __global__ void zero_u64_kernel(unsigned long long *p, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0ull;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0ull;
 }
 
 // mu = nearest float32 (ties to even) of N / nb, N the numerator in units of
@@ -306,7 +309,7 @@ qlora_status launch_quantize(const uint16_t *W0, int64_t n, uint8_t *codes,
   }
   float *amax = (float *)ws;
   unsigned long long *hist = (unsigned long long *)((char *)ws + ql_rup(4 * nb, 256));
-  zero_u64_kernel<<<1, 256, 0, st>>>(hist, NHC * 256);
+  zero_u64_kernel<<<NHC, 256, 0, st>>>(hist, NHC * 256);
   {
     QlProf prof(QLORA_K_QUANTIZE, st);
     quantize_kernel<true><<<(unsigned)grid, QT, 0, st>>>((const uint4 *)W0, (uint32_t *)codes, amax,

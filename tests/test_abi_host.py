@@ -171,3 +171,15 @@ def test_invalid_arguments_return_status_without_launching():
     assert p.returncode == 0, p.stderr
     got = eval(p.stdout.strip().splitlines()[-1])
     assert got == EXPECTED
+
+
+def test_half_gaps_leave_room_for_the_packed_threshold_index():
+    # The quantiser's cell table stores H_j with the threshold index j (< 16)
+    # in the low four mantissa bits; that is lossless only because every H_j
+    # is a power of two (zero mantissa).
+    text = open(os.path.join(ROOT, "bit_nf4_quantized_19_amd", "csrc", "nf4_tables.h")).read()
+    hg = re.search(r"#define NF4_HALFGAP_BITS \{([^}]*)\}", text).group(1)
+    bits = [int(v.strip().rstrip("u"), 16) for v in hg.split(",")]
+    assert len(bits) == 15
+    for b in bits:
+        assert b & 0x7FFFFF == 0 and 0 < (b >> 23) < 255
