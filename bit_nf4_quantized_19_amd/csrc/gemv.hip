@@ -331,33 +331,41 @@ __global__ __launch_bounds__(256) void gemv_epilogue_kernel(
   __shared__ float hs[128];
   const int64_t m = blockIdx.y;
   const int tid = threadIdx.x;
+  // the loads that do not depend on H go first (slice partials of output j
+  // and the first 16 ranks of its B row), so one memory round trip covers
+  // them and the H partials
+  const int64_t j = (int64_t)blockIdx.x * 256 + tid;
+  const int64_t jc = j < d ? j : d - 1;
+  const uint4 b0 = *(const uint4 *)(Bp + jc * rp), b1 = *(const uint4 *)(Bp + jc * rp + 8);
+  float acc = 0.0f;
+#pragma unroll 4
+  for (int sp = 0; sp < S; ++sp) acc += part[((int64_t)sp * M + m) * d + jc];
   // H[m][t]: lane group grp adds partials p = grp, grp + ng, ... of rank t
   // (ng = 256 / rp groups), then rank t adds the groups in order
   {
     const int ng = 256 / rp, t = tid % rp, grp = tid / rp;
     if (grp < ng) {
-      float acc = 0.0f;
+      float ha = 0.0f;
 #pragma unroll 4
-      for (int p = grp; p < nhp; p += ng) acc += hpart[((int64_t)p * M + m) * rp + t];
-      hp[grp][t] = acc;
+      for (int p = grp; p < nhp; p += ng) ha += hpart[((int64_t)p * M + m) * rp + t];
+      hp[grp][t] = ha;
     }
     __syncthreads();
     if (tid < rp) {
-      float acc = 0.0f;
-      for (int gi = 0; gi < ng; ++gi) acc += hp[gi][tid];
-      hs[tid] = acc;
-      if (hsave && blockIdx.x == 0 && tid < r) hsave[m * r + tid] = acc;
+      float ha = 0.0f;
+      for (int gi = 0; gi < ng; ++gi) ha += hp[gi][tid];
+      hs[tid] = ha;
+      if (hsave && blockIdx.x == 0 && tid < r) hsave[m * r + tid] = ha;
     }
     __syncthreads();
   }
-  const int64_t j = (int64_t)blockIdx.x * 256 + tid;
   if (j >= d) return;
-  float acc = 0.0f;
-#pragma unroll 4
-  for (int sp = 0; sp < S; ++sp) acc += part[((int64_t)sp * M + m) * d + j];
+  const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
   float l = 0.0f;
-#pragma unroll 8
-  for (int t = 0; t < rp; ++t) l = fmaf(hs[t], ql::bf16_to_f(Bp[j * rp + t]), l);
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+    l = fmaf(hs[t], (t & 1) ? ql::bf16hi(bw[t >> 1]) : ql::bf16lo(bw[t >> 1]), l);
+  for (int t = 16; t < rp; ++t) l = fmaf(hs[t], ql::bf16_to_f(Bp[j * rp + t]), l);
   Y[m * d + j] = ql::f_to_bf16(acc + s * l);
 }
 
