@@ -15,6 +15,8 @@ Modules
                  rational arithmetic for the mean, float64 for the levels.
 ``oracle.lora``  The LoRA linear: forward, backward (chain rule) and merge,
                  all in float64 on bf16-exact inputs, rounded once to bf16.
+``oracle.adamw`` The 32-bit AdamW step of the LoRA matrices (the paged
+                 optimiser's update), elementwise float32 in a stated order.
 
 Every function cites the page passage it follows. A page is cited by its
 title and section, e.g. "QLoRA glossary (Ultralytics), 'QLoRA 的工作原理'".
