@@ -277,6 +277,59 @@ qlora_status qlora_merge(const qlora_nf4_weight *w, const uint16_t *A, const uin
                       (hipStream_t)stream);
 }
 
+// Device address of a buffer the AdamW step may touch: device memory as is,
+// page-locked host memory through its device mapping. Anything else
+// (pageable host memory, unknown pointers) is refused, so the kernel never
+// dereferences an address the device cannot reach.
+static bool device_view(const void *p, void **dp) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (a.type == hipMemoryTypeDevice) {
+    *dp = const_cast<void *>(p);
+    return true;
+  }
+  if (a.type == hipMemoryTypeHost && a.devicePointer) {
+    // the offset of p inside its allocation carries over to the mapping
+    *dp = (char *)a.devicePointer + ((const char *)p - (const char *)a.hostPointer);
+    return true;
+  }
+  return false;
+}
+
+qlora_status qlora_adamw_step(float *param, float *exp_avg, float *exp_avg_sq,
+                              const uint16_t *grad, uint16_t *param_bf16, int64_t n,
+                              const qlora_adamw_hparams *hp, int64_t step, void *stream) {
+  if (!param || !exp_avg || !exp_avg_sq || !grad || !param_bf16 || !hp || n < 1 || step < 1)
+    return QLORA_ERR_INVALID_ARG;
+  if (!aligned16(param) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) ||
+      ((uintptr_t)grad & 7u) || ((uintptr_t)param_bf16 & 7u))
+    return QLORA_ERR_INVALID_ARG;
+  const double b1 = hp->beta1, b2 = hp->beta2;
+  if (!(b1 >= 0.0 && b1 < 1.0) || !(b2 >= 0.0 && b2 < 1.0)) return QLORA_ERR_INVALID_ARG;
+  if (!(isfinite(hp->lr) && hp->lr >= 0.0) || !(isfinite(hp->eps) && hp->eps >= 0.0) ||
+      !(isfinite(hp->weight_decay) && hp->weight_decay >= 0.0))
+    return QLORA_ERR_INVALID_ARG;
+  void *dv[5];
+  const void *hv[5] = {param, exp_avg, exp_avg_sq, grad, param_bf16};
+  for (int i = 0; i < 5; ++i)
+    if (!device_view(hv[i], &dv[i])) return QLORA_ERR_INVALID_ARG;
+  AdamScalars s;
+  s.b1 = (float)b1;
+  s.b2 = (float)b2;
+  s.c1 = (float)(1.0 - b1);
+  s.c2 = (float)(1.0 - b2);
+  s.bc1 = (float)(1.0 - pow(b1, (double)step));
+  s.bc2 = (float)(1.0 - pow(b2, (double)step));
+  s.lr = (float)hp->lr;
+  s.eps = (float)hp->eps;
+  s.wd = (float)hp->weight_decay;
+  return launch_adamw((float *)dv[0], (float *)dv[1], (float *)dv[2], (const uint16_t *)dv[3],
+                      (uint16_t *)dv[4], n, s, (hipStream_t)stream);
+}
+
 }  // extern "C"
 
 // ---- kernel timing hooks ------------------------------------------------------

@@ -75,6 +75,13 @@ qlora_status launch_merge(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
                           int64_t k, const uint16_t *A, const uint16_t *B,
                           int r, float s, uint16_t *Wm, hipStream_t st);
 
+// adamw.hip : one AdamW step over n elements (scalars prepared on the host)
+struct AdamScalars {
+  float b1, b2, c1, c2, bc1, bc2, lr, eps, wd;
+};
+qlora_status launch_adamw(float *p, float *m, float *v, const uint16_t *g, uint16_t *out,
+                          int64_t n, const AdamScalars &s, hipStream_t st);
+
 // tables (quantize.hip)
 void host_codebook(float levels[16], float thresholds[15]);
 

@@ -66,12 +66,13 @@ SIGNATURES = {
     "qlora_profile_query": (ctypes.c_int, [_i32, ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_double)]),
     "qlora_profile_release": (ctypes.c_int, []),
+    "qlora_adamw_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
 }
 
 #: kernel ids of the timing hooks (QLORA_K_* in the header)
 KERNELS = ["quantize", "double_quant", "dequantize", "gemm_fwd", "gemm_dx", "gemv",
            "gemv_epilogue", "lora_down", "lora_reduce", "lora_colacc", "lora_colacc_reduce",
-           "merge", "layout"]
+           "merge", "layout", "adamw"]
 
 
 def lib() -> ctypes.CDLL:
@@ -256,6 +257,37 @@ def merge(w: NF4Weight, A: torch.Tensor, B: torch.Tensor, lora_alpha: float,
     _check(lib().qlora_merge(ctypes.byref(cw), A.data_ptr(), B.data_ptr(), r,
                              float(lora_alpha), Wm.data_ptr(), _stream(stream)), "qlora_merge")
     return Wm
+
+
+class AdamWHParamsC(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
+
+
+def adamw_step(param: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+               grad: torch.Tensor, param_bf16: torch.Tensor, step: int, lr: float = 2e-4,
+               beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+               weight_decay: float = 0.0, stream=None):
+    """One AdamW step in place on (param, exp_avg, exp_avg_sq) (float32) with
+    the bf16 gradient, writing the bf16 copy of the updated parameter.
+
+    The float32 state may be CUDA tensors or page-locked host tensors
+    (``pin_memory=True``; the paged-out state), which the kernel reads and
+    writes in place over the host link."""
+    n = param.numel()
+    for t, name in ((param, "param"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+            raise ValueError(f"{name} must be a contiguous float32 tensor of {n} elements")
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be a CUDA tensor or page-locked host memory")
+    for t, name in ((grad, "grad"), (param_bf16, "param_bf16")):
+        _dev_bf16(t, name)
+        if t.numel() != n:
+            raise ValueError(f"{name} must have {n} elements")
+    hp = AdamWHParamsC(lr, beta1, beta2, eps, weight_decay)
+    _check(lib().qlora_adamw_step(_ptr(param), _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(grad),
+                                  _ptr(param_bf16), n, ctypes.addressof(hp), int(step),
+                                  _stream(stream)), "qlora_adamw_step")
 
 
 def profile_begin(cap: int = 4096, kernels=None):

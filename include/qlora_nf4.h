@@ -149,6 +149,44 @@ qlora_status qlora_merge(const qlora_nf4_weight *w, const uint16_t *A,
                          const uint16_t *B, int32_t r, float lora_alpha,
                          uint16_t *W_merged, void *stream);
 
+/*
+ * One 32-bit AdamW step over the n elements of a LoRA matrix (A or B): the
+ * update of the paged optimiser (Day-25 notes 3.4: Adam's two moments kept in
+ * float32 and paged out to CPU RAM when device memory runs short; QLoRA
+ * glossary, "QLoRA 的工作原理", paged-optimiser bullet;
+ * "如何利用QLoRA在消费级GPU上实现大模型的高效微调", sections 3 and 4:
+ * paged_adamw_32bit). The pages print no update rule; this is AdamW as
+ * published (bias-corrected moments, decoupled weight decay).
+ *   param      [n] float32 master copy of A or B              (in/out)
+ *   exp_avg    [n] float32 first moment m                      (in/out)
+ *   exp_avg_sq [n] float32 second moment v                     (in/out)
+ *   grad       [n] bf16 gradient (dA or dB of qlora_linear_bwd) (in)
+ *   param_bf16 [n] bf16 copy of the updated param: the A or B the next
+ *              forward and backward read                      (out)
+ * `step` is the 1-based step count t. Per element, every float32 operation
+ * rounded once (IEEE division and square root), in this order:
+ *   m = b1*m + c1*g;  v = b2*v + c2*(g*g);
+ *   u = (m / bc1) / (sqrt(v / bc2) + eps);
+ *   param = param - lr * (u + weight_decay * param);  param_bf16 = bf16_rne(param)
+ * with b1, b2, lr, eps, weight_decay the float32 roundings of the
+ * hyperparameters and c1 = 1 - beta1, c2 = 1 - beta2, bc1 = 1 - beta1^t,
+ * bc2 = 1 - beta2^t evaluated in double and rounded once to float32.
+ * Paging: param, exp_avg and exp_avg_sq may be device memory or page-locked
+ * host memory mapped into the device address space (hipHostMalloc); the
+ * caller moves the state out to host memory when device memory is short and
+ * back when it is not, and the step updates it in place either way (over the
+ * host link when it is paged out). param, exp_avg, exp_avg_sq: 16-byte
+ * aligned; grad, param_bf16: 8-byte aligned; n >= 1; step >= 1;
+ * 0 <= beta1, beta2 < 1; lr, eps, weight_decay finite and >= 0; otherwise
+ * QLORA_ERR_INVALID_ARG and nothing is launched.
+ */
+typedef struct qlora_adamw_hparams {
+  double lr, beta1, beta2, eps, weight_decay;
+} qlora_adamw_hparams;
+qlora_status qlora_adamw_step(float *param, float *exp_avg, float *exp_avg_sq,
+                              const uint16_t *grad, uint16_t *param_bf16, int64_t n,
+                              const qlora_adamw_hparams *hp, int64_t step, void *stream);
+
 /* Bytes of the quantised record for d x k: d*k/2 + 4*nb (no double quant)
  * or d*k/2 + nb + 4*ceil(nb/256) + 4 (double quant), nb = d*k/64.
  * Returns 0 for an unsupported shape. */
@@ -183,7 +221,7 @@ enum {
   QLORA_K_GEMM_FWD = 3, QLORA_K_GEMM_DX = 4, QLORA_K_GEMV = 5, QLORA_K_GEMV_EPILOGUE = 6,
   QLORA_K_LORA_DOWN = 7, QLORA_K_LORA_REDUCE = 8, QLORA_K_LORA_COLACC = 9,
   QLORA_K_LORA_COLACC_REDUCE = 10, QLORA_K_MERGE = 11, QLORA_K_LAYOUT = 12,
-  QLORA_K_COUNT = 13
+  QLORA_K_ADAMW = 13, QLORA_K_COUNT = 14
 };
 qlora_status qlora_profile_begin(int32_t cap, uint32_t mask);
 qlora_status qlora_profile_end(void);

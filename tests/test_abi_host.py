@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     ops = _ops()
     L = ops.lib()
     names = _declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for name in names:
         assert hasattr(L, name), name
         assert name in ops.SIGNATURES, name
@@ -145,6 +145,24 @@ out["merge_null_out"] = L.qlora_merge(ctypes.byref(w), P, P, 8, 16.0, None, None
 out["merge_r_big"] = L.qlora_merge(ctypes.byref(w), P, P, 500, 16.0, P, None)
 out["deq_null_out"] = L.qlora_nf4_dequantize(ctypes.byref(w), None, None)
 out["codebook_null"] = L.qlora_nf4_codebook(None, None)
+class HP(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_double) for n in ("lr", "beta1", "beta2", "eps", "weight_decay")]
+def adam(name, step=1, n=64, hp=None, **kw):
+    a = dict(p=P, m=P, v=P, g=P, o=P)
+    a.update(kw)
+    h = hp if hp is not None else HP(2e-4, 0.9, 0.999, 1e-8, 0.0)
+    out[name] = L.qlora_adamw_step(a["p"], a["m"], a["v"], a["g"], a["o"], n,
+                                   ctypes.addressof(h), step, None)
+adam("adam_null_param", p=None)
+adam("adam_null_grad", g=None)
+adam("adam_n0", n=0)
+adam("adam_step0", step=0)
+adam("adam_misaligned_m", m=P + 8)
+adam("adam_misaligned_out", o=P + 2)
+adam("adam_beta1_one", hp=HP(2e-4, 1.0, 0.999, 1e-8, 0.0))
+adam("adam_neg_lr", hp=HP(-1e-3, 0.9, 0.999, 1e-8, 0.0))
+adam("adam_nan_eps", hp=HP(2e-4, 0.9, 0.999, float("nan"), 0.0))
+adam("adam_unknown_pointer")   # not memory the device can reach: refused
 print(repr(out))
 """
 
@@ -156,7 +174,9 @@ EXPECTED = {
     "fwd_inf_alpha": -1, "fwd_M0": -1, "fwd_null_X": -1, "fwd_misaligned_B": -1,
     "fwd_ws_small": -3, "bwd_null_dY": -1, "bwd_null_dA": -1, "bwd_ws_small": -3,
     "bwd_r0": -1, "merge_null_out": -1, "merge_r_big": -2, "deq_null_out": -1,
-    "codebook_null": -1,
+    "codebook_null": -1, "adam_null_param": -1, "adam_null_grad": -1, "adam_n0": -1,
+    "adam_step0": -1, "adam_misaligned_m": -1, "adam_misaligned_out": -1,
+    "adam_beta1_one": -1, "adam_neg_lr": -1, "adam_nan_eps": -1, "adam_unknown_pointer": -1,
 }
 
 
