@@ -334,6 +334,27 @@ def measure_rows(ops, synth, torch, dev):
             out["gemv"][f"{d}x{k}_M{Mt}"] = _row(gbytes, ms_call, _kernel_us(ops, "gemv", fg, nset, 96))
         del gq
         torch.cuda.empty_cache()
+    # paged 32-bit AdamW step over the LoRA parameters of a Llama-7B-shaped
+    # all-linear adapter set (32 layers x q,k,v,o 4096^2, gate/up 4096->11008,
+    # down 11008->4096; r = 16: 39,976,960 parameters) as one flat buffer,
+    # state in device memory; then a 4M-parameter slice of it with the state
+    # paged out to page-locked host memory (updated over the host link)
+    npar = 32 * (4 * 2 * R * 4096 + 3 * R * (4096 + 11008))
+    st = [torch.zeros(npar, dtype=torch.float32, device=dev) for _ in range(3)]
+    ga = synth.normal_bf16_device((npar,), 0.01, 51, device=dev)
+    oa = torch.empty(npar, dtype=torch.bfloat16, device=dev)
+    fa = lambda i: ops.adamw_step(st[0], st[1], st[2], ga, oa, 1)
+    abytes = 28 * npar
+    out["adamw"] = {"params": npar, "state": "device",
+                    **_row(abytes, _call_ms(fa, 1, 20), _kernel_us(ops, "adamw", fa, 1, 20))}
+    nh = 4 * 1024 * 1024
+    sth = [torch.zeros(nh, dtype=torch.float32).pin_memory() for _ in range(3)]
+    fh = lambda i: ops.adamw_step(sth[0], sth[1], sth[2], ga[:nh], oa[:nh], 1)
+    hbytes = 28 * nh
+    out["adamw_paged_out"] = {"params": nh, "state": "page-locked host",
+                              **_row(hbytes, _rotated(fh, 1, 10), _kernel_us(ops, "adamw", fh, 1, 10))}
+    del st, sth, ga, oa
+    torch.cuda.empty_cache()
     log(f"[bench] rows: {json.dumps(out)}")
     return out
 
