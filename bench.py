@@ -332,6 +332,20 @@ def measure_rows(ops, synth, torch, dev):
             ms_call = _call_ms(fg, nset, 96)
             gbytes = (ops.storage_bytes(d, k, True) + 2 * R * (d + k) + 2 * Mt * k + 2 * Mt * d)
             out["gemv"][f"{d}x{k}_M{Mt}"] = _row(gbytes, ms_call, _kernel_us(ops, "gemv", fg, nset, 96))
+            if d == 11008:
+                # sibling projections: gate and up (both 4096 -> 11008) read the
+                # same X in one call (8 distinct pairs)
+                Y2 = [torch.empty(Mt, d, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+                wsm = ops.workspace_bytes(ops.OP_FWD_MULTI, 2 * d, k, Mt, R, True)
+                wsmt = torch.empty(wsm + 256, dtype=torch.uint8, device=dev)
+                o3 = (-wsmt.data_ptr()) % 256
+                wsmt = wsmt[o3:o3 + wsm]
+                fp = lambda i: ops.linear_fwd_multi([gq[2 * i], gq[2 * i + 1]], Xg, [Ag, Ag],
+                                                    [Bg, Bg], ALPHA, save_h=False, Ys=Y2, ws=wsmt)
+                ms_pair = _call_ms(fp, nset // 2, 48)
+                pbytes = 2 * gbytes - 2 * Mt * k   # X read once
+                out["gemv"][f"gate_up_2x{d}x{k}_M{Mt}"] = _row(
+                    pbytes, ms_pair, _kernel_us(ops, "gemv", fp, nset // 2, 48))
         del gq
         torch.cuda.empty_cache()
     # paged 32-bit AdamW step over the LoRA parameters of a Llama-7B-shaped

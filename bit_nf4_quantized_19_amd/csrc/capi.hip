@@ -61,31 +61,44 @@ struct Carve {
   }
 };
 
+constexpr int kMaxGroup = 4;   // weights per qlora_linear_fwd_multi call
+
 struct FwdWs {
-  uint16_t *Ap, *Bp, *Hs_hi, *Hs_lo;
-  float *H, *gpart;
+  uint16_t *Ap[kMaxGroup], *Bp[kMaxGroup], *Hs_hi[kMaxGroup], *Hs_lo[kMaxGroup];
+  float *H[kMaxGroup], *gpart;
   int64_t bytes;
 };
 
-FwdWs fwd_layout(char *base, int64_t d, int64_t k, int64_t M, int r) {
+// nw weights of d[i] rows each that read the same X (M x k)
+FwdWs fwd_layout(char *base, const int64_t *d, int nw, int64_t k, int64_t M, int r) {
   const int rp = (int)ql_rup(r, 16);
   Carve c{base};
   FwdWs L{};
+  int64_t dtot = 0;
+  for (int i = 0; i < nw; ++i) dtot += d[i];
   if (M > 16) {
-    L.Ap = L.Bp = nullptr;
-    L.H = c.take<float>(M * rp * 4);
-    L.Hs_hi = c.take<uint16_t>(M * rp * 2);
-    L.Hs_lo = c.take<uint16_t>(M * rp * 2);
+    for (int i = 0; i < nw; ++i) {
+      L.H[i] = c.take<float>(M * rp * 4);
+      L.Hs_hi[i] = c.take<uint16_t>(M * rp * 2);
+      L.Hs_lo[i] = c.take<uint16_t>(M * rp * 2);
+    }
     L.gpart = nullptr;
   } else {  // the GEMV computes H itself from zero-padded A and B
-    L.Ap = (r % 16) ? c.take<uint16_t>((int64_t)rp * k * 2) : nullptr;
-    L.Bp = (r % 16) ? c.take<uint16_t>(d * rp * 2) : nullptr;
-    L.H = nullptr;
-    L.Hs_hi = L.Hs_lo = nullptr;
-    L.gpart = c.take<float>((int64_t)gemv_part_bytes(d, k, M, rp));
+    for (int i = 0; i < nw; ++i) {
+      L.Ap[i] = (r % 16) ? c.take<uint16_t>((int64_t)rp * k * 2) : nullptr;
+      L.Bp[i] = (r % 16) ? c.take<uint16_t>(d[i] * rp * 2) : nullptr;
+    }
+    L.gpart = c.take<float>((int64_t)gemv_part_bytes(dtot, k, M, rp, nw));
   }
   L.bytes = c.off;
   return L;
+}
+
+// Bound for any split of dtot rows over up to kMaxGroup weights: the pieces
+// that scale with d sum to the same bytes up to one alignment each.
+int64_t fwd_multi_bytes(int64_t dtot, int64_t k, int64_t M, int r) {
+  const int64_t d[kMaxGroup] = {dtot, 0, 0, 0};
+  return fwd_layout(nullptr, d, kMaxGroup, k, M, r).bytes + kMaxGroup * kAlign;
 }
 
 struct BwdWs {
@@ -141,7 +154,8 @@ size_t qlora_workspace_bytes(int32_t op, int64_t d, int64_t k, int64_t M, int32_
   if (check_weight_shape(d, k) != QLORA_OK) return (size_t)-1;
   if (op == QLORA_OP_QUANTIZE) return quantize_ws_bytes(d * k, double_quant);
   if (M < 1 || r < 1 || r > 128) return (size_t)-1;
-  if (op == QLORA_OP_FWD) return (size_t)fwd_layout(nullptr, d, k, M, r).bytes;
+  if (op == QLORA_OP_FWD) return (size_t)fwd_layout(nullptr, &d, 1, k, M, r).bytes;
+  if (op == QLORA_OP_FWD_MULTI) return (size_t)fwd_multi_bytes(d, k, M, r);
   // backward: sized for the largest case (H recomputed, dX requested)
   if (op == QLORA_OP_BWD) return (size_t)bwd_layout(nullptr, d, k, M, r, true, true).bytes;
   return (size_t)-1;
@@ -180,39 +194,86 @@ static qlora_status check_lora(const uint16_t *A, const uint16_t *B, int32_t r, 
   return QLORA_OK;
 }
 
+// Forward of nw weights that read the same X (nw == 1: qlora_linear_fwd).
+static qlora_status linear_fwd_group(const qlora_nf4_weight *const *w, int nw, const uint16_t *X,
+                                     int64_t M, const uint16_t *const *A,
+                                     const uint16_t *const *B, int32_t r, float lora_alpha,
+                                     uint16_t *const *Y, float *const *H_save, void *ws,
+                                     size_t ws_bytes, void *stream, int64_t ws_need) {
+  if (nw < 1 || nw > kMaxGroup || !w || !A || !B || !Y) return QLORA_ERR_INVALID_ARG;
+  qlora_status s;
+  int64_t d[kMaxGroup];
+  for (int i = 0; i < nw; ++i) {
+    if ((s = check_weight(w[i], false)) != QLORA_OK) return s;
+    if ((s = check_lora(A[i], B[i], r, lora_alpha)) != QLORA_OK) return s;
+    if (!Y[i] || !aligned16(Y[i])) return QLORA_ERR_INVALID_ARG;
+    if (H_save && H_save[i] && ((uintptr_t)H_save[i] & 3u)) return QLORA_ERR_INVALID_ARG;
+    if (w[i]->k != w[0]->k || w[i]->double_quant != w[0]->double_quant)
+      return QLORA_ERR_INVALID_ARG;
+    d[i] = w[i]->d;
+  }
+  if (!X || !aligned16(X) || M < 1) return QLORA_ERR_INVALID_ARG;
+  const int64_t k = w[0]->k;
+  const FwdWs L = fwd_layout((char *)ws, d, nw, k, M, r);
+  if (ws_need < L.bytes) ws_need = L.bytes;
+  if (!ws_ok(ws, ws_bytes, ws_need)) return QLORA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int rp = (int)ql_rup(r, 16);
+  const float sc = lora_alpha / (float)r;
+
+  if (M <= 16) {  // H = X A^T inside the GEMV; H_save gets the M x r copy
+    GemvIn in[kMaxGroup];
+    for (int i = 0; i < nw; ++i) {
+      const uint16_t *Ap = A[i], *Bp = B[i];
+      if (r % 16) {
+        const LayoutReq req[2] = {{A[i], r, k, L.Ap[i], rp, k, 0}, {B[i], d[i], r, L.Bp[i], d[i], rp, 0}};
+        if ((s = launch_layout(req, 2, st)) != QLORA_OK) return s;
+        Ap = L.Ap[i];
+        Bp = L.Bp[i];
+      }
+      in[i] = GemvIn{w[i]->codes, scale_src(w[i]), d[i], Ap, Bp, H_save ? H_save[i] : nullptr, Y[i]};
+    }
+    return launch_gemv_fwd(nw, in, k, X, M, r, rp, sc, L.gpart, st);
+  }
+  for (int i = 0; i < nw; ++i) {
+    // H = X A^T (float32, M x rp) and s*H as bf16 hi/lo; H_save gets the M x r copy
+    if ((s = launch_skinny(X, M, k, A[i], false, r, rp, L.H[i], H_save ? H_save[i] : nullptr, r,
+                           sc, L.Hs_hi[i], L.Hs_lo[i], st)) != QLORA_OK)
+      return s;
+    if ((s = launch_gemm_fwd(w[i]->codes, scale_src(w[i]), d[i], k, X, M, B[i], r, L.Hs_hi[i],
+                             L.Hs_lo[i], rp, Y[i], st)) != QLORA_OK)
+      return s;
+  }
+  return QLORA_OK;
+}
+
 qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
                               const uint16_t *A, const uint16_t *B, int32_t r, float lora_alpha,
                               uint16_t *Y, float *H_save, void *ws, size_t ws_bytes,
                               void *stream) {
-  qlora_status s = check_weight(w, false);
-  if (s != QLORA_OK) return s;
-  if ((s = check_lora(A, B, r, lora_alpha)) != QLORA_OK) return s;
-  if (!X || !Y || !aligned16(X) || !aligned16(Y) || M < 1) return QLORA_ERR_INVALID_ARG;
-  if (H_save && ((uintptr_t)H_save & 3u)) return QLORA_ERR_INVALID_ARG;
-  const int64_t d = w->d, k = w->k;
-  const FwdWs need = fwd_layout(nullptr, d, k, M, r);
-  if (!ws_ok(ws, ws_bytes, need.bytes)) return QLORA_ERR_WORKSPACE;
-  const FwdWs L = fwd_layout((char *)ws, d, k, M, r);
-  hipStream_t st = (hipStream_t)stream;
-  const int rp = (int)ql_rup(r, 16);
-  const float sc = lora_alpha / (float)r;
-  const ql::ScaleSrc src = scale_src(w);
+  if (!w) return QLORA_ERR_INVALID_ARG;
+  const qlora_nf4_weight *const wl[1] = {w};
+  const uint16_t *const Al[1] = {A}, *const Bl[1] = {B};
+  uint16_t *const Yl[1] = {Y};
+  float *const Hl[1] = {H_save};
+  return linear_fwd_group(wl, 1, X, M, Al, Bl, r, lora_alpha, Yl, Hl, ws, ws_bytes, stream, 0);
+}
 
-  if (M <= 16) {  // H = X A^T inside the GEMV; H_save gets the M x r copy
-    const uint16_t *Ap = A, *Bp = B;
-    if (r % 16) {
-      const LayoutReq req[2] = {{A, r, k, L.Ap, rp, k, 0}, {B, d, r, L.Bp, d, rp, 0}};
-      if ((s = launch_layout(req, 2, st)) != QLORA_OK) return s;
-      Ap = L.Ap;
-      Bp = L.Bp;
-    }
-    return launch_gemv_fwd(w->codes, src, d, k, X, M, Ap, Bp, r, rp, sc, L.gpart, H_save, Y, st);
+qlora_status qlora_linear_fwd_multi(const qlora_nf4_weight *const *w, int32_t nw,
+                                    const uint16_t *X, int64_t M, const uint16_t *const *A,
+                                    const uint16_t *const *B, int32_t r, float lora_alpha,
+                                    uint16_t *const *Y, float *const *H_save, void *ws,
+                                    size_t ws_bytes, void *stream) {
+  if (nw < 1 || nw > kMaxGroup || !w) return QLORA_ERR_INVALID_ARG;
+  int64_t dtot = 0;
+  for (int i = 0; i < nw; ++i) {
+    if (!w[i]) return QLORA_ERR_INVALID_ARG;
+    dtot += w[i]->d;
   }
-  // H = X A^T (float32, M x rp) and s*H as bf16 hi/lo; H_save gets the M x r copy
-  if ((s = launch_skinny(X, M, k, A, false, r, rp, L.H, H_save, r, sc, L.Hs_hi, L.Hs_lo, st)) !=
-      QLORA_OK)
-    return s;
-  return launch_gemm_fwd(w->codes, src, d, k, X, M, B, r, L.Hs_hi, L.Hs_lo, rp, Y, st);
+  if (check_weight_shape(dtot, w[0]->k) != QLORA_OK) return QLORA_ERR_UNSUPPORTED;
+  // the documented size (qlora_workspace_bytes(QLORA_OP_FWD_MULTI, sum of d, ...))
+  const int64_t need = (r >= 1 && r <= 128 && M >= 1) ? fwd_multi_bytes(dtot, w[0]->k, M, r) : 0;
+  return linear_fwd_group(w, nw, X, M, A, B, r, lora_alpha, Y, H_save, ws, ws_bytes, stream, need);
 }
 
 qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
@@ -331,6 +392,18 @@ qlora_status qlora_adamw_step(float *param, float *exp_avg, float *exp_avg_sq,
 }
 
 }  // extern "C"
+
+int ql_num_cus() {
+  static int ncu = 0;
+  if (ncu == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    ncu = n;
+  }
+  return ncu;
+}
 
 // ---- kernel timing hooks ------------------------------------------------------
 namespace {

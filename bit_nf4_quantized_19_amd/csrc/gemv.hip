@@ -46,6 +46,7 @@ constexpr int GW = 8;            // waves per workgroup, one row group of 16 row
 constexpr int GT = 64 * GW;
 constexpr int GX = 2048 / GT;    // X chunks (16 tokens x 16 blocks x 8) per thread
 constexpr int GB = 16;           // blocks per slice (1024 columns)
+constexpr int GMAXW = 4;         // weights per grouped call
 // LDS: 256 rows of 256 bytes (table copies in bytes 0-127, X in 128-255),
 // then the zero region read by lanes outside their token group
 constexpr uint32_t ZBASE = 65536 + 64;
@@ -53,21 +54,61 @@ constexpr uint32_t ZBYTES = 15 * 256 + 64 + 16;
 constexpr int LDS_BYTES = (int)(ZBASE + ZBYTES);
 __constant__ uint32_t c_levels_v[16] = NF4_LEVEL_BITS;
 
-struct GemvArgs {
+// One weight of a grouped call (sibling projections that read the same X).
+struct GemvW {
   const uint8_t *codes;
   ql::ScaleSrc sc;
-  int64_t d, k;
-  const uint16_t *X;
-  int64_t M;
+  int64_t d;
   int64_t nb;      // blocks of the weight (d k / 64)
-  int64_t ngroups; // row groups of 16 rows
-  int G;           // workgroups per slice
-  int rpw;         // row groups per workgroup, <= 2 GW (the last ones may be past the end)
-  float *part;     // [S][M][d]
+  int64_t gbase;   // first row group of this weight in the grouped numbering
+  int64_t rbase;   // first column of this weight in the partial-sum rows
   const uint16_t *Ap;  // LoRA A, rp x k (ranks past r are zero rows)
-  int rp;
   float *hpart;    // [S * GW][M][rp]: H = X A^T partial sums per slice and wave
 };
+
+struct GemvArgs {
+  GemvW w[GMAXW];
+  int nw;          // weights in the call (1..GMAXW)
+  int64_t k;
+  const uint16_t *X;
+  int64_t M;
+  int64_t ngroups; // row groups of 16 rows, all weights
+  int G;           // workgroups per slice
+  int rpw;         // row groups per workgroup, <= 2 GW (the last ones may be past the end)
+  float *part;     // [S][M][dtot]: slice partial sums, weights side by side
+  int64_t dtot;
+  int rp;
+};
+
+// Weight i of the call, field by field through uniform selects (a dynamic
+// index into the argument block would copy it to scratch memory).
+template <class T>
+QL_DEV T pick4(int i, T a0, T a1, T a2, T a3) {
+  return i == 0 ? a0 : i == 1 ? a1 : i == 2 ? a2 : a3;
+}
+#define QL_PICK(arr, i, f) pick4(i, arr[0].f, arr[1].f, arr[2].f, arr[3].f)
+QL_DEV GemvW wsel(const GemvArgs &g, int i) {
+  GemvW W;
+  W.codes = QL_PICK(g.w, i, codes);
+  W.sc.absmax = QL_PICK(g.w, i, sc.absmax);
+  W.sc.q = QL_PICK(g.w, i, sc.q);
+  W.sc.s2 = QL_PICK(g.w, i, sc.s2);
+  W.sc.mu = QL_PICK(g.w, i, sc.mu);
+  W.sc.dq = QL_PICK(g.w, i, sc.dq);
+  W.d = QL_PICK(g.w, i, d);
+  W.nb = QL_PICK(g.w, i, nb);
+  W.gbase = QL_PICK(g.w, i, gbase);
+  W.rbase = QL_PICK(g.w, i, rbase);
+  W.Ap = QL_PICK(g.w, i, Ap);
+  W.hpart = QL_PICK(g.w, i, hpart);
+  return W;
+}
+QL_DEV int weight_of(const GemvArgs &g, int64_t rg) {
+  int i = 0;
+#pragma unroll
+  for (int j = 1; j < GMAXW; ++j) i += (j < g.nw && rg >= g.w[j].gbase) ? 1 : 0;
+  return i;
+}
 
 // LDS byte offset of X[token 4 tp + t][slice block 4c + g][8s .. 8s+7]: row
 // tp*64 + g*16 + c*4 + s/2, upper half, 16-byte slot (s%2)*4 + t
@@ -84,34 +125,42 @@ struct GUnit {
   uint32_t qw[5];   // int8 scale codes of the row's slice (aligned dwords)
   float araw[4];    // absmax of blocks 4c + q (no double quantisation)
   float s2lo, s2hi;
+  float mu;         // the weight's DQ mean
   int64_t blk0;     // first block of the row's slice
-  int64_t row0;     // first row of the unit
+  int64_t row0;     // first row of the unit (in its weight)
+  int64_t dlim;     // rows of its weight
+  int64_t rbase;    // its weight's first column in the partial-sum rows
 };
 
 template <bool DQ, bool FULL>
 QL_DEV void unit_load(const GemvArgs &g, GUnit &u, int64_t rg, int64_t b0, int nblk, int n,
                       int q) {
   const int64_t nbr = g.k >> 6;
-  u.row0 = rg * 16;
-  const int64_t row = min(u.row0 + n, g.d - 1);
+  const GemvW W = wsel(g, weight_of(g, rg));   // rg is wave-uniform
+  u.row0 = (rg - W.gbase) * 16;
+  u.dlim = W.d;
+  u.rbase = W.rbase;
+  const int64_t row = min(u.row0 + n, W.d - 1);
   u.blk0 = row * nbr + b0;
   if (DQ) {
-    u.s2lo = g.sc.s2[u.blk0 >> 8];
-    u.s2hi = g.sc.s2[(u.blk0 + nblk - 1) >> 8];
+    u.mu = W.sc.mu[0];
+    u.s2lo = W.sc.s2[u.blk0 >> 8];
+    u.s2hi = W.sc.s2[(u.blk0 + nblk - 1) >> 8];
     // the row's int8 codes from the 5 aligned dwords around them (the code
     // array has a multiple of 8 bytes, so a clamped dword index stays in it)
-    const uint32_t *qp = (const uint32_t *)g.sc.q;
-    const int64_t w0 = u.blk0 >> 2, wlast = (g.nb >> 2) - 1;
+    const uint32_t *qp = (const uint32_t *)W.sc.q;
+    const int64_t w0 = u.blk0 >> 2, wlast = (W.nb >> 2) - 1;
 #pragma unroll
     for (int j = 0; j < 5; ++j) u.qw[j] = qp[min(w0 + j, wlast)];
   } else {
+    u.mu = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      u.araw[c] = g.sc.absmax[u.blk0 + (FULL ? 4 * c + q : min(4 * c + q, nblk - 1))];
+      u.araw[c] = W.sc.absmax[u.blk0 + (FULL ? 4 * c + q : min(4 * c + q, nblk - 1))];
   }
   // blocks past the end of a ragged slice re-read the last block; their X
   // chunks are zero
-  const uint8_t *crow = g.codes + row * (g.k >> 1) + b0 * 32;
+  const uint8_t *crow = W.codes + row * (g.k >> 1) + b0 * 32;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int bb = FULL ? 4 * c + q : min(4 * c + q, nblk - 1);
@@ -126,7 +175,7 @@ QL_DEV void unit_load(const GemvArgs &g, GUnit &u, int64_t rg, int64_t b0, int n
 template <bool DQ, int TP, int NU>
 QL_DEV void unit_compute(const GemvArgs &g, const GUnit *const (&us)[NU],
                          const unsigned char *smem, const uint32_t (&abase)[TP], uint32_t lcopy,
-                         float mu, int n, int q, int64_t slice) {
+                         int n, int q, int64_t slice) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[NU][TP];
 #pragma unroll
@@ -169,7 +218,7 @@ QL_DEV void unit_compute(const GemvArgs &g, const GUnit *const (&us)[NU],
         const uint32_t win =
             __builtin_amdgcn_alignbyte(u.qw[c + 1], u.qw[c], (uint32_t)(u.blk0 & 3));
         const int qv = (int)(int8_t)(win >> (8 * q));
-        ap = (float)qv * s2 + mu;
+        ap = (float)qv * s2 + u.mu;
       } else {
         ap = u.araw[c];
       }
@@ -193,13 +242,14 @@ QL_DEV void unit_compute(const GemvArgs &g, const GUnit *const (&us)[NU],
         acc[v][tp][i] = x;
       }
     const int64_t row0 = us[v]->row0;
-    if (q == 0 && row0 + n < g.d) {
+    if (q == 0 && row0 + n < us[v]->dlim) {
+      const int64_t col = us[v]->rbase + row0 + n;
 #pragma unroll
       for (int tp = 0; tp < TP; ++tp)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 4 * tp + i;
-          if (t < g.M) g.part[(slice * g.M + t) * g.d + row0 + n] = acc[v][tp][i];
+          if (t < g.M) g.part[(slice * g.M + t) * g.dtot + col] = acc[v][tp][i];
         }
     }
   }
@@ -208,7 +258,8 @@ QL_DEV void unit_compute(const GemvArgs &g, const GUnit *const (&us)[NU],
 // LoRA down projection H = X A^T (QLoRA glossary, forward paragraph), partial
 // sums over the 128 columns of this slice that wave w covers, on 16x16x32
 // MFMA: A operand = X rows (tokens), B operand = A rows (ranks 16 cb ..
-// 16 cb + 15); D[4q + i][n] = partial H[token 4q + i][rank 16 cb + n].
+// 16 cb + 15); D[4q + i][n] = partial H[token 4q + i][rank 16 cb + n]. One
+// X read serves every weight of the call.
 QL_DEV void lora_down_partial(const GemvArgs &g, int64_t slice, int nblk, int wave, int n,
                               int q) {
   const int64_t c0 = slice * (64 * GB) + 128 * wave;  // first column of the wave
@@ -219,21 +270,24 @@ QL_DEV void lora_down_partial(const GemvArgs &g, int64_t slice, int nblk, int wa
     const bool ok = 32 * i + 8 * q < ncol && n < g.M;
     xa[i] = ok ? *(const uint4 *)(g.X + n * g.k + c0 + 32 * i + 8 * q) : ql::zero4();
   }
-  for (int cb = 0; cb < g.rp / 16; ++cb) {
-    uint4 aa[4];
+  for (int wi = 0; wi < g.nw; ++wi) {
+    const GemvW W = wsel(g, wi);
+    for (int cb = 0; cb < g.rp / 16; ++cb) {
+      uint4 aa[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = 32 * i + 8 * q < ncol;
-      aa[i] = ok ? *(const uint4 *)(g.Ap + (int64_t)(16 * cb + n) * g.k + c0 + 32 * i + 8 * q)
-                 : ql::zero4();
-    }
-    f32x4 hacc = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = 32 * i + 8 * q < ncol;
+        aa[i] = ok ? *(const uint4 *)(W.Ap + (int64_t)(16 * cb + n) * g.k + c0 + 32 * i + 8 * q)
+                   : ql::zero4();
+      }
+      f32x4 hacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hacc = ql::mfma16(xa[i], aa[i], hacc);
+      for (int i = 0; i < 4; ++i) hacc = ql::mfma16(xa[i], aa[i], hacc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * q + i;
-      if (t < g.M) g.hpart[((slice * GW + wave) * g.M + t) * g.rp + 16 * cb + n] = hacc[i];
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * q + i;
+        if (t < g.M) W.hpart[((slice * GW + wave) * g.M + t) * g.rp + 16 * cb + n] = hacc[i];
+      }
     }
   }
 }
@@ -275,7 +329,6 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
     xv[i] = *(const uint4 *)(g.X + (ok ? m * g.k + (b0 + b) * 64 + 8 * sc8 : 0));
   }
   __builtin_amdgcn_sched_barrier(0);
-  const float mu = DQ ? g.sc.mu[0] : 0.0f;
   // 3. the wave's two units (row groups wave and wave + GW of this
   //    workgroup), loaded unconditionally (clamped) so every wait is exact
   const int64_t rga = rg_of(wave), rgb = rg_of(wave + GW);
@@ -311,35 +364,67 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
   for (int tp = 0; tp < TP; ++tp) abase[tp] = a_on ? xa_base(tp, q, n & 3) : ZBASE;
   if (has_b) {  // has_b implies has_a
     const GUnit *const both[2] = {&ua, &ub};
-    unit_compute<DQ, TP, 2>(g, both, smem, abase, lcopy, mu, n, q, slice);
+    unit_compute<DQ, TP, 2>(g, both, smem, abase, lcopy, n, q, slice);
   } else if (has_a) {
     const GUnit *const one[1] = {&ua};
-    unit_compute<DQ, TP, 1>(g, one, smem, abase, lcopy, mu, n, q, slice);
+    unit_compute<DQ, TP, 1>(g, one, smem, abase, lcopy, n, q, slice);
   }
   if (blockIdx.x == gridDim.x - 1) lora_down_partial(g, slice, nblk, wave, n, q);  // fewest units
 }
 
 // Y[m][j] = bf16(sum_s part[s][m][j] + s_l * sum_t H[m][t] B[j][t]) with
-// H[m][t] = sum_p hpart[p][m][t] (fixed orders); workgroup (x, m) builds
-// H[m] in LDS (256 / rp lane groups of rp lanes, rp <= 128), workgroups with
-// x == 0 also write H_save (M x r).
-__global__ __launch_bounds__(256) void gemv_epilogue_kernel(
-    const float *__restrict__ part, int S, int64_t M, int64_t d,
-    const uint16_t *__restrict__ Bp, const float *__restrict__ hpart, int nhp, int rp, float s,
-    uint16_t *__restrict__ Y, float *__restrict__ hsave, int r) {
+// H[m][t] = sum_p hpart[p][m][t] (fixed orders), per weight of the call;
+// workgroup (x, m) serves 256 columns of one weight and builds its H[m] in
+// LDS (256 / rp lane groups of rp lanes, rp <= 128); the first workgroup of
+// each weight also writes H_save (M x r).
+struct EpiW {
+  const uint16_t *Bp;   // d x rp
+  const float *hpart;   // [nhp][M][rp]
+  uint16_t *Y;          // M x d
+  float *hsave;         // M x r or NULL
+  int64_t d, rbase, ebase;   // rows, first partial-sum column, first workgroup
+};
+struct EpiArgs {
+  EpiW w[GMAXW];
+  int nw;
+  const float *part;    // [S][M][dtot]
+  int S;
+  int64_t M, dtot;
+  int nhp, rp, r;
+  float s;
+};
+QL_DEV EpiW esel(const EpiArgs &e, int i) {
+  EpiW W;
+  W.Bp = QL_PICK(e.w, i, Bp);
+  W.hpart = QL_PICK(e.w, i, hpart);
+  W.Y = QL_PICK(e.w, i, Y);
+  W.hsave = QL_PICK(e.w, i, hsave);
+  W.d = QL_PICK(e.w, i, d);
+  W.rbase = QL_PICK(e.w, i, rbase);
+  W.ebase = QL_PICK(e.w, i, ebase);
+  return W;
+}
+
+__global__ __launch_bounds__(256) void gemv_epilogue_kernel(EpiArgs e) {
   __shared__ float hp[16][128];  // per lane-group sums of the H partials
   __shared__ float hs[128];
   const int64_t m = blockIdx.y;
   const int tid = threadIdx.x;
+  int wi = 0;
+#pragma unroll
+  for (int j = 1; j < GMAXW; ++j) wi += (j < e.nw && (int64_t)blockIdx.x >= e.w[j].ebase) ? 1 : 0;
+  const EpiW W = esel(e, wi);
+  const int rp = e.rp;
   // the loads that do not depend on H go first (slice partials of output j
   // and the first 16 ranks of its B row), so one memory round trip covers
   // them and the H partials
-  const int64_t j = (int64_t)blockIdx.x * 256 + tid;
-  const int64_t jc = j < d ? j : d - 1;
-  const uint4 b0 = *(const uint4 *)(Bp + jc * rp), b1 = *(const uint4 *)(Bp + jc * rp + 8);
+  const int64_t xb = (int64_t)blockIdx.x - W.ebase;
+  const int64_t j = xb * 256 + tid;
+  const int64_t jc = j < W.d ? j : W.d - 1;
+  const uint4 b0 = *(const uint4 *)(W.Bp + jc * rp), b1 = *(const uint4 *)(W.Bp + jc * rp + 8);
   float acc = 0.0f;
 #pragma unroll 4
-  for (int sp = 0; sp < S; ++sp) acc += part[((int64_t)sp * M + m) * d + jc];
+  for (int sp = 0; sp < e.S; ++sp) acc += e.part[((int64_t)sp * e.M + m) * e.dtot + W.rbase + jc];
   // H[m][t]: lane group grp adds partials p = grp, grp + ng, ... of rank t
   // (ng = 256 / rp groups), then rank t adds the groups in order
   {
@@ -347,7 +432,7 @@ __global__ __launch_bounds__(256) void gemv_epilogue_kernel(
     if (grp < ng) {
       float ha = 0.0f;
 #pragma unroll 4
-      for (int p = grp; p < nhp; p += ng) ha += hpart[((int64_t)p * M + m) * rp + t];
+      for (int p = grp; p < e.nhp; p += ng) ha += W.hpart[((int64_t)p * e.M + m) * rp + t];
       hp[grp][t] = ha;
     }
     __syncthreads();
@@ -355,51 +440,72 @@ __global__ __launch_bounds__(256) void gemv_epilogue_kernel(
       float ha = 0.0f;
       for (int gi = 0; gi < ng; ++gi) ha += hp[gi][tid];
       hs[tid] = ha;
-      if (hsave && blockIdx.x == 0 && tid < r) hsave[m * r + tid] = ha;
+      if (W.hsave && xb == 0 && tid < e.r) W.hsave[m * e.r + tid] = ha;
     }
     __syncthreads();
   }
-  if (j >= d) return;
+  if (j >= W.d) return;
   const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
   float l = 0.0f;
 #pragma unroll
   for (int t = 0; t < 16; ++t)
     l = fmaf(hs[t], (t & 1) ? ql::bf16hi(bw[t >> 1]) : ql::bf16lo(bw[t >> 1]), l);
-  for (int t = 16; t < rp; ++t) l = fmaf(hs[t], ql::bf16_to_f(Bp[j * rp + t]), l);
-  Y[m * d + j] = ql::f_to_bf16(acc + s * l);
+  for (int t = 16; t < rp; ++t) l = fmaf(hs[t], ql::bf16_to_f(W.Bp[j * rp + t]), l);
+  W.Y[m * W.d + j] = ql::f_to_bf16(acc + e.s * l);
 }
 
 }  // namespace
 
 static int64_t gemv_splits(int64_t k) { return ql_cdiv(k >> 6, GB); }
 
-size_t gemv_part_bytes(int64_t d, int64_t k, int64_t M, int rp) {
-  return (size_t)(gemv_splits(k) * M * d * 4 + gemv_splits(k) * GW * M * rp * 4);
+size_t gemv_part_bytes(int64_t dtot, int64_t k, int64_t M, int rp, int nw) {
+  return (size_t)(gemv_splits(k) * M * dtot * 4 + nw * gemv_splits(k) * GW * M * rp * 4);
 }
 
-qlora_status launch_gemv_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, int64_t k,
-                             const uint16_t *X, int64_t M, const uint16_t *Ap,
-                             const uint16_t *Bp, int r, int rp, float s, float *part,
-                             float *H_save, uint16_t *Y, hipStream_t st) {
+qlora_status launch_gemv_fwd(int nw, const GemvIn *in, int64_t k, const uint16_t *X, int64_t M,
+                             int r, int rp, float s, float *part, hipStream_t st) {
   if (M < 1 || M > 16 || rp < 16 || rp > 128 || rp % 16) return QLORA_ERR_INVALID_ARG;
-  static int ncu = 0;
-  if (ncu == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        ncu < 1)
-      ncu = 256;
-  }
+  if (nw < 1 || nw > GMAXW) return QLORA_ERR_INVALID_ARG;
+  for (int i = 1; i < nw; ++i)
+    if (in[i].sc.dq != in[0].sc.dq) return QLORA_ERR_INVALID_ARG;
+  const int ncu = ql_num_cus();
   const int64_t S = gemv_splits(k);
-  const int64_t ngroups = ql_cdiv(d, 16);
+  int64_t dtot = 0, ngroups = 0, eblocks = 0;
+  GemvArgs g{};
+  EpiArgs e{};
+  for (int i = 0; i < nw; ++i) {
+    const int64_t d = in[i].d;
+    g.w[i] = GemvW{in[i].codes, in[i].sc, d, d * (k >> 6), ngroups, dtot, in[i].Ap, nullptr};
+    e.w[i] = EpiW{in[i].Bp, nullptr, in[i].Y, in[i].H_save, d, dtot, eblocks};
+    ngroups += ql_cdiv(d, 16);
+    eblocks += ql_cdiv(d, 256);
+    dtot += d;
+  }
+  for (int i = 0; i < nw; ++i) {
+    float *hpart = part + S * M * dtot + (int64_t)i * S * GW * M * rp;
+    g.w[i].hpart = hpart;
+    e.w[i].hpart = hpart;
+  }
+  for (int i = nw; i < GMAXW; ++i) {  // unused slots: never selected
+    g.w[i] = g.w[0];
+    e.w[i] = e.w[0];
+  }
   // about one workgroup per compute unit, each slice served by G of them,
   // and at most two row groups per wave
   const int64_t G = std::min<int64_t>(
       ngroups, std::max<int64_t>(std::max<int64_t>(1, ncu / S), ql_cdiv(ngroups, 2 * GW)));
   const int64_t rpw = ql_cdiv(ngroups, G);
-  if (S > 65535 || G > (int64_t(1) << 30)) return QLORA_ERR_UNSUPPORTED;
-  float *hpart = part + S * M * d;
-  GemvArgs g{codes, sc, d, k, X, M, d * (k >> 6), ngroups, (int)G, (int)rpw, part, Ap, rp, hpart};
+  if (S > 65535 || G > (int64_t(1) << 30) || eblocks > 0x7fffffff) return QLORA_ERR_UNSUPPORTED;
+  g.nw = nw;
+  g.k = k;
+  g.X = X;
+  g.M = M;
+  g.ngroups = ngroups;
+  g.G = (int)G;
+  g.rpw = (int)rpw;
+  g.part = part;
+  g.dtot = dtot;
+  g.rp = rp;
   dim3 grid((unsigned)G, (unsigned)S);
   {
     QlProf prof(QLORA_K_GEMV, st);
@@ -412,7 +518,7 @@ qlora_status launch_gemv_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, i
   else                                                                  \
     nf4_gemv_kernel<DQV, TPV, false><<<grid, GT, 0, st>>>(g);
 #define QL_GEMV(TPV)                                                    \
-  if (sc.dq) {                                                          \
+  if (in[0].sc.dq) {                                                    \
     QL_GEMV3(true, TPV)                                                 \
   } else {                                                              \
     QL_GEMV3(false, TPV)                                                \
@@ -422,10 +528,18 @@ qlora_status launch_gemv_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, i
 #undef QL_GEMV3
   }
   {
+    e.nw = nw;
+    e.part = part;
+    e.S = (int)S;
+    e.M = M;
+    e.dtot = dtot;
+    e.nhp = (int)(S * GW);
+    e.rp = rp;
+    e.r = r;
+    e.s = s;
     QlProf prof(QLORA_K_GEMV_EPILOGUE, st);
-    dim3 eg((unsigned)ql_cdiv(d, 256), (unsigned)M);
-    gemv_epilogue_kernel<<<eg, 256, 0, st>>>(part, (int)S, M, d, Bp, hpart, (int)(S * GW), rp, s,
-                                             Y, H_save, r);
+    dim3 eg((unsigned)eblocks, (unsigned)M);
+    gemv_epilogue_kernel<<<eg, 256, 0, st>>>(e);
   }
   QL_LAUNCH_CHECK();
   return QLORA_OK;

@@ -62,13 +62,22 @@ qlora_status launch_gemm_dx(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
                             hipStream_t st);
 
 // gemv.hip : memory-bound forward for M <= 16, including the LoRA down
-// projection (Ap, Bp zero-padded to rp ranks; H_save may be NULL)
-qlora_status launch_gemv_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
-                             int64_t k, const uint16_t *X, int64_t M,
-                             const uint16_t *Ap, const uint16_t *Bp, int r, int rp,
-                             float s, float *part, float *H_save, uint16_t *Y,
-                             hipStream_t st);
-size_t gemv_part_bytes(int64_t d, int64_t k, int64_t M, int rp);
+// projection, for nw (1..4) weights that read the same X (sibling
+// projections) in one launch plus one epilogue launch. Per weight: codes and
+// scales, d, Ap (rp x k) and Bp (d x rp) zero-padded to rp ranks, H_save
+// (M x r, may be NULL) and Y (M x d). All weights share k and the
+// double-quantisation mode.
+struct GemvIn {
+  const uint8_t *codes;
+  ql::ScaleSrc sc;
+  int64_t d;
+  const uint16_t *Ap, *Bp;
+  float *H_save;
+  uint16_t *Y;
+};
+qlora_status launch_gemv_fwd(int nw, const GemvIn *in, int64_t k, const uint16_t *X, int64_t M,
+                             int r, int rp, float s, float *part, hipStream_t st);
+size_t gemv_part_bytes(int64_t dtot, int64_t k, int64_t M, int rp, int nw);
 
 // merge.hip
 qlora_status launch_merge(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
@@ -81,6 +90,10 @@ struct AdamScalars {
 };
 qlora_status launch_adamw(float *p, float *m, float *v, const uint16_t *g, uint16_t *out,
                           int64_t n, const AdamScalars &s, hipStream_t st);
+
+// compute units of the current device (capi.hip; queried once, 256 if the
+// query fails)
+int ql_num_cus();
 
 // tables (quantize.hip)
 void host_codebook(float levels[16], float thresholds[15]);

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
 
 QLORA_OK, QLORA_ERR_INVALID_ARG, QLORA_ERR_UNSUPPORTED, QLORA_ERR_WORKSPACE, QLORA_ERR_HIP = (
     0, -1, -2, -3, -4)
-OP_QUANTIZE, OP_FWD, OP_BWD = 0, 1, 2
+OP_QUANTIZE, OP_FWD, OP_BWD, OP_FWD_MULTI = 0, 1, 2, 3
 
 
 class QLoRAError(RuntimeError):
@@ -55,6 +55,8 @@ SIGNATURES = {
                                         _vp, _sz, _vp]),
     "qlora_linear_bwd": (ctypes.c_int, [_PW, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp,
                                         _vp, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_linear_fwd_multi": (ctypes.c_int, [_vp, _i32, _vp, _i64, _vp, _vp, _i32, _f32, _vp,
+                                              _vp, _vp, _sz, _vp]),
     "qlora_merge": (ctypes.c_int, [_PW, _vp, _vp, _i32, _f32, _vp, _vp]),
     "qlora_nf4_storage_bytes": (_sz, [_i64, _i64, _i32]),
     "qlora_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64, _i32, _i32]),
@@ -218,6 +220,38 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                                   _ptr(H) if save_h else None, _ptr(wst), wsn,
                                   _stream(stream)), "qlora_linear_fwd")
     return Y, (H if save_h else None)
+
+
+def linear_fwd_multi(ws_: list, X: torch.Tensor, As: list, Bs: list, lora_alpha: float,
+                     save_h: bool = True, Ys: list | None = None, ws: torch.Tensor | None = None,
+                     stream=None):
+    """Sibling projections: Y_i = X W_i'^T + (alpha/r) (X A_i^T) B_i^T for up
+    to four weights reading the same X, in one call. Returns (Ys, Hs)."""
+    nw = len(ws_)
+    if not (1 <= nw <= 4) or len(As) != nw or len(Bs) != nw:
+        raise ValueError("one to four weights, each with its A and B")
+    _dev_bf16(X, "X")
+    for i in range(nw):
+        _dev_bf16(As[i], f"A[{i}]")
+        _dev_bf16(Bs[i], f"B[{i}]")
+    M, r = X.shape[0], As[0].shape[0]
+    if Ys is None:
+        Ys = [torch.empty(M, w.d, dtype=torch.bfloat16, device=X.device) for w in ws_]
+    Hs = ([torch.empty(M, r, dtype=torch.float32, device=X.device) for _ in range(nw)]
+          if save_h else None)
+    dtot = sum(w.d for w in ws_)
+    wsb = workspace_bytes(OP_FWD_MULTI, dtot, ws_[0].k, M, r, ws_[0].double_quant)
+    wst, wsn = _workspace(wsb, X.device, ws)
+    cws = [w.c_struct() for w in ws_]
+    wp = (ctypes.c_void_p * nw)(*[ctypes.addressof(c) for c in cws])
+    ap = (ctypes.c_void_p * nw)(*[a.data_ptr() for a in As])
+    bp = (ctypes.c_void_p * nw)(*[b.data_ptr() for b in Bs])
+    yp = (ctypes.c_void_p * nw)(*[y.data_ptr() for y in Ys])
+    hp = (ctypes.c_void_p * nw)(*[h.data_ptr() for h in Hs]) if save_h else None
+    _check(lib().qlora_linear_fwd_multi(wp, nw, X.data_ptr(), M, ap, bp, r, float(lora_alpha), yp,
+                                        hp, _ptr(wst), wsn, _stream(stream)),
+           "qlora_linear_fwd_multi")
+    return Ys, Hs
 
 
 def linear_bwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,

@@ -77,8 +77,9 @@ typedef struct qlora_nf4_weight {
   float *absmax_offset;
 } qlora_nf4_weight;
 
-/* Operation ids for qlora_workspace_bytes. */
-enum { QLORA_OP_QUANTIZE = 0, QLORA_OP_FWD = 1, QLORA_OP_BWD = 2 };
+/* Operation ids for qlora_workspace_bytes. For QLORA_OP_FWD_MULTI pass the
+ * sum of the weights' d as `d`. */
+enum { QLORA_OP_QUANTIZE = 0, QLORA_OP_FWD = 1, QLORA_OP_BWD = 2, QLORA_OP_FWD_MULTI = 3 };
 
 /*
  * Quantise a bf16 weight W0 (d x k) into `w` (all of w's pointers are
@@ -121,6 +122,28 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X,
                               int32_t r, float lora_alpha, uint16_t *Y,
                               float *H_save, void *ws, size_t ws_bytes,
                               void *stream);
+
+/*
+ * Sibling projections: the forward above for nw (1..4) weights that read the
+ * same activations X -- q, k, v of an attention block, or gate and up of the
+ * MLP (LLM tutorial ch. 3, 3.3 and Day-25 notes 4.3: the adapters target
+ * every such linear; QLoRA glossary, "QLoRA 的工作原理": adapters on every
+ * linear layer of the block). Weight i has its own d_i, A[i] (r x k),
+ * B[i] (d_i x r) and output Y[i] (M x d_i); H_save may be NULL or hold a
+ * NULL / an M x r float32 buffer per weight. All weights share k, r,
+ * lora_alpha and the double-quantisation mode. For M <= 16 the weights run
+ * as one GEMV launch (row groups of all weights in one grid; X and the LoRA
+ * down projections read once) plus one epilogue launch; for larger M each
+ * weight runs the two-launch GEMM path. Results are bit-identical to nw
+ * separate qlora_linear_fwd calls.
+ * Workspace: qlora_workspace_bytes(QLORA_OP_FWD_MULTI, sum of d_i, k, M, r, dq).
+ */
+qlora_status qlora_linear_fwd_multi(const qlora_nf4_weight *const *w, int32_t nw,
+                                    const uint16_t *X, int64_t M,
+                                    const uint16_t *const *A, const uint16_t *const *B,
+                                    int32_t r, float lora_alpha, uint16_t *const *Y,
+                                    float *const *H_save, void *ws, size_t ws_bytes,
+                                    void *stream);
 
 /*
  * Backward of the forward above for upstream gradient dY (M x d, bf16)

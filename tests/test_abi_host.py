@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     ops = _ops()
     L = ops.lib()
     names = _declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for name in names:
         assert hasattr(L, name), name
         assert name in ops.SIGNATURES, name
