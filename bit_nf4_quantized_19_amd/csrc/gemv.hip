@@ -132,11 +132,12 @@ struct GUnit {
   int64_t rbase;    // its weight's first column in the partial-sum rows
 };
 
-template <bool DQ, bool FULL>
+template <bool DQ, bool FULL, bool GRP>
 QL_DEV void unit_load(const GemvArgs &g, GUnit &u, int64_t rg, int64_t b0, int nblk, int n,
                       int q) {
   const int64_t nbr = g.k >> 6;
-  const GemvW W = wsel(g, weight_of(g, rg));   // rg is wave-uniform
+  // grouped calls pick the unit's weight (rg is wave-uniform)
+  const GemvW W = GRP ? wsel(g, weight_of(g, rg)) : g.w[0];
   u.row0 = (rg - W.gbase) * 16;
   u.dlim = W.d;
   u.rbase = W.rbase;
@@ -260,6 +261,7 @@ QL_DEV void unit_compute(const GemvArgs &g, const GUnit *const (&us)[NU],
 // MFMA: A operand = X rows (tokens), B operand = A rows (ranks 16 cb ..
 // 16 cb + 15); D[4q + i][n] = partial H[token 4q + i][rank 16 cb + n]. One
 // X read serves every weight of the call.
+template <bool GRP>
 QL_DEV void lora_down_partial(const GemvArgs &g, int64_t slice, int nblk, int wave, int n,
                               int q) {
   const int64_t c0 = slice * (64 * GB) + 128 * wave;  // first column of the wave
@@ -270,8 +272,8 @@ QL_DEV void lora_down_partial(const GemvArgs &g, int64_t slice, int nblk, int wa
     const bool ok = 32 * i + 8 * q < ncol && n < g.M;
     xa[i] = ok ? *(const uint4 *)(g.X + n * g.k + c0 + 32 * i + 8 * q) : ql::zero4();
   }
-  for (int wi = 0; wi < g.nw; ++wi) {
-    const GemvW W = wsel(g, wi);
+  for (int wi = 0; wi < (GRP ? g.nw : 1); ++wi) {
+    const GemvW W = GRP ? wsel(g, wi) : g.w[0];
     for (int cb = 0; cb < g.rp / 16; ++cb) {
       uint4 aa[4];
 #pragma unroll
@@ -296,7 +298,7 @@ QL_DEV void lora_down_partial(const GemvArgs &g, int64_t slice, int nblk, int wa
 // of them) of one slice; wave w takes the workgroup's row groups w and
 // w + GW, both loaded before the table is built, then computed together. The
 // table and the X slice are built once per workgroup.
-template <bool DQ, int TP, bool FULL>
+template <bool DQ, int TP, bool FULL, bool GRP>
 __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
   __shared__ __align__(16) unsigned char smem[LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -335,8 +337,8 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
   const bool has_a = wave < g.rpw && rga < g.ngroups;
   const bool has_b = wave + GW < g.rpw && rgb < g.ngroups;
   GUnit ua, ub;
-  unit_load<DQ, FULL>(g, ua, min(rga, g.ngroups - 1), b0, nblk, n, q);
-  unit_load<DQ, FULL>(g, ub, min(rgb, g.ngroups - 1), b0, nblk, n, q);
+  unit_load<DQ, FULL, GRP>(g, ua, min(rga, g.ngroups - 1), b0, nblk, n, q);
+  unit_load<DQ, FULL, GRP>(g, ub, min(rgb, g.ngroups - 1), b0, nblk, n, q);
   // 4. table (bf16 pair, even element in the low half), 32 copies per entry;
   //    X chunks; zero region
   {
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
     const GUnit *const one[1] = {&ua};
     unit_compute<DQ, TP, 1>(g, one, smem, abase, lcopy, n, q, slice);
   }
-  if (blockIdx.x == gridDim.x - 1) lora_down_partial(g, slice, nblk, wave, n, q);  // fewest units
+  if (blockIdx.x == gridDim.x - 1) lora_down_partial<GRP>(g, slice, nblk, wave, n, q);  // fewest units
 }
 
 // Y[m][j] = bf16(sum_s part[s][m][j] + s_l * sum_t H[m][t] B[j][t]) with
@@ -512,11 +514,17 @@ qlora_status launch_gemv_fwd(int nw, const GemvIn *in, int64_t k, const uint16_t
     const int tp = (int)ql_cdiv(M, 4);
     // every slice is full when k is a multiple of 1024
     const bool full = (k % (64 * GB)) == 0;
-#define QL_GEMV3(DQV, TPV)                                              \
-  if (full)                                                             \
-    nf4_gemv_kernel<DQV, TPV, true><<<grid, GT, 0, st>>>(g);            \
+#define QL_GEMV4(DQV, TPV, FV)                                          \
+  if (nw > 1)                                                           \
+    nf4_gemv_kernel<DQV, TPV, FV, true><<<grid, GT, 0, st>>>(g);        \
   else                                                                  \
-    nf4_gemv_kernel<DQV, TPV, false><<<grid, GT, 0, st>>>(g);
+    nf4_gemv_kernel<DQV, TPV, FV, false><<<grid, GT, 0, st>>>(g);
+#define QL_GEMV3(DQV, TPV)                                              \
+  if (full) {                                                           \
+    QL_GEMV4(DQV, TPV, true)                                            \
+  } else {                                                              \
+    QL_GEMV4(DQV, TPV, false)                                           \
+  }
 #define QL_GEMV(TPV)                                                    \
   if (in[0].sc.dq) {                                                    \
     QL_GEMV3(true, TPV)                                                 \
@@ -526,6 +534,7 @@ qlora_status launch_gemv_fwd(int nw, const GemvIn *in, int64_t k, const uint16_t
     if (tp == 1) { QL_GEMV(1) } else if (tp == 2) { QL_GEMV(2) } else if (tp == 3) { QL_GEMV(3) } else { QL_GEMV(4) }
 #undef QL_GEMV
 #undef QL_GEMV3
+#undef QL_GEMV4
   }
   {
     e.nw = nw;
