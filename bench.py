@@ -348,6 +348,28 @@ def measure_rows(ops, synth, torch, dev):
                     pbytes, ms_pair, _kernel_us(ops, "gemv", fp, nset // 2, 48))
         del gq
         torch.cuda.empty_cache()
+    # sibling projections on the GEMM path: q, k, v (3 x 4096x4096) of one
+    # block reading the same 2048 tokens, one multi call against three calls
+    Xq = synth.normal_bf16_device((M, K), 1.0, 61, device=dev)
+    wq = [ops.quantize(synth.normal_bf16_device((D, K), 0.02, 62 + i, device=dev), True)
+          for i in range(3)]
+    Aq = [synth.normal_bf16_device((R, K), 0.01, 65 + i, device=dev) for i in range(3)]
+    Bq = [synth.normal_bf16_device((D, R), 0.01, 68 + i, device=dev) for i in range(3)]
+    Yq = [torch.empty(M, D, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    wsq3 = torch.empty(ops.workspace_bytes(ops.OP_FWD_MULTI, 3 * D, K, M, R, True) + 256,
+                       dtype=torch.uint8, device=dev)
+    wsq3 = wsq3[(-wsq3.data_ptr()) % 256:]
+    fq3 = lambda i: ops.linear_fwd_multi(wq, Xq, Aq, Bq, ALPHA, save_h=False, Ys=Yq, ws=wsq3)
+    f3 = lambda i: [ops.linear_fwd(wq[j], Xq, Aq[j], Bq[j], ALPHA, save_h=False, Y=Yq[j])
+                    for j in range(3)]
+    ms_multi, ms_three = _call_ms(fq3, 1, 20), _call_ms(f3, 1, 20)
+    qflops = 3 * (2 * M * D * K + 4 * M * R * D)
+    out["qkv_fwd_multi"] = {"shape": [3, D, K], "tokens": M, "r": R,
+                            "multi_call_us": round(1e3 * ms_multi, 2),
+                            "three_calls_us": round(1e3 * ms_three, 2),
+                            "multi_TFLOP_s": round(qflops / (ms_multi * 1e-3) / 1e12, 1)}
+    del wq, Xq, Yq
+    torch.cuda.empty_cache()
     # paged 32-bit AdamW step over the LoRA parameters of a Llama-7B-shaped
     # all-linear adapter set (32 layers x q,k,v,o 4096^2, gate/up 4096->11008,
     # down 11008->4096; r = 16: 39,976,960 parameters) as one flat buffer,

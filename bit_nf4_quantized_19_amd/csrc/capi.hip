@@ -235,16 +235,20 @@ static qlora_status linear_fwd_group(const qlora_nf4_weight *const *w, int nw, c
     }
     return launch_gemv_fwd(nw, in, k, X, M, r, rp, sc, L.gpart, st);
   }
-  for (int i = 0; i < nw; ++i) {
-    // H = X A^T (float32, M x rp) and s*H as bf16 hi/lo; H_save gets the M x r copy
-    if ((s = launch_skinny(X, M, k, A[i], false, r, rp, L.H[i], H_save ? H_save[i] : nullptr, r,
-                           sc, L.Hs_hi[i], L.Hs_lo[i], st)) != QLORA_OK)
-      return s;
-    if ((s = launch_gemm_fwd(w[i]->codes, scale_src(w[i]), d[i], k, X, M, B[i], r, L.Hs_hi[i],
-                             L.Hs_lo[i], rp, Y[i], st)) != QLORA_OK)
-      return s;
-  }
-  return QLORA_OK;
+  // H_i = X A_i^T (float32, M x rp) and s*H_i as bf16 hi/lo for every weight
+  // in one launch; H_save gets the M x r copies
+  SkinnyOut so[kMaxGroup];
+  for (int i = 0; i < nw; ++i)
+    so[i] = SkinnyOut{A[i], L.H[i], H_save ? H_save[i] : nullptr, L.Hs_hi[i], L.Hs_lo[i]};
+  if ((s = launch_skinny(X, M, k, nw, so, false, r, rp, r, sc, st)) != QLORA_OK) return s;
+  if (nw == 1)
+    return launch_gemm_fwd(w[0]->codes, scale_src(w[0]), d[0], k, X, M, B[0], r, L.Hs_hi[0],
+                           L.Hs_lo[0], rp, Y[0], st);
+  // the weights' column tiles in one GEMM launch
+  GemmFwdIn gi[kMaxGroup];
+  for (int i = 0; i < nw; ++i)
+    gi[i] = GemmFwdIn{w[i]->codes, scale_src(w[i]), d[i], B[i], L.Hs_hi[i], L.Hs_lo[i], Y[i]};
+  return launch_gemm_fwd_group(nw, gi, k, X, M, r, rp, st);
 }
 
 qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,

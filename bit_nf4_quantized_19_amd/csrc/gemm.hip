@@ -147,7 +147,8 @@ struct Tile {
 
   f32x16 acc[2][2];
 
-  QL_DEV void init(const GemmArgs &ga) {
+  // tile (tm, tn): token rows tm*BM.., output columns tn*BN..
+  QL_DEV void init(const GemmArgs &ga, int64_t tm, int64_t tn) {
     g = ga;
     tid = threadIdx.x;
     lane = tid & 63;
@@ -156,11 +157,6 @@ struct Tile {
     h = lane >> 5;
     wn = wave & 1;
     wm = wave >> 1;
-    const int64_t ntn = ql_cdiv(g.Ntot, BN), ntm = ql_cdiv(g.M, BM);
-    const int64_t total = ntn * ntm;
-    int64_t tile = blockIdx.x;
-    if ((total & 7) == 0) tile = (int64_t)(blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-    const int64_t tm = tile / ntn, tn = tile % ntn;
     m0 = tm * BM;
     n0 = tn * BN;
     nk = ql_cdiv(g.Ktot, BK);
@@ -498,11 +494,67 @@ struct Tile {
   }
 };
 
+// Workgroup -> tile, XCD-aware: with 8 XCDs taking workgroups round-robin,
+// consecutive tiles (the column tiles of one token block) land on one XCD,
+// whose L2 then holds that token block.
+QL_DEV void tile_of(int64_t ntn, int64_t ntm, int64_t &tm, int64_t &tn) {
+  const int64_t total = ntn * ntm;
+  int64_t tile = blockIdx.x;
+  if ((total & 7) == 0) tile = (int64_t)(blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  tm = tile / ntn;
+  tn = tile % ntn;
+}
+
 template <int MODE, bool DQ>
 __global__ __launch_bounds__(NT, 1) void nf4_gemm_kernel(GemmArgs g) {
   if (threadIdx.x < 16) s_lv[threadIdx.x] = __uint_as_float(c_levels_g[threadIdx.x]);
+  int64_t tm, tn;
+  tile_of(ql_cdiv(g.Ntot, BN), ql_cdiv(g.M, BM), tm, tn);
   Tile<MODE, DQ> t;
-  t.init(g);
+  t.init(g, tm, tn);
+  __syncthreads();  // level table
+  t.run();
+  t.epilogue();
+}
+
+// Forward of up to four weights that read the same X (sibling projections):
+// their column tiles are numbered one after another, so a single launch
+// covers them all; each workgroup picks its weight's fields by uniform
+// selects (an indexed read of the argument block would go through scratch).
+struct GemmGroupArgs {
+  GemmArgs w[4];      // per weight; In, M, k, Ktot, r, rp equal
+  int64_t nbase[4];   // first column tile of each weight
+  int64_t ntn;        // column tiles, all weights
+  int nw;
+};
+template <class T>
+QL_DEV T gpick(int i, T a0, T a1, T a2, T a3) {
+  return i == 0 ? a0 : i == 1 ? a1 : i == 2 ? a2 : a3;
+}
+#define QL_GPICK(f) gpick(wi, ga.w[0].f, ga.w[1].f, ga.w[2].f, ga.w[3].f)
+
+template <bool DQ>
+__global__ __launch_bounds__(NT, 1) void nf4_gemm_group_kernel(GemmGroupArgs ga) {
+  if (threadIdx.x < 16) s_lv[threadIdx.x] = __uint_as_float(c_levels_g[threadIdx.x]);
+  int64_t tm, tng;
+  tile_of(ga.ntn, ql_cdiv(ga.w[0].M, BM), tm, tng);
+  int wi = 0;
+#pragma unroll
+  for (int j = 1; j < 4; ++j) wi += (j < ga.nw && tng >= ga.nbase[j]) ? 1 : 0;
+  GemmArgs g = ga.w[0];
+  g.codes = QL_GPICK(codes);
+  g.sc.absmax = QL_GPICK(sc.absmax);
+  g.sc.q = QL_GPICK(sc.q);
+  g.sc.s2 = QL_GPICK(sc.s2);
+  g.sc.mu = QL_GPICK(sc.mu);
+  g.d = QL_GPICK(d);
+  g.Ntot = QL_GPICK(Ntot);
+  g.L = QL_GPICK(L);
+  g.Shi = QL_GPICK(Shi);
+  g.Slo = QL_GPICK(Slo);
+  g.Out = QL_GPICK(Out);
+  Tile<0, DQ> t;
+  t.init(g, tm, tng - gpick(wi, ga.nbase[0], ga.nbase[1], ga.nbase[2], ga.nbase[3]));
   __syncthreads();  // level table
   t.run();
   t.epilogue();
@@ -535,6 +587,31 @@ qlora_status launch_gemm_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, i
                              uint16_t *Y, hipStream_t st) {
   GemmArgs g{codes, sc, d, k, X, M, d, k, B, Hs_hi, Hs_lo, r, rp, Y};
   return launch_gemm(0, g, st);
+}
+
+qlora_status launch_gemm_fwd_group(int nw, const GemmFwdIn *in, int64_t k, const uint16_t *X,
+                                   int64_t M, int r, int rp, hipStream_t st) {
+  if (nw < 1 || nw > 4) return QLORA_ERR_INVALID_ARG;
+  GemmGroupArgs ga{};
+  int64_t ntn = 0;
+  for (int i = 0; i < 4; ++i) {
+    const GemmFwdIn &x = in[i < nw ? i : 0];   // unused slots: never selected
+    ga.w[i] = GemmArgs{x.codes, x.sc, x.d, k, X, M, x.d, k, x.B, x.Hs_hi, x.Hs_lo, r, rp, x.Y};
+    if (i < nw && x.sc.dq != in[0].sc.dq) return QLORA_ERR_INVALID_ARG;
+    ga.nbase[i] = ntn;
+    if (i < nw) ntn += ql_cdiv(x.d, BN);
+  }
+  ga.ntn = ntn;
+  ga.nw = nw;
+  const int64_t tiles = ntn * ql_cdiv(M, BM);
+  if (tiles > 0x7fffffff) return QLORA_ERR_UNSUPPORTED;
+  QlProf prof(QLORA_K_GEMM_FWD, st);
+  if (in[0].sc.dq)
+    nf4_gemm_group_kernel<true><<<(unsigned)tiles, NT, 0, st>>>(ga);
+  else
+    nf4_gemm_group_kernel<false><<<(unsigned)tiles, NT, 0, st>>>(ga);
+  QL_LAUNCH_CHECK();
+  return QLORA_OK;
 }
 
 qlora_status launch_gemm_dx(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, int64_t k,

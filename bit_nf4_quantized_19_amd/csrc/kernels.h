@@ -34,6 +34,15 @@ qlora_status launch_layout(const LayoutReq *req, int nreq, hipStream_t st);
 qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, const uint16_t *P,
                            bool p_col, int r, int rp, float *out, float *out2, int out2_ld,
                            float s, uint16_t *hi, uint16_t *lo, hipStream_t st);
+// The same for nw (1..4) contractions of one In (sibling projections) in one
+// launch: o[i] = {P, out, out2, hi, lo} of contraction i.
+struct SkinnyOut {
+  const uint16_t *P;
+  float *out, *out2;
+  uint16_t *hi, *lo;
+};
+qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, int nw, const SkinnyOut *o,
+                           bool p_col, int r, int rp, int out2_ld, float s, hipStream_t st);
 // Two problems out = s * sum_m In[m][c] * Q[m][t] rounded to bf16 (In M x C,
 // Q M x rp fp32) in one launch plus one reduction launch.
 // transpose_out == 0: out is C x r (ld r); == 1: out is r x C (ld C).
@@ -55,6 +64,16 @@ qlora_status launch_gemm_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
                              const uint16_t *B, int r, const uint16_t *Hs_hi,
                              const uint16_t *Hs_lo, int rp, uint16_t *Y,
                              hipStream_t st);
+// The forward for nw (1..4) weights that read the same X in one launch.
+struct GemmFwdIn {
+  const uint8_t *codes;
+  ql::ScaleSrc sc;
+  int64_t d;
+  const uint16_t *B, *Hs_hi, *Hs_lo;
+  uint16_t *Y;
+};
+qlora_status launch_gemm_fwd_group(int nw, const GemmFwdIn *in, int64_t k, const uint16_t *X,
+                                   int64_t M, int r, int rp, hipStream_t st);
 qlora_status launch_gemm_dx(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
                             int64_t k, const uint16_t *dY, int64_t M,
                             const uint16_t *A, int r, const uint16_t *Gs_hi,

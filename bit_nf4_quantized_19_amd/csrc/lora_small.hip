@@ -75,18 +75,45 @@ constexpr int SK_UNROLL = 8;   // K-slices of 32 whose loads are issued together
 // is transposed through the wave's own LDS slot. The 16 waves' sums are
 // added in LDS in a fixed order and written as out (M x rp), out2 (M x r,
 // optional) and s*out as bf16 hi + lo parts (optional).
+// Up to four contractions of the same In (sibling projections): grid row y
+// = weight * (rp / 16) + t-block.
+struct SkW {
+  const uint16_t *P;
+  float *out, *out2;
+  uint16_t *hi, *lo;
+};
+struct SkinnyArgs {
+  SkW w[4];
+  const uint16_t *In;
+  int64_t M, C, cpw;
+  int r, rp, tbw, out2_ld;
+  float s;
+};
+template <class T>
+QL_DEV T pick4s(int i, T a0, T a1, T a2, T a3) {
+  return i == 0 ? a0 : i == 1 ? a1 : i == 2 ? a2 : a3;
+}
+#define QL_SKPICK(f) pick4s(wi, a.w[0].f, a.w[1].f, a.w[2].f, a.w[3].f)
+
 template <bool PCOL>
-__global__ __launch_bounds__(64 * SK_W) void skinny_kernel(
-    const uint16_t *__restrict__ In, int64_t M, int64_t C, const uint16_t *__restrict__ Pm, int r,
-    int rp, int64_t cpw, float *__restrict__ out, float *__restrict__ out2, int out2_ld, float s,
-    uint16_t *__restrict__ hi, uint16_t *__restrict__ lo) {
+__global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
+  const int wi = (int)blockIdx.y / a.tbw;   // uniform: fields picked by selects
+  const uint16_t *__restrict__ In = a.In;
+  const uint16_t *__restrict__ Pm = QL_SKPICK(P);
+  float *__restrict__ out = QL_SKPICK(out);
+  float *__restrict__ out2 = QL_SKPICK(out2);
+  uint16_t *__restrict__ hi = QL_SKPICK(hi);
+  uint16_t *__restrict__ lo = QL_SKPICK(lo);
+  const int64_t M = a.M, C = a.C, cpw = a.cpw;
+  const int r = a.r, rp = a.rp, out2_ld = a.out2_ld;
+  const float s = a.s;
   constexpr int PQ = 272;   // bytes per lane group in the transposition slot (256 + pad)
   __shared__ f32x4 red[SK_W][64];
   __shared__ __align__(16) unsigned char pst[PCOL ? SK_W : 1][4 * PQ];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
   const int64_t mb = blockIdx.x;
-  const int t0 = 16 * (int)blockIdx.y;
+  const int t0 = 16 * ((int)blockIdx.y % a.tbw);
   const int64_t m = mb * 16 + r16;
   const bool m_ok = m < M;
   const uint16_t *inr = In + (m_ok ? m : 0) * C + 8 * kq;
@@ -344,23 +371,41 @@ qlora_status launch_layout(const LayoutReq *req, int nreq, hipStream_t st) {
   return QLORA_OK;
 }
 
+qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, int nw, const SkinnyOut *o,
+                           bool p_col, int r, int rp, int out2_ld, float s, hipStream_t st) {
+  if (nw < 1 || nw > 4) return QLORA_ERR_INVALID_ARG;
+  if (p_col && (r % 16 != 0 || r != rp)) return QLORA_ERR_UNSUPPORTED;
+  SkinnyArgs a{};
+  for (int i = 0; i < 4; ++i) {
+    const SkinnyOut &x = o[i < nw ? i : 0];   // unused slots: never selected
+    a.w[i] = SkW{x.P, x.out, x.out2, x.hi, x.lo};
+  }
+  a.In = In;
+  a.M = M;
+  a.C = C;
+  a.cpw = ql_rup(ql_cdiv(C, SK_W), 32);
+  a.r = r;
+  a.rp = rp;
+  a.tbw = rp / 16;
+  a.out2_ld = out2_ld;
+  a.s = s;
+  const int64_t mbs = ql_cdiv(M, 16);
+  if (mbs > 0x7fffffff || (int64_t)nw * a.tbw > 65535) return QLORA_ERR_UNSUPPORTED;
+  dim3 grid((unsigned)mbs, (unsigned)(nw * a.tbw));
+  QlProf prof(QLORA_K_LORA_DOWN, st);
+  if (p_col)
+    skinny_kernel<true><<<grid, 64 * SK_W, 0, st>>>(a);
+  else
+    skinny_kernel<false><<<grid, 64 * SK_W, 0, st>>>(a);
+  QL_LAUNCH_CHECK();
+  return QLORA_OK;
+}
+
 qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, const uint16_t *P,
                            bool p_col, int r, int rp, float *out, float *out2, int out2_ld,
                            float s, uint16_t *hi, uint16_t *lo, hipStream_t st) {
-  if (p_col && (r % 16 != 0 || r != rp)) return QLORA_ERR_UNSUPPORTED;
-  const int64_t cpw = ql_rup(ql_cdiv(C, SK_W), 32);
-  const int64_t mbs = ql_cdiv(M, 16);
-  if (mbs > 0x7fffffff || rp / 16 > 65535) return QLORA_ERR_UNSUPPORTED;
-  dim3 grid((unsigned)mbs, (unsigned)(rp / 16));
-  QlProf prof(QLORA_K_LORA_DOWN, st);
-  if (p_col)
-    skinny_kernel<true><<<grid, 64 * SK_W, 0, st>>>(In, M, C, P, r, rp, cpw, out, out2, out2_ld,
-                                                    s, hi, lo);
-  else
-    skinny_kernel<false><<<grid, 64 * SK_W, 0, st>>>(In, M, C, P, r, rp, cpw, out, out2, out2_ld,
-                                                     s, hi, lo);
-  QL_LAUNCH_CHECK();
-  return QLORA_OK;
+  const SkinnyOut o{P, out, out2, hi, lo};
+  return launch_skinny(In, M, C, 1, &o, p_col, r, rp, out2_ld, s, st);
 }
 
 size_t colacc_part_bytes(int64_t M, int64_t C0, int64_t C1, int rp) {

@@ -133,8 +133,9 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X,
  * NULL / an M x r float32 buffer per weight. All weights share k, r,
  * lora_alpha and the double-quantisation mode. For M <= 16 the weights run
  * as one GEMV launch (row groups of all weights in one grid; X and the LoRA
- * down projections read once) plus one epilogue launch; for larger M each
- * weight runs the two-launch GEMM path. Results are bit-identical to nw
+ * down projections read once) plus one epilogue launch; for larger M as one
+ * launch computing every H_i = X A_i^T plus one fused dequant-GEMM launch
+ * over the column tiles of all weights. Results are bit-identical to nw
  * separate qlora_linear_fwd calls.
  * Workspace: qlora_workspace_bytes(QLORA_OP_FWD_MULTI, sum of d_i, k, M, r, dq).
  */

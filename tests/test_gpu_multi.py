@@ -1,7 +1,8 @@
 """GPU checks of the sibling-projection forward (qlora_linear_fwd_multi):
 weights that read the same X (q/k/v, gate/up) in one call give bit-identical
 Y and H to separate qlora_linear_fwd calls, on the GEMV path (one grouped
-launch) and the GEMM path, and agree with the float64 oracle."""
+launch) and the GEMM path (one launch for all H, one grouped GEMM), and
+agree with the float64 oracle."""
 
 import numpy as np
 import pytest
@@ -30,6 +31,8 @@ CASES = [
     ([200, 320], 576, 7, 5, True),             # padded ranks, ragged row groups
     ([256, 512], 512, 40, 16, True),           # GEMM path
     ([136, 264, 64], 192, 300, 8, False),      # GEMM path, ragged tiles, padded ranks
+    ([128, 64, 192, 256], 320, 100, 16, True), # GEMM path, four weights in one launch
+    ([4096, 4096, 4096], 4096, 512, 16, True), # q/k/v-shaped
 ]
 
 
