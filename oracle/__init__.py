@@ -17,6 +17,8 @@ Modules
                  all in float64 on bf16-exact inputs, rounded once to bf16.
 ``oracle.adamw`` The 32-bit AdamW step of the LoRA matrices (the paged
                  optimiser's update), elementwise float32 in a stated order.
+``oracle.dropout`` LoRA dropout on the adapter input: Philox4x32-10 keep
+                 mask and the float64 forward/backward with the mask.
 
 Every function cites the page passage it follows. A page is cited by its
 title and section, e.g. "QLoRA glossary (Ultralytics), 'QLoRA 的工作原理'".
