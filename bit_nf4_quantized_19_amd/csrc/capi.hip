@@ -104,8 +104,27 @@ int64_t fwd_multi_bytes(int64_t dtot, int64_t k, int64_t M, int r) {
 struct BwdWs {
   uint16_t *Bt, *Gs_hi, *Gs_lo;
   float *H, *G, *cpart;
+  uint8_t *keep;
   int64_t bytes;
 };
+
+// Kernel-side dropout parameters of weight `i` of a call (seed + i, so the
+// sibling projections of one call draw independent masks).
+DropParams drop_params(const qlora_lora_dropout *dr, int i) {
+  DropParams dp{0u, 0u, 0u, 1.0f, 0};
+  if (dr && dr->p > 0.0f) {
+    const uint64_t seed = dr->seed + (uint64_t)i;
+    dp.k0 = (uint32_t)seed;
+    dp.k1 = (uint32_t)(seed >> 32);
+    dp.thr = (uint32_t)floor((double)dr->p * 4294967296.0);
+    dp.inv_keep = (float)(1.0 / (1.0 - (double)dr->p));
+    dp.on = 1;
+  }
+  return dp;
+}
+bool drop_ok(const qlora_lora_dropout *dr) {
+  return !dr || (isfinite(dr->p) && dr->p >= 0.0f && dr->p < 1.0f);
+}
 
 BwdWs bwd_layout(char *base, int64_t d, int64_t k, int64_t M, int r, bool need_h, bool need_dx) {
   const int rp = (int)ql_rup(r, 16);
@@ -118,6 +137,7 @@ BwdWs bwd_layout(char *base, int64_t d, int64_t k, int64_t M, int r, bool need_h
   L.Gs_hi = need_dx ? c.take<uint16_t>(M * rp * 2) : nullptr;
   L.Gs_lo = need_dx ? c.take<uint16_t>(M * rp * 2) : nullptr;
   L.cpart = c.take<float>((int64_t)colacc_part_bytes(M, d, k, rp));
+  L.keep = c.take<uint8_t>(M * (k >> 2));   // adapter-input dropout: keep nibbles of X
   L.bytes = c.off;
   return L;
 }
@@ -198,9 +218,11 @@ static qlora_status check_lora(const uint16_t *A, const uint16_t *B, int32_t r, 
 static qlora_status linear_fwd_group(const qlora_nf4_weight *const *w, int nw, const uint16_t *X,
                                      int64_t M, const uint16_t *const *A,
                                      const uint16_t *const *B, int32_t r, float lora_alpha,
-                                     uint16_t *const *Y, float *const *H_save, void *ws,
-                                     size_t ws_bytes, void *stream, int64_t ws_need) {
+                                     const qlora_lora_dropout *drop, uint16_t *const *Y,
+                                     float *const *H_save, void *ws, size_t ws_bytes,
+                                     void *stream, int64_t ws_need) {
   if (nw < 1 || nw > kMaxGroup || !w || !A || !B || !Y) return QLORA_ERR_INVALID_ARG;
+  if (!drop_ok(drop)) return QLORA_ERR_INVALID_ARG;
   qlora_status s;
   int64_t d[kMaxGroup];
   for (int i = 0; i < nw; ++i) {
@@ -231,7 +253,8 @@ static qlora_status linear_fwd_group(const qlora_nf4_weight *const *w, int nw, c
         Ap = L.Ap[i];
         Bp = L.Bp[i];
       }
-      in[i] = GemvIn{w[i]->codes, scale_src(w[i]), d[i], Ap, Bp, H_save ? H_save[i] : nullptr, Y[i]};
+      in[i] = GemvIn{w[i]->codes, scale_src(w[i]), d[i], Ap, Bp, H_save ? H_save[i] : nullptr, Y[i],
+                     drop_params(drop, i)};
     }
     return launch_gemv_fwd(nw, in, k, X, M, r, rp, sc, L.gpart, st);
   }
@@ -239,7 +262,8 @@ static qlora_status linear_fwd_group(const qlora_nf4_weight *const *w, int nw, c
   // in one launch; H_save gets the M x r copies
   SkinnyOut so[kMaxGroup];
   for (int i = 0; i < nw; ++i)
-    so[i] = SkinnyOut{A[i], L.H[i], H_save ? H_save[i] : nullptr, L.Hs_hi[i], L.Hs_lo[i]};
+    so[i] = SkinnyOut{A[i], L.H[i], H_save ? H_save[i] : nullptr, L.Hs_hi[i], L.Hs_lo[i],
+                      drop_params(drop, i)};
   if ((s = launch_skinny(X, M, k, nw, so, false, r, rp, r, sc, st)) != QLORA_OK) return s;
   if (nw == 1)
     return launch_gemm_fwd(w[0]->codes, scale_src(w[0]), d[0], k, X, M, B[0], r, L.Hs_hi[0],
@@ -260,7 +284,22 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int6
   const uint16_t *const Al[1] = {A}, *const Bl[1] = {B};
   uint16_t *const Yl[1] = {Y};
   float *const Hl[1] = {H_save};
-  return linear_fwd_group(wl, 1, X, M, Al, Bl, r, lora_alpha, Yl, Hl, ws, ws_bytes, stream, 0);
+  return linear_fwd_group(wl, 1, X, M, Al, Bl, r, lora_alpha, nullptr, Yl, Hl, ws, ws_bytes,
+                          stream, 0);
+}
+
+qlora_status qlora_linear_fwd_ex(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
+                                 const uint16_t *A, const uint16_t *B, int32_t r,
+                                 float lora_alpha, const qlora_lora_dropout *dropout,
+                                 uint16_t *Y, float *H_save, void *ws, size_t ws_bytes,
+                                 void *stream) {
+  if (!w) return QLORA_ERR_INVALID_ARG;
+  const qlora_nf4_weight *const wl[1] = {w};
+  const uint16_t *const Al[1] = {A}, *const Bl[1] = {B};
+  uint16_t *const Yl[1] = {Y};
+  float *const Hl[1] = {H_save};
+  return linear_fwd_group(wl, 1, X, M, Al, Bl, r, lora_alpha, dropout, Yl, Hl, ws, ws_bytes,
+                          stream, 0);
 }
 
 qlora_status qlora_linear_fwd_multi(const qlora_nf4_weight *const *w, int32_t nw,
@@ -277,13 +316,25 @@ qlora_status qlora_linear_fwd_multi(const qlora_nf4_weight *const *w, int32_t nw
   if (check_weight_shape(dtot, w[0]->k) != QLORA_OK) return QLORA_ERR_UNSUPPORTED;
   // the documented size (qlora_workspace_bytes(QLORA_OP_FWD_MULTI, sum of d, ...))
   const int64_t need = (r >= 1 && r <= 128 && M >= 1) ? fwd_multi_bytes(dtot, w[0]->k, M, r) : 0;
-  return linear_fwd_group(w, nw, X, M, A, B, r, lora_alpha, Y, H_save, ws, ws_bytes, stream, need);
+  return linear_fwd_group(w, nw, X, M, A, B, r, lora_alpha, nullptr, Y, H_save, ws, ws_bytes,
+                          stream, need);
 }
 
 qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
                               const uint16_t *A, const uint16_t *B, int32_t r, float lora_alpha,
                               const uint16_t *dY, const float *H, uint16_t *dX, uint16_t *dA,
                               uint16_t *dB, void *ws, size_t ws_bytes, void *stream) {
+  return qlora_linear_bwd_ex(w, X, M, A, B, r, lora_alpha, nullptr, dY, H, dX, dA, dB, ws,
+                             ws_bytes, stream);
+}
+
+qlora_status qlora_linear_bwd_ex(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
+                                 const uint16_t *A, const uint16_t *B, int32_t r,
+                                 float lora_alpha, const qlora_lora_dropout *dropout,
+                                 const uint16_t *dY, const float *H, uint16_t *dX, uint16_t *dA,
+                                 uint16_t *dB, void *ws, size_t ws_bytes, void *stream) {
+  if (!drop_ok(dropout)) return QLORA_ERR_INVALID_ARG;
+  const DropParams dp = drop_params(dropout, 0);
   qlora_status s = check_weight(w, false);
   if (s != QLORA_OK) return s;
   if ((s = check_lora(A, B, r, lora_alpha)) != QLORA_OK) return s;
@@ -304,9 +355,8 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, int6
 
   const float *Hq = H;  // M x rp
   if (need_h) {
-    if ((s = launch_skinny(X, M, k, A, false, r, rp, L.H, nullptr, 0, sc, nullptr, nullptr,
-                           st)) != QLORA_OK)
-      return s;
+    const SkinnyOut so{A, L.H, nullptr, nullptr, nullptr, dp};
+    if ((s = launch_skinny(X, M, k, 1, &so, false, r, rp, 0, sc, st)) != QLORA_OK) return s;
     Hq = L.H;
   }
   // G = dY B (float32, M x rp) and s*G as bf16 hi/lo for the dX epilogue; B
@@ -320,12 +370,15 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, int6
   }
   if (s != QLORA_OK) return s;
   // dB = s dY^T H (d x r) and dA = s G^T X (r x k), one launch
-  if ((s = launch_colacc2(ColaccReq{dY, d, Hq, dB, 0}, ColaccReq{X, k, L.G, dA, 1}, M, rp, r, sc,
+  const DropParams none{0u, 0u, 0u, 1.0f, 0};
+  if ((s = launch_colacc2(ColaccReq{dY, d, Hq, dB, 0, none, nullptr},
+                          ColaccReq{X, k, L.G, dA, 1, dp, (dp.on && need_dx) ? L.keep : nullptr},
+                          M, rp, r, sc,
                           L.cpart, st)) != QLORA_OK)
     return s;
   if (need_dx) {
     if ((s = launch_gemm_dx(w->codes, scale_src(w), d, k, dY, M, A, r, L.Gs_hi, L.Gs_lo, rp, dX,
-                            st)) != QLORA_OK)
+                            dp.on ? L.keep : nullptr, dp.inv_keep, st)) != QLORA_OK)
       return s;
   }
   return QLORA_OK;

@@ -64,6 +64,8 @@ struct GemmArgs {
   const uint16_t *Shi, *Slo;  // M x rp
   int r, rp;
   uint16_t *Out;         // M x Ntot
+  const uint8_t *keep;   // dX with adapter-input dropout: keep nibbles (M x Ntot/4), else NULL
+  float inv_keep;        // 1/(1-p)
 };
 
 // LDS, one object per stage.
@@ -418,7 +420,42 @@ struct Tile {
 
   // LoRA rank-r term: two extra K-chunks per 16 of rp (hi and lo of S), then
   // the bf16 stores. Lane holds D[8(e/4) + 4(l/32) + e%4][l%32] = Out[m][n].
+  // With adapter-input dropout (dX only) the rank-r term goes to its own
+  // accumulators and is added where the input element was kept, times
+  // 1/(1-p): dX = dY W' + s (G A) * keep / (1 - p).
   QL_DEV void epilogue() {
+    if (MODE == 1 && g.keep) {
+      f32x16 lacc[2][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) lacc[i][j][q] = 0.0f;
+      lora_term(lacc);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          int64_t m = m0 + wm * 64 + 32 * j + r32;
+          m = m < g.M ? m : g.M - 1;   // rows past M: not stored
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            int64_t n = n0 + wn * 64 + 32 * i + 8 * q4 + 4 * h;
+            n = n < g.Ntot ? n : g.Ntot - 4;   // columns past Ntot: not stored
+            const uint32_t kb = g.keep[m * (g.Ntot >> 2) + (n >> 2)];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if ((kb >> e) & 1u) acc[i][j][4 * q4 + e] += lacc[i][j][4 * q4 + e] * g.inv_keep;
+          }
+        }
+    } else {
+      lora_term(acc);
+    }
+    store();
+  }
+
+  QL_DEV void lora_term(f32x16 (&dst)[2][2]) {
     for (int t0 = 0; t0 < g.rp; t0 += 16) {
       // L[n][t0 + 8h .. +7] read in place (ranks past r and n past Ntot: 0);
       // loads from clamped addresses, the zeroing applied afterwards
@@ -472,9 +509,12 @@ struct Tile {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = ql::mfma32(a[i], b[j], acc[i][j]);
+          for (int j = 0; j < 2; ++j) dst[i][j] = ql::mfma32(a[i], b[j], dst[i][j]);
       }
     }
+  }
+
+  QL_DEV void store() {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -617,7 +657,7 @@ qlora_status launch_gemm_fwd_group(int nw, const GemmFwdIn *in, int64_t k, const
 qlora_status launch_gemm_dx(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, int64_t k,
                             const uint16_t *dY, int64_t M, const uint16_t *A, int r,
                             const uint16_t *Gs_hi, const uint16_t *Gs_lo, int rp,
-                            uint16_t *dX, hipStream_t st) {
-  GemmArgs g{codes, sc, d, k, dY, M, k, d, A, Gs_hi, Gs_lo, r, rp, dX};
+                            uint16_t *dX, const uint8_t *keep, float inv_keep, hipStream_t st) {
+  GemmArgs g{codes, sc, d, k, dY, M, k, d, A, Gs_hi, Gs_lo, r, rp, dX, keep, inv_keep};
   return launch_gemm(1, g, st);
 }

@@ -39,6 +39,7 @@
 
 #include "kernels.h"
 #include "nf4_tables.h"
+#include "philox.h"
 
 namespace {
 
@@ -64,6 +65,7 @@ struct GemvW {
   int64_t rbase;   // first column of this weight in the partial-sum rows
   const uint16_t *Ap;  // LoRA A, rp x k (ranks past r are zero rows)
   float *hpart;    // [S * GW][M][rp]: H = X A^T partial sums per slice and wave
+  DropParams dp;   // dropout of X on this weight's adapter input
 };
 
 struct GemvArgs {
@@ -101,6 +103,11 @@ QL_DEV GemvW wsel(const GemvArgs &g, int i) {
   W.rbase = QL_PICK(g.w, i, rbase);
   W.Ap = QL_PICK(g.w, i, Ap);
   W.hpart = QL_PICK(g.w, i, hpart);
+  W.dp.k0 = QL_PICK(g.w, i, dp.k0);
+  W.dp.k1 = QL_PICK(g.w, i, dp.k1);
+  W.dp.thr = QL_PICK(g.w, i, dp.thr);
+  W.dp.inv_keep = QL_PICK(g.w, i, dp.inv_keep);
+  W.dp.on = QL_PICK(g.w, i, dp.on);
   return W;
 }
 QL_DEV int weight_of(const GemvArgs &g, int64_t rg) {
@@ -274,6 +281,16 @@ QL_DEV void lora_down_partial(const GemvArgs &g, int64_t slice, int nblk, int wa
   }
   for (int wi = 0; wi < (GRP ? g.nw : 1); ++wi) {
     const GemvW W = GRP ? wsel(g, wi) : g.w[0];
+    uint4 xm[4];   // X with this weight's adapter-input dropout applied
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xm[i] = xa[i];
+      if (W.dp.on) {
+        const uint64_t e = (uint64_t)(n < g.M ? n : 0) * (uint64_t)g.k +
+                           (uint64_t)(c0 + 32 * i + 8 * q);
+        xm[i] = mask_bf16x8(xa[i], keep4(W.dp, e) | (keep4(W.dp, e + 4) << 4));
+      }
+    }
     for (int cb = 0; cb < g.rp / 16; ++cb) {
       uint4 aa[4];
 #pragma unroll
@@ -284,7 +301,7 @@ QL_DEV void lora_down_partial(const GemvArgs &g, int64_t slice, int nblk, int wa
       }
       f32x4 hacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hacc = ql::mfma16(xa[i], aa[i], hacc);
+      for (int i = 0; i < 4; ++i) hacc = ql::mfma16(xm[i], aa[i], hacc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 4 * q + i;
@@ -385,6 +402,7 @@ struct EpiW {
   uint16_t *Y;          // M x d
   float *hsave;         // M x r or NULL
   int64_t d, rbase, ebase;   // rows, first partial-sum column, first workgroup
+  float hscale;         // 1/(1-p) with adapter-input dropout, else 1
 };
 struct EpiArgs {
   EpiW w[GMAXW];
@@ -404,6 +422,7 @@ QL_DEV EpiW esel(const EpiArgs &e, int i) {
   W.d = QL_PICK(e.w, i, d);
   W.rbase = QL_PICK(e.w, i, rbase);
   W.ebase = QL_PICK(e.w, i, ebase);
+  W.hscale = QL_PICK(e.w, i, hscale);
   return W;
 }
 
@@ -441,6 +460,7 @@ __global__ __launch_bounds__(256) void gemv_epilogue_kernel(EpiArgs e) {
     if (tid < rp) {
       float ha = 0.0f;
       for (int gi = 0; gi < ng; ++gi) ha += hp[gi][tid];
+      ha *= W.hscale;   // inverted dropout of the adapter input (exactly 1 without)
       hs[tid] = ha;
       if (W.hsave && xb == 0 && tid < e.r) W.hsave[m * e.r + tid] = ha;
     }
@@ -477,8 +497,10 @@ qlora_status launch_gemv_fwd(int nw, const GemvIn *in, int64_t k, const uint16_t
   EpiArgs e{};
   for (int i = 0; i < nw; ++i) {
     const int64_t d = in[i].d;
-    g.w[i] = GemvW{in[i].codes, in[i].sc, d, d * (k >> 6), ngroups, dtot, in[i].Ap, nullptr};
-    e.w[i] = EpiW{in[i].Bp, nullptr, in[i].Y, in[i].H_save, d, dtot, eblocks};
+    g.w[i] = GemvW{in[i].codes, in[i].sc, d, d * (k >> 6), ngroups, dtot, in[i].Ap, nullptr,
+                   in[i].dp};
+    e.w[i] = EpiW{in[i].Bp, nullptr, in[i].Y, in[i].H_save, d, dtot, eblocks,
+                  in[i].dp.on ? in[i].dp.inv_keep : 1.0f};
     ngroups += ql_cdiv(d, 16);
     eblocks += ql_cdiv(d, 256);
     dtot += d;

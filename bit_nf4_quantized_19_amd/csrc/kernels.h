@@ -3,6 +3,7 @@
 #pragma once
 
 #include "common.h"
+#include "philox.h"
 
 // quantize.hip
 qlora_status launch_quantize(const uint16_t *W0, int64_t n, uint8_t *codes,
@@ -40,6 +41,7 @@ struct SkinnyOut {
   const uint16_t *P;
   float *out, *out2;
   uint16_t *hi, *lo;
+  DropParams dp;   // dropout on In (row form only; dp.on == 0: none)
 };
 qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, int nw, const SkinnyOut *o,
                            bool p_col, int r, int rp, int out2_ld, float s, hipStream_t st);
@@ -52,6 +54,8 @@ struct ColaccReq {
   const float *Q;
   uint16_t *out;
   int transpose_out;
+  DropParams dp;     // dropout of In (dp.on == 0: none); the result is scaled by 1/(1-p)
+  uint8_t *keep;     // with dropout: M x C/4 keep nibbles written here (may be NULL)
 };
 qlora_status launch_colacc2(const ColaccReq &a, const ColaccReq &b, int64_t M, int rp,
                             int r, float s, float *part, hipStream_t st);
@@ -74,11 +78,13 @@ struct GemmFwdIn {
 };
 qlora_status launch_gemm_fwd_group(int nw, const GemmFwdIn *in, int64_t k, const uint16_t *X,
                                    int64_t M, int r, int rp, hipStream_t st);
+// keep (M x k/4 keep nibbles, or NULL): adapter-input dropout of the forward;
+// the rank-r term of dX is then kept per element and scaled by inv_keep.
 qlora_status launch_gemm_dx(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
                             int64_t k, const uint16_t *dY, int64_t M,
                             const uint16_t *A, int r, const uint16_t *Gs_hi,
                             const uint16_t *Gs_lo, int rp, uint16_t *dX,
-                            hipStream_t st);
+                            const uint8_t *keep, float inv_keep, hipStream_t st);
 
 // gemv.hip : memory-bound forward for M <= 16, including the LoRA down
 // projection, for nw (1..4) weights that read the same X (sibling
@@ -93,6 +99,7 @@ struct GemvIn {
   const uint16_t *Ap, *Bp;
   float *H_save;
   uint16_t *Y;
+  DropParams dp;   // adapter-input dropout (dp.on == 0: none)
 };
 qlora_status launch_gemv_fwd(int nw, const GemvIn *in, int64_t k, const uint16_t *X, int64_t M,
                              int r, int rp, float s, float *part, hipStream_t st);

@@ -27,6 +27,7 @@
 #include <algorithm>
 
 #include "kernels.h"
+#include "philox.h"
 
 namespace {
 
@@ -81,6 +82,7 @@ struct SkW {
   const uint16_t *P;
   float *out, *out2;
   uint16_t *hi, *lo;
+  DropParams dp;   // dropout of In's elements (row form only)
 };
 struct SkinnyArgs {
   SkW w[4];
@@ -107,6 +109,12 @@ __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
   const int64_t M = a.M, C = a.C, cpw = a.cpw;
   const int r = a.r, rp = a.rp, out2_ld = a.out2_ld;
   const float s = a.s;
+  DropParams dp;
+  dp.k0 = QL_SKPICK(dp.k0);
+  dp.k1 = QL_SKPICK(dp.k1);
+  dp.thr = QL_SKPICK(dp.thr);
+  dp.inv_keep = QL_SKPICK(dp.inv_keep);
+  dp.on = !PCOL && QL_SKPICK(dp.on);
   constexpr int PQ = 272;   // bytes per lane group in the transposition slot (256 + pad)
   __shared__ f32x4 red[SK_W][64];
   __shared__ __align__(16) unsigned char pst[PCOL ? SK_W : 1][4 * PQ];
@@ -133,6 +141,10 @@ __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
       if (cc + 8 * kq < c_hi) {   // c_hi % 8 == 0: a chunk is all in or all out
         if (m_ok) a[u] = *(const uint4 *)(inr + cc);
         if (!PCOL && t_ok) b[u] = *(const uint4 *)(prow + cc);
+      }
+      if (dp.on) {   // dropped elements of X (token m, columns cc + 8kq ..) read as 0
+        const uint64_t e = (uint64_t)(m_ok ? m : 0) * (uint64_t)C + (uint64_t)(cc + 8 * kq);
+        a[u] = mask_bf16x8(a[u], keep4(dp, e) | (keep4(dp, e + 4) << 4));
       }
       if (PCOL) {
         const int64_t row = cc + 8 * kq + rho;   // B row, t = t0 + 8 hf .. +7
@@ -174,6 +186,7 @@ __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int64_t mm = mb * 16 + 4 * kq + i;
     if (mm >= M) continue;
+    if (dp.on) v[i] *= dp.inv_keep;   // inverted dropout: kept elements scaled by 1/(1-p)
     out[mm * rp + t] = v[i];
     if (out2 && t < out2_ld) out2[mm * out2_ld + t] = v[i];
     if (hi) {
@@ -197,6 +210,8 @@ struct ColaccProb {
   const float *Q;      // M x rp
   float *part;         // S x C x rp
   int64_t groups;      // column groups of CA_COLS
+  DropParams dp;       // dropout of In's elements (dp.on == 0: none)
+  uint8_t *keep;       // M x C/4 keep nibbles written when dropping (or NULL)
 };
 
 // Batch of CA_TOK tokens of one wave: this lane's 4 columns of each token
@@ -217,6 +232,20 @@ QL_DEV void ca_load(CaBatch &b, const uint16_t *inc, int64_t C, bool c_ok, const
   const int64_t mq = m + (lane >> 2);
   b.q = mq < m_hi ? *(const float4 *)(Q + mq * rp + t0 + 4 * (lane & 3))
                   : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// Dropout of the batch's first n tokens: their dropped elements become 0,
+// and the keep bits (4 per lane and token) are stored for the dX epilogue.
+QL_DEV void ca_drop(CaBatch &b, const DropParams &dp, int64_t m, int n, int64_t C, int64_t c0,
+                    uint8_t *keep) {
+#pragma unroll
+  for (int u = 0; u < CA_TOK; ++u) {
+    if (u >= n) continue;  // wave-uniform
+    const uint32_t bits = keep4(dp, (uint64_t)(m + u) * (uint64_t)C + (uint64_t)c0);
+    b.v[u].x &= ((bits & 1u) ? 0x0000FFFFu : 0u) | ((bits & 2u) ? 0xFFFF0000u : 0u);
+    b.v[u].y &= ((bits & 4u) ? 0x0000FFFFu : 0u) | ((bits & 8u) ? 0xFFFF0000u : 0u);
+    if (keep) keep[(m + u) * (C >> 2) + (c0 >> 2)] = (uint8_t)bits;
+  }
 }
 
 // acc[c][t] += x[token][c] * Q[token][t] over the batch's tokens (the first
@@ -278,6 +307,9 @@ __global__ __launch_bounds__(64 * CA_W) void colacc_kernel(ColaccProb p0, Colacc
       cur = nxt;
       if (m + CA_TOK < w_hi) ca_load(nxt, inc, P.C, c_ok, P.Q, rp, t0, m + CA_TOK, w_hi, lane);
       qst[wave][lane] = cur.q;   // this wave's previous reads of the slot precede (in order)
+      if (P.dp.on && c_ok)
+        ca_drop(cur, P.dp, m, (int)min<int64_t>(CA_TOK, w_hi - m), P.C, c0,
+                tb == 0 ? P.keep : nullptr);
       if (m + CA_TOK <= w_hi)
         ca_batch<false>(acc, cur, qst[wave], CA_TOK);
       else
@@ -312,11 +344,12 @@ struct ColaccOut {
   uint16_t *out;
   int transpose_out;  // 0: out is C x r; 1: out is r x C
   int64_t n;          // C * r
+  float scale;        // s, times 1/(1-p) for a dropped input
 };
 
 // one thread per output element of problem 0 then problem 1
 __global__ __launch_bounds__(256) void colacc_reduce_kernel(ColaccOut o0, ColaccOut o1, int S,
-                                                            int rp, int r, float s) {
+                                                            int rp, int r) {
   int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool second = idx >= o0.n;
   const ColaccOut &O = second ? o1 : o0;
@@ -338,7 +371,7 @@ __global__ __launch_bounds__(256) void colacc_reduce_kernel(ColaccOut o0, Colacc
 #pragma unroll
   for (int sp = 0; sp < CA_MAXSPLIT; ++sp)
     if (sp < S) v += p[sp];
-  O.out[idx] = ql::f_to_bf16(s * v);
+  O.out[idx] = ql::f_to_bf16(O.scale * v);
 }
 
 int64_t colacc_split(int64_t M, int64_t C, int rp) {
@@ -378,7 +411,7 @@ qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, int nw, con
   SkinnyArgs a{};
   for (int i = 0; i < 4; ++i) {
     const SkinnyOut &x = o[i < nw ? i : 0];   // unused slots: never selected
-    a.w[i] = SkW{x.P, x.out, x.out2, x.hi, x.lo};
+    a.w[i] = SkW{x.P, x.out, x.out2, x.hi, x.lo, x.dp};
   }
   a.In = In;
   a.M = M;
@@ -404,7 +437,7 @@ qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, int nw, con
 qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, const uint16_t *P,
                            bool p_col, int r, int rp, float *out, float *out2, int out2_ld,
                            float s, uint16_t *hi, uint16_t *lo, hipStream_t st) {
-  const SkinnyOut o{P, out, out2, hi, lo};
+  const SkinnyOut o{P, out, out2, hi, lo, DropParams{0u, 0u, 0u, 1.0f, 0}};
   return launch_skinny(In, M, C, 1, &o, p_col, r, rp, out2_ld, s, st);
 }
 
@@ -418,19 +451,19 @@ qlora_status launch_colacc2(const ColaccReq &a, const ColaccReq &b, int64_t M, i
   const int64_t S0 = colacc_split(M, a.C + b.C, rp);
   const int64_t mps = ql_cdiv(M, S0);
   const int64_t S = ql_cdiv(M, mps);
-  ColaccProb p0{a.In, a.C, a.Q, part, ql_cdiv(a.C, CA_COLS)};
-  ColaccProb p1{b.In, b.C, b.Q, part + S * a.C * rp, ql_cdiv(b.C, CA_COLS)};
+  ColaccProb p0{a.In, a.C, a.Q, part, ql_cdiv(a.C, CA_COLS), a.dp, a.keep};
+  ColaccProb p1{b.In, b.C, b.Q, part + S * a.C * rp, ql_cdiv(b.C, CA_COLS), b.dp, b.keep};
   const int64_t tbs = rp / 16;
   dim3 grid((unsigned)((p0.groups + p1.groups) * tbs), (unsigned)S);
   {
     QlProf prof(QLORA_K_LORA_COLACC, st);
     colacc_kernel<<<grid, 64 * CA_W, 0, st>>>(p0, p1, M, rp, mps);
   }
-  ColaccOut o0{p0.part, a.C, a.out, a.transpose_out, a.C * r};
-  ColaccOut o1{p1.part, b.C, b.out, b.transpose_out, b.C * r};
+  ColaccOut o0{p0.part, a.C, a.out, a.transpose_out, a.C * r, a.dp.on ? s * a.dp.inv_keep : s};
+  ColaccOut o1{p1.part, b.C, b.out, b.transpose_out, b.C * r, b.dp.on ? s * b.dp.inv_keep : s};
   QlProf prof(QLORA_K_LORA_COLACC_REDUCE, st);
   colacc_reduce_kernel<<<(unsigned)ql_cdiv(o0.n + o1.n, 256), 256, 0, st>>>(o0, o1, (int)S, rp,
-                                                                           r, s);
+                                                                           r);
   QL_LAUNCH_CHECK();
   return QLORA_OK;
 }

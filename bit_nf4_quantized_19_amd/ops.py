@@ -55,6 +55,10 @@ SIGNATURES = {
                                         _vp, _sz, _vp]),
     "qlora_linear_bwd": (ctypes.c_int, [_PW, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp,
                                         _vp, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_linear_fwd_ex": (ctypes.c_int, [_PW, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
+                                           _vp, _sz, _vp]),
+    "qlora_linear_bwd_ex": (ctypes.c_int, [_PW, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
+                                           _vp, _vp, _vp, _vp, _sz, _vp]),
     "qlora_linear_fwd_multi": (ctypes.c_int, [_vp, _i32, _vp, _i64, _vp, _vp, _i32, _f32, _vp,
                                               _vp, _vp, _sz, _vp]),
     "qlora_merge": (ctypes.c_int, [_PW, _vp, _vp, _i32, _f32, _vp, _vp]),
@@ -200,10 +204,16 @@ def dequantize(w: NF4Weight, out: torch.Tensor | None = None, stream=None) -> to
     return Y
 
 
+class LoraDropoutC(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_float), ("reserved", ctypes.c_uint32), ("seed", ctypes.c_uint64)]
+
+
 def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                lora_alpha: float, save_h: bool = True, Y: torch.Tensor | None = None,
-               H: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
-    """Y = X W'^T + (alpha/r) (X A^T) B^T. Returns (Y, H or None)."""
+               H: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None,
+               dropout: float = 0.0, seed: int = 0):
+    """Y = X W'^T + (alpha/r) (X~ A^T) B^T with X~ the adapter input after
+    dropout at rate `dropout` (mask from `seed`; 0 = none). Returns (Y, H or None)."""
     for t, nm in ((X, "X"), (A, "A"), (B, "B")):
         _dev_bf16(t, nm)
     M = X.shape[0]
@@ -215,10 +225,17 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
     wsb = workspace_bytes(OP_FWD, w.d, w.k, M, r, w.double_quant)
     wst, wsn = _workspace(wsb, X.device, ws)
     cw = w.c_struct()
-    _check(lib().qlora_linear_fwd(ctypes.byref(cw), X.data_ptr(), M, A.data_ptr(),
-                                  B.data_ptr(), r, float(lora_alpha), Y.data_ptr(),
-                                  _ptr(H) if save_h else None, _ptr(wst), wsn,
-                                  _stream(stream)), "qlora_linear_fwd")
+    if dropout:
+        dr = LoraDropoutC(float(dropout), 0, int(seed))
+        _check(lib().qlora_linear_fwd_ex(ctypes.byref(cw), X.data_ptr(), M, A.data_ptr(),
+                                         B.data_ptr(), r, float(lora_alpha), ctypes.addressof(dr),
+                                         Y.data_ptr(), _ptr(H) if save_h else None, _ptr(wst),
+                                         wsn, _stream(stream)), "qlora_linear_fwd_ex")
+    else:
+        _check(lib().qlora_linear_fwd(ctypes.byref(cw), X.data_ptr(), M, A.data_ptr(),
+                                      B.data_ptr(), r, float(lora_alpha), Y.data_ptr(),
+                                      _ptr(H) if save_h else None, _ptr(wst), wsn,
+                                      _stream(stream)), "qlora_linear_fwd")
     return Y, (H if save_h else None)
 
 
@@ -257,8 +274,8 @@ def linear_fwd_multi(ws_: list, X: torch.Tensor, As: list, Bs: list, lora_alpha:
 def linear_bwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                lora_alpha: float, dY: torch.Tensor, H: torch.Tensor | None = None,
                need_dx: bool = True, dX=None, dA=None, dB=None,
-               ws: torch.Tensor | None = None, stream=None):
-    """Returns (dX or None, dA, dB)."""
+               ws: torch.Tensor | None = None, stream=None, dropout: float = 0.0, seed: int = 0):
+    """Returns (dX or None, dA, dB); `dropout`/`seed` as given to the forward."""
     for t, nm in ((X, "X"), (A, "A"), (B, "B"), (dY, "dY")):
         _dev_bf16(t, nm)
     M = X.shape[0]
@@ -273,10 +290,18 @@ def linear_bwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
     wsb = workspace_bytes(OP_BWD, w.d, w.k, M, r, w.double_quant)
     wst, wsn = _workspace(wsb, dev, ws)
     cw = w.c_struct()
-    _check(lib().qlora_linear_bwd(ctypes.byref(cw), X.data_ptr(), M, A.data_ptr(),
-                                  B.data_ptr(), r, float(lora_alpha), dY.data_ptr(), _ptr(H),
-                                  _ptr(dX) if need_dx else None, dA.data_ptr(), dB.data_ptr(),
-                                  _ptr(wst), wsn, _stream(stream)), "qlora_linear_bwd")
+    if dropout:
+        dr = LoraDropoutC(float(dropout), 0, int(seed))
+        _check(lib().qlora_linear_bwd_ex(ctypes.byref(cw), X.data_ptr(), M, A.data_ptr(),
+                                         B.data_ptr(), r, float(lora_alpha), ctypes.addressof(dr),
+                                         dY.data_ptr(), _ptr(H), _ptr(dX) if need_dx else None,
+                                         dA.data_ptr(), dB.data_ptr(), _ptr(wst), wsn,
+                                         _stream(stream)), "qlora_linear_bwd_ex")
+    else:
+        _check(lib().qlora_linear_bwd(ctypes.byref(cw), X.data_ptr(), M, A.data_ptr(),
+                                      B.data_ptr(), r, float(lora_alpha), dY.data_ptr(), _ptr(H),
+                                      _ptr(dX) if need_dx else None, dA.data_ptr(), dB.data_ptr(),
+                                      _ptr(wst), wsn, _stream(stream)), "qlora_linear_bwd")
     return (dX if need_dx else None), dA, dB
 
 

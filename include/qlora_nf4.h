@@ -124,6 +124,34 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X,
                               void *stream);
 
 /*
+ * LoRA dropout on the adapter input (LLM tutorial ch. 3, 3.3 and Day-25
+ * notes 4.3: LoraConfig(lora_dropout=0.05); notes 7.x: 0.1 against
+ * overfitting). The pages give only the rate; reading taken: inverted
+ * dropout of X before A on the LoRA branch only, so with keep mask K
+ *   H  = ((X * K) A^T) / (1 - p),       Y  = X W'^T + s H B^T,
+ *   dA = s G^T (X * K) / (1 - p),       dB = s dY^T H,
+ *   dX = dY W' + s (G A) * K / (1 - p).
+ * K[m][c] is drawn from Philox4x32-10 (Salmon et al., SC'11): element
+ * e = m*k + c keeps when word e%4 of philox(counter (e/4 low, e/4 high, 0,
+ * 0), key (seed low, seed high)) >= floor(p * 2^32). The forward and the
+ * backward of one step must get the same p and seed. p == 0 (or a NULL
+ * pointer) is no dropout. 0 <= p < 1, else QLORA_ERR_INVALID_ARG.
+ */
+typedef struct qlora_lora_dropout {
+  float p;
+  uint32_t reserved;   /* set to 0 */
+  uint64_t seed;
+} qlora_lora_dropout;
+
+/* qlora_linear_fwd with adapter-input dropout (workspace as for QLORA_OP_FWD). */
+qlora_status qlora_linear_fwd_ex(const qlora_nf4_weight *w, const uint16_t *X,
+                                 int64_t M, const uint16_t *A, const uint16_t *B,
+                                 int32_t r, float lora_alpha,
+                                 const qlora_lora_dropout *dropout, uint16_t *Y,
+                                 float *H_save, void *ws, size_t ws_bytes,
+                                 void *stream);
+
+/*
  * Sibling projections: the forward above for nw (1..4) weights that read the
  * same activations X -- q, k, v of an attention block, or gate and up of the
  * MLP (LLM tutorial ch. 3, 3.3 and Day-25 notes 4.3: the adapters target
@@ -163,6 +191,17 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X,
                               const float *H, uint16_t *dX, uint16_t *dA,
                               uint16_t *dB, void *ws, size_t ws_bytes,
                               void *stream);
+
+/* qlora_linear_bwd for a forward run with adapter-input dropout (same p and
+ * seed); H, if passed, is the H_save of that forward. Workspace as for
+ * QLORA_OP_BWD. */
+qlora_status qlora_linear_bwd_ex(const qlora_nf4_weight *w, const uint16_t *X,
+                                 int64_t M, const uint16_t *A, const uint16_t *B,
+                                 int32_t r, float lora_alpha,
+                                 const qlora_lora_dropout *dropout, const uint16_t *dY,
+                                 const float *H, uint16_t *dX, uint16_t *dA,
+                                 uint16_t *dB, void *ws, size_t ws_bytes,
+                                 void *stream);
 
 /*
  * Merge: W_merged (d x k, bf16) = bf16(float(w') + s (B A)) with B A summed

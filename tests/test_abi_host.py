@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     ops = _ops()
     L = ops.lib()
     names = _declared_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     for name in names:
         assert hasattr(L, name), name
         assert name in ops.SIGNATURES, name
@@ -141,6 +141,21 @@ b("bwd_null_dY", dY=None)
 b("bwd_null_dA", dA=None)
 b("bwd_ws_small", wsb=128)
 b("bwd_r0", r=0)
+class DR(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_float), ("reserved", ctypes.c_uint32), ("seed", ctypes.c_uint64)]
+def fx(name, rate):
+    dr = DR(rate, 0, 7)
+    out[name] = L.qlora_linear_fwd_ex(ctypes.byref(w), P, 16, P, P, 8, 16.0, ctypes.addressof(dr),
+                                      P, P, P, 1 << 30, None)
+def bx(name, rate):
+    dr = DR(rate, 0, 7)
+    out[name] = L.qlora_linear_bwd_ex(ctypes.byref(w), P, 16, P, P, 8, 16.0, ctypes.addressof(dr),
+                                      P, None, P, P, P, P, 1 << 30, None)
+fx("fwd_drop_one", 1.0)
+fx("fwd_drop_neg", -0.25)
+fx("fwd_drop_nan", float("nan"))
+bx("bwd_drop_one", 1.0)
+bx("bwd_drop_inf", float("inf"))
 out["merge_null_out"] = L.qlora_merge(ctypes.byref(w), P, P, 8, 16.0, None, None)
 out["merge_r_big"] = L.qlora_merge(ctypes.byref(w), P, P, 500, 16.0, P, None)
 out["deq_null_out"] = L.qlora_nf4_dequantize(ctypes.byref(w), None, None)
@@ -173,7 +188,8 @@ EXPECTED = {
     "ws_misaligned": -3, "W0_null": -1, "fwd_r0": -1, "fwd_r129": -2, "fwd_nan_alpha": -1,
     "fwd_inf_alpha": -1, "fwd_M0": -1, "fwd_null_X": -1, "fwd_misaligned_B": -1,
     "fwd_ws_small": -3, "bwd_null_dY": -1, "bwd_null_dA": -1, "bwd_ws_small": -3,
-    "bwd_r0": -1, "merge_null_out": -1, "merge_r_big": -2, "deq_null_out": -1,
+    "bwd_r0": -1, "fwd_drop_one": -1, "fwd_drop_neg": -1, "fwd_drop_nan": -1,
+    "bwd_drop_one": -1, "bwd_drop_inf": -1, "merge_null_out": -1, "merge_r_big": -2, "deq_null_out": -1,
     "codebook_null": -1, "adam_null_param": -1, "adam_null_grad": -1, "adam_n0": -1,
     "adam_step0": -1, "adam_misaligned_m": -1, "adam_misaligned_out": -1,
     "adam_beta1_one": -1, "adam_neg_lr": -1, "adam_nan_eps": -1, "adam_unknown_pointer": -1,

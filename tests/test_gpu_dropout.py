@@ -1,0 +1,109 @@
+"""GPU parity of LoRA dropout on the adapter input against the float64 oracle
+(Philox4x32-10 keep mask drawn on each side from its own implementation of
+the generator). H and the all-zero-base dX are sums over the masked inputs,
+so a single mask bit that differs between the two sides shows far above the
+tolerances used here."""
+
+import numpy as np
+import pytest
+
+from _helpers import bf16_f64, oracle_quant, oracle_wdeq, rel_frob, to_dev, to_host_bits
+from bit_nf4_quantized_19_amd import synth
+from oracle import dropout as od
+from oracle import lora as olora
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bit_nf4_quantized_19_amd import ops as o
+    o.lib()
+    return o
+
+
+CASES = [
+    # d, k, M, r, p, seed, w_zero
+    (264, 512, 300, 16, 0.1, 11, False),     # GEMM path
+    (264, 512, 300, 16, 0.1, 11, True),      # GEMM path, LoRA branch alone
+    (704, 1088, 4, 16, 0.05, 12, False),     # GEMV path (decode), ragged slice
+    (704, 1088, 4, 16, 0.05, 12, True),
+    (200, 320, 40, 8, 0.3, 2 ** 40 + 5, True),   # padded ranks, 64-bit seed
+]
+
+
+@pytest.mark.parametrize("d,k,M,r,p,seed,w_zero", CASES)
+def test_dropout_matches_oracle(ops, d, k, M, r, p, seed, w_zero):
+    print(f"[dropout] d={d} k={k} M={M} r={r} p={p} seed={seed} w_zero={w_zero}", flush=True)
+    alpha = 2.0 * r
+    inp = synth.linear_inputs(d, k, M, r, idx=d + M)
+    if w_zero:
+        inp["W0"] = np.zeros_like(inp["W0"])
+    w = ops.quantize(to_dev(inp["W0"]), True)
+    X, A, B, dY = (to_dev(inp[n]) for n in ("X", "A", "B", "dY"))
+    Y, H = ops.linear_fwd(w, X, A, B, alpha, dropout=p, seed=seed)
+    dX, dA, dB = ops.linear_bwd(w, X, A, B, alpha, dY, H=H, dropout=p, seed=seed)
+    _, dA2, dB2 = ops.linear_bwd(w, X, A, B, alpha, dY, H=None, need_dx=False,
+                                 dropout=p, seed=seed)
+    torch.cuda.synchronize()
+    keep = od.keep_mask(seed, M, k, p)
+    s = olora.lora_scale(alpha, r)
+    Wd = oracle_wdeq(oracle_quant(inp["W0"], True), d, k)
+    Xf, Af, Bf, dYf = (bf16_f64(inp[n]) for n in ("X", "A", "B", "dY"))
+    Yo, Ho = od.forward(Wd, Xf, Af, Bf, s, keep, p)
+    dXo, dAo, dBo, _ = od.backward(Wd, Xf, Af, Bf, s, dYf, keep, p)
+    assert rel_frob(H.cpu().numpy().astype(np.float64), Ho) < 1e-5
+    for name, got, want in (("Y", Y, Yo), ("dX", dX, dXo), ("dA", dA, dAo), ("dB", dB, dBo)):
+        err = rel_frob(bf16_f64(to_host_bits(got)), want)
+        assert err <= TOL, f"{name}: {err:.3e}"
+    if w_zero:
+        # the masked rank-r term alone: a wrong keep bit would show at ~1e-2
+        assert rel_frob(bf16_f64(to_host_bits(dX)), dXo) < 8e-3
+    # the backward without H redraws the same mask: dA (which does not read H)
+    # is identical; dB is identical where the forward's H comes from the same
+    # kernel as the recomputation (M > 16), else equal up to the float32
+    # summation order of H over the slices of k
+    assert np.array_equal(to_host_bits(dA), to_host_bits(dA2))
+    if M > 16:
+        assert np.array_equal(to_host_bits(dB), to_host_bits(dB2))
+    else:
+        assert rel_frob(bf16_f64(to_host_bits(dB2)), bf16_f64(to_host_bits(dB))) < 1e-2
+
+
+@pytest.mark.parametrize("M", [4, 100])
+def test_zero_rate_equals_plain_calls(ops, M):
+    d, k, r = 128, 256, 16
+    inp = synth.linear_inputs(d, k, M, r, idx=5)
+    w = ops.quantize(to_dev(inp["W0"]), True)
+    X, A, B, dY = (to_dev(inp[n]) for n in ("X", "A", "B", "dY"))
+    # rate 0 through the dropout entry points is bit-identical to no dropout
+    from bit_nf4_quantized_19_amd import ops as o
+    import ctypes
+    Y0, H0 = ops.linear_fwd(w, X, A, B, 32.0)
+    Y1 = torch.empty_like(Y0)
+    H1 = torch.empty_like(H0)
+    dr = o.LoraDropoutC(0.0, 0, 123)
+    cw = w.c_struct()
+    wsb = o.workspace_bytes(o.OP_FWD, d, k, M, r, True)
+    ws = torch.empty(wsb + 256, dtype=torch.uint8, device="cuda")
+    ws = ws[(-ws.data_ptr()) % 256:]
+    st = o.lib().qlora_linear_fwd_ex(ctypes.byref(cw), X.data_ptr(), M, A.data_ptr(), B.data_ptr(),
+                                     r, 32.0, ctypes.addressof(dr), Y1.data_ptr(), H1.data_ptr(),
+                                     ws.data_ptr(), wsb, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(Y0), to_host_bits(Y1))
+    assert np.array_equal(H0.cpu().numpy().view(np.uint32), H1.cpu().numpy().view(np.uint32))
+
+
+def test_invalid_rate_is_rejected(ops):
+    inp = synth.linear_inputs(64, 128, 8, 16, idx=6)
+    w = ops.quantize(to_dev(inp["W0"]), True)
+    X, A, B = (to_dev(inp[n]) for n in ("X", "A", "B"))
+    for bad in (1.0, -0.1, float("nan")):
+        with pytest.raises(ops.QLoRAError):
+            ops.linear_fwd(w, X, A, B, 32.0, dropout=bad, seed=1)
