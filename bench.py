@@ -177,6 +177,24 @@ def main():
                 "algorithmic_flops_per_launch": dom[1], "avg_launch_us": round(avg_s * 1e6, 2)}
 
     rows = measure_rows(ops, synth, torch, dev) if args.rows == "on" else None
+    if rows is not None:
+        # the same step with dropout 0.05 on the adapter input (mask drawn in
+        # the kernels from a per-step seed) against the step without
+        def step_drop(i):
+            ops.linear_fwd(w, X, A, B, ALPHA, save_h=True, Y=Y, H=H, ws=ws_f,
+                           dropout=0.05, seed=1000 + i)
+            ops.linear_bwd(w, X, A, B, ALPHA, dY, H=H, dX=dX, dA=dA, dB=dB, ws=ws_b,
+                           dropout=0.05, seed=1000 + i)
+        ms_plain = _rotated(lambda i: step(), 1, 20)
+        ms_drop = _rotated(step_drop, 4, 20)
+        rows["lora_dropout_step"] = {
+            "p": 0.05, "shape": [D, K], "tokens": M, "r": R,
+            "step_ms_plain": round(ms_plain, 4), "step_ms_dropout": round(ms_drop, 4),
+            "overhead_frac": round(ms_drop / ms_plain - 1.0, 4),
+            "gemm_dx_us_dropout": round(_kernel_us(ops, "gemm_dx", step_drop, 4, 8), 2),
+            "lora_colacc_us_dropout": round(_kernel_us(ops, "lora_colacc", step_drop, 4, 8), 2),
+            "lora_down_us_dropout": round(_kernel_us(ops, "lora_down", step_drop, 4, 8), 2)}
+        log(f"[bench] dropout row: {json.dumps(rows['lora_dropout_step'])}")
     cpu = cpu_baseline(inp, flops) if args.cpu_baseline == "on" else None
 
     line = {
