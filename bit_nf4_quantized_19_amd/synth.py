@@ -33,6 +33,28 @@ def normal_bf16(shape, std: float, seed: int) -> np.ndarray:
     return _round_to_bf16_bits(x).reshape(shape)
 
 
+def normal_f32(shape, seed: int) -> np.ndarray:
+    """float32 ``N(0, 1)`` drawn with ``seed`` (a Gaussian test matrix for the
+    randomized range finder of the LoftQ factorisation)."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def lowrank_bf16(d: int, k: int, rank: int, scale: float, noise: float, seed: int) -> np.ndarray:
+    """bf16 bits of a d x k matrix with ``rank`` dominant directions plus noise:
+    ``sum_j scale * (1 - j / (2 rank)) u_j v_j^T + noise * N(0, 1)`` with
+    u_j, v_j unit vectors drawn from ``seed`` (a weight with a decaying
+    spectrum, as pretrained weights have, unlike i.i.d. normal ones)."""
+    rng = np.random.default_rng(seed)
+    U = rng.standard_normal((d, rank))
+    V = rng.standard_normal((k, rank))
+    U /= np.linalg.norm(U, axis=0)
+    V /= np.linalg.norm(V, axis=0)
+    sv = scale * (1.0 - np.arange(rank) / (2.0 * rank))
+    x = (U * sv) @ V.T + noise * rng.standard_normal((d, k))
+    return _round_to_bf16_bits(x.astype(np.float32)).reshape(d, k)
+
+
 def zeros_bf16(shape) -> np.ndarray:
     return np.zeros(shape, dtype=np.uint16)
 

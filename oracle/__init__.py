@@ -19,6 +19,9 @@ Modules
                  optimiser's update), elementwise float32 in a stated order.
 ``oracle.dropout`` LoRA dropout on the adapter input: Philox4x32-10 keep
                  mask and the float64 forward/backward with the mask.
+``oracle.loftq`` LoftQ initialisation: randomized rank-r SVD (float64,
+                 numpy QR/SVD as steps), LoRA factors, the float32 residual
+                 W - s B A rounded to bf16, and the alternation with NF4.
 
 Every function cites the page passage it follows. A page is cited by its
 title and section, e.g. "QLoRA glossary (Ultralytics), 'QLoRA 的工作原理'".
