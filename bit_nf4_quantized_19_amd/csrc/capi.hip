@@ -173,6 +173,11 @@ size_t qlora_workspace_bytes(int32_t op, int64_t d, int64_t k, int64_t M, int32_
                              int32_t double_quant) {
   if (check_weight_shape(d, k) != QLORA_OK) return (size_t)-1;
   if (op == QLORA_OP_QUANTIZE) return quantize_ws_bytes(d * k, double_quant);
+  if (op == QLORA_OP_QUANTIZE_RESIDUAL || op == QLORA_OP_LOFTQ) {
+    if (r < 1 || r > 64) return (size_t)-1;
+    return op == QLORA_OP_LOFTQ ? loftq_ws_bytes(d, k, r, double_quant)
+                                : residual_quantize_ws_bytes(d, k, double_quant);
+  }
   if (M < 1 || r < 1 || r > 128) return (size_t)-1;
   if (op == QLORA_OP_FWD) return (size_t)fwd_layout(nullptr, &d, 1, k, M, r).bytes;
   if (op == QLORA_OP_FWD_MULTI) return (size_t)fwd_multi_bytes(d, k, M, r);
@@ -197,6 +202,55 @@ qlora_status qlora_nf4_quantize(const uint16_t *W0, const qlora_nf4_weight *w, v
   if (!ws_ok(ws, ws_bytes, need)) return QLORA_ERR_WORKSPACE;
   return launch_quantize(W0, n, w->codes, w->absmax, w->double_quant, w->absmax_q,
                          w->absmax_scale, w->absmax_offset, ws, (hipStream_t)stream);
+}
+
+static QuantOut quant_out(const qlora_nf4_weight *w) {
+  return QuantOut{w->codes, w->absmax, w->absmax_q, w->absmax_scale, w->absmax_offset,
+                  scale_src(w)};
+}
+
+// shared checks of the two LoftQ entry points
+static qlora_status check_loftq_common(const uint16_t *W, const qlora_nf4_weight *out, int32_t r,
+                                       float lora_alpha) {
+  qlora_status s = check_weight(out, true);
+  if (s != QLORA_OK) return s;
+  if (!W || !aligned16(W)) return QLORA_ERR_INVALID_ARG;
+  if (r < 1) return QLORA_ERR_INVALID_ARG;
+  if (r > 64) return QLORA_ERR_UNSUPPORTED;
+  if (!isfinite(lora_alpha)) return QLORA_ERR_INVALID_ARG;
+  return QLORA_OK;
+}
+
+qlora_status qlora_nf4_quantize_residual(const uint16_t *W, const uint16_t *A, const uint16_t *B,
+                                         int32_t r, float lora_alpha, const qlora_nf4_weight *out,
+                                         void *ws, size_t ws_bytes, void *stream) {
+  qlora_status s = check_loftq_common(W, out, r, lora_alpha);
+  if (s != QLORA_OK) return s;
+  if (!A || !B || !aligned16(A) || !aligned16(B)) return QLORA_ERR_INVALID_ARG;
+  const int64_t need = (int64_t)residual_quantize_ws_bytes(out->d, out->k, out->double_quant);
+  if (!ws_ok(ws, ws_bytes, need)) return QLORA_ERR_WORKSPACE;
+  const float sc = lora_alpha / (float)r;
+  return launch_residual_quantize_ws(W, A, B, out->d, out->k, r, sc, quant_out(out), ws,
+                                     (hipStream_t)stream);
+}
+
+qlora_status qlora_loftq_init(const uint16_t *W, const float *omega, int32_t r, float lora_alpha,
+                              int32_t iters, int32_t power_iters, const qlora_nf4_weight *out,
+                              uint16_t *A, uint16_t *B, float *sigma, void *ws, size_t ws_bytes,
+                              void *stream) {
+  qlora_status s = check_loftq_common(W, out, r, lora_alpha);
+  if (s != QLORA_OK) return s;
+  if (!omega || ((uintptr_t)omega & 3u)) return QLORA_ERR_INVALID_ARG;
+  if (!A || !B || !aligned16(A) || !aligned16(B)) return QLORA_ERR_INVALID_ARG;
+  if (sigma && ((uintptr_t)sigma & 3u)) return QLORA_ERR_INVALID_ARG;
+  if (iters < 1 || iters > 64 || power_iters < 0 || power_iters > 64)
+    return QLORA_ERR_INVALID_ARG;
+  if (lora_alpha == 0.0f) return QLORA_ERR_INVALID_ARG;   // B = U sqrt(S) / s
+  const int64_t need = (int64_t)loftq_ws_bytes(out->d, out->k, r, out->double_quant);
+  if (!ws_ok(ws, ws_bytes, need)) return QLORA_ERR_WORKSPACE;
+  const float sc = lora_alpha / (float)r;
+  return launch_loftq(W, omega, out->d, out->k, r, sc, iters, power_iters, quant_out(out), A, B,
+                      sigma, ws, (hipStream_t)stream);
 }
 
 qlora_status qlora_nf4_dequantize(const qlora_nf4_weight *w, uint16_t *W_out, void *stream) {

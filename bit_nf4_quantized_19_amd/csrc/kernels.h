@@ -11,6 +11,31 @@ qlora_status launch_quantize(const uint16_t *W0, int64_t n, uint8_t *codes,
                              float *mu, void *ws, hipStream_t st);
 size_t quantize_ws_bytes(int64_t n, int dq);
 
+// Output buffers of one quantisation (the fields of qlora_nf4_weight) and
+// the same record read back as a scale source.
+struct QuantOut {
+  uint8_t *codes;
+  float *absmax;
+  int8_t *q;
+  float *s2;
+  float *mu;
+  ql::ScaleSrc sc;
+};
+
+// loftq.hip
+size_t loftq_ws_bytes(int64_t d, int64_t k, int r, int dq);
+size_t residual_quantize_ws_bytes(int64_t d, int64_t k, int dq);
+// NF4 (+DQ) of bf16(W - s B A) into qo; Wt (d x k bf16) and qws are scratch.
+qlora_status launch_residual_quantize(const uint16_t *W, const uint16_t *A, const uint16_t *B,
+                                      int64_t d, int64_t k, int r, float s, const QuantOut &qo,
+                                      uint16_t *Wt, void *qws, hipStream_t st);
+qlora_status launch_residual_quantize_ws(const uint16_t *W, const uint16_t *A, const uint16_t *B,
+                                         int64_t d, int64_t k, int r, float s, const QuantOut &qo,
+                                         void *ws, hipStream_t st);
+qlora_status launch_loftq(const uint16_t *W, const float *omega, int64_t d, int64_t k, int r,
+                          float s, int iters, int power_iters, const QuantOut &qo, uint16_t *A,
+                          uint16_t *B, float *sigma, void *ws, hipStream_t st);
+
 // dequant.hip
 qlora_status launch_dequantize(const uint8_t *codes, ql::ScaleSrc sc, int64_t n,
                                uint16_t *out, hipStream_t st);

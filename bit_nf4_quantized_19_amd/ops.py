@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
 
 QLORA_OK, QLORA_ERR_INVALID_ARG, QLORA_ERR_UNSUPPORTED, QLORA_ERR_WORKSPACE, QLORA_ERR_HIP = (
     0, -1, -2, -3, -4)
-OP_QUANTIZE, OP_FWD, OP_BWD, OP_FWD_MULTI = 0, 1, 2, 3
+OP_QUANTIZE, OP_FWD, OP_BWD, OP_FWD_MULTI, OP_QUANTIZE_RESIDUAL, OP_LOFTQ = 0, 1, 2, 3, 4, 5
 
 
 class QLoRAError(RuntimeError):
@@ -62,6 +62,10 @@ SIGNATURES = {
     "qlora_linear_fwd_multi": (ctypes.c_int, [_vp, _i32, _vp, _i64, _vp, _vp, _i32, _f32, _vp,
                                               _vp, _vp, _sz, _vp]),
     "qlora_merge": (ctypes.c_int, [_PW, _vp, _vp, _i32, _f32, _vp, _vp]),
+    "qlora_nf4_quantize_residual": (ctypes.c_int, [_vp, _vp, _vp, _i32, _f32, _PW, _vp, _sz,
+                                                   _vp]),
+    "qlora_loftq_init": (ctypes.c_int, [_vp, _vp, _i32, _f32, _i32, _i32, _PW, _vp, _vp, _vp,
+                                        _vp, _sz, _vp]),
     "qlora_nf4_storage_bytes": (_sz, [_i64, _i64, _i32]),
     "qlora_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64, _i32, _i32]),
     "qlora_nf4_codebook": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float),
@@ -78,7 +82,7 @@ SIGNATURES = {
 #: kernel ids of the timing hooks (QLORA_K_* in the header)
 KERNELS = ["quantize", "double_quant", "dequantize", "gemm_fwd", "gemm_dx", "gemv",
            "gemv_epilogue", "lora_down", "lora_reduce", "lora_colacc", "lora_colacc_reduce",
-           "merge", "layout", "adamw"]
+           "merge", "layout", "adamw", "loftq_product", "loftq_small", "residual"]
 
 
 def lib() -> ctypes.CDLL:
@@ -193,6 +197,50 @@ def quantize(W0: torch.Tensor, double_quant: bool = True, out: NF4Weight | None 
     _check(lib().qlora_nf4_quantize(W0.data_ptr(), ctypes.byref(cw), _ptr(wst), wsn,
                                     _stream(stream)), "qlora_nf4_quantize")
     return w
+
+
+def quantize_residual(W: torch.Tensor, A: torch.Tensor, B: torch.Tensor, lora_alpha: float,
+                      double_quant: bool = True, out: NF4Weight | None = None,
+                      ws: torch.Tensor | None = None, stream=None) -> NF4Weight:
+    """NF4 (+DQ) of bf16(W - (alpha/r) B A): the base of one LoftQ step."""
+    for t, nm in ((W, "W"), (A, "A"), (B, "B")):
+        _dev_bf16(t, nm)
+    d, k = W.shape
+    r = A.shape[0]
+    w = out if out is not None else NF4Weight.empty(d, k, double_quant, W.device)
+    wsb = workspace_bytes(OP_QUANTIZE_RESIDUAL, d, k, 0, r, double_quant)
+    wst, wsn = _workspace(wsb, W.device, ws)
+    cw = w.c_struct()
+    _check(lib().qlora_nf4_quantize_residual(W.data_ptr(), A.data_ptr(), B.data_ptr(), r,
+                                             float(lora_alpha), ctypes.byref(cw), _ptr(wst), wsn,
+                                             _stream(stream)), "qlora_nf4_quantize_residual")
+    return w
+
+
+def loftq_init(W: torch.Tensor, omega: torch.Tensor, lora_alpha: float, iters: int = 1,
+               power_iters: int = 4, double_quant: bool = True, ws: torch.Tensor | None = None,
+               stream=None):
+    """LoftQ: returns (NF4Weight, A (r x k bf16), B (d x r bf16), sigma (r fp32)).
+    ``omega`` is the k x r float32 Gaussian test matrix (its column count is r)."""
+    _dev_bf16(W, "W")
+    if omega.dtype != torch.float32 or not omega.is_cuda or not omega.is_contiguous():
+        raise ValueError("omega must be a contiguous float32 CUDA tensor")
+    d, k = W.shape
+    if omega.dim() != 2 or omega.shape[0] != k:
+        raise ValueError("omega must be k x r")
+    r = omega.shape[1]
+    w = NF4Weight.empty(d, k, double_quant, W.device)
+    A = torch.empty(r, k, dtype=torch.bfloat16, device=W.device)
+    B = torch.empty(d, r, dtype=torch.bfloat16, device=W.device)
+    sigma = torch.empty(r, dtype=torch.float32, device=W.device)
+    wsb = workspace_bytes(OP_LOFTQ, d, k, 0, r, double_quant)
+    wst, wsn = _workspace(wsb, W.device, ws)
+    cw = w.c_struct()
+    _check(lib().qlora_loftq_init(W.data_ptr(), omega.data_ptr(), r, float(lora_alpha), int(iters),
+                                  int(power_iters), ctypes.byref(cw), A.data_ptr(), B.data_ptr(),
+                                  sigma.data_ptr(), _ptr(wst), wsn, _stream(stream)),
+           "qlora_loftq_init")
+    return w, A, B, sigma
 
 
 def dequantize(w: NF4Weight, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

@@ -78,8 +78,10 @@ typedef struct qlora_nf4_weight {
 } qlora_nf4_weight;
 
 /* Operation ids for qlora_workspace_bytes. For QLORA_OP_FWD_MULTI pass the
- * sum of the weights' d as `d`. */
-enum { QLORA_OP_QUANTIZE = 0, QLORA_OP_FWD = 1, QLORA_OP_BWD = 2, QLORA_OP_FWD_MULTI = 3 };
+ * sum of the weights' d as `d`; QLORA_OP_QUANTIZE_RESIDUAL and QLORA_OP_LOFTQ
+ * take r and ignore M. */
+enum { QLORA_OP_QUANTIZE = 0, QLORA_OP_FWD = 1, QLORA_OP_BWD = 2, QLORA_OP_FWD_MULTI = 3,
+       QLORA_OP_QUANTIZE_RESIDUAL = 4, QLORA_OP_LOFTQ = 5 };
 
 /*
  * Quantise a bf16 weight W0 (d x k) into `w` (all of w's pointers are
@@ -250,6 +252,49 @@ qlora_status qlora_adamw_step(float *param, float *exp_avg, float *exp_avg_sq,
                               const uint16_t *grad, uint16_t *param_bf16, int64_t n,
                               const qlora_adamw_hparams *hp, int64_t step, void *stream);
 
+/*
+ * LoftQ initialisation (LLM-train tutorial ch. 3, jwzheng96.github.io,
+ * section 3.10: factor the gap between the 16-bit weight and its 4-bit base
+ * into the LoRA branch, alternating an SVD with the quantisation).
+ *
+ * qlora_nf4_quantize_residual: quantise bf16(W - s B A) into `out` exactly as
+ * qlora_nf4_quantize would quantise that bf16 matrix (the base of one LoftQ
+ * step). Per element, in float32: acc = 0; acc = fma(B[i][j], A[j][c], acc)
+ * for j = 0..r-1 in order (each product is exact); t = fl(s * acc);
+ * W~ = bf16_rne(fl(W - t)); s = fl32(lora_alpha / r).
+ * W: d x k bf16, A: r x k bf16, B: d x r bf16 (row-major, 16-byte aligned),
+ * 1 <= r <= 64. `out` as for qlora_nf4_quantize (its pointers are outputs).
+ * Workspace: qlora_workspace_bytes(QLORA_OP_QUANTIZE_RESIDUAL, d, k, 0, r, dq).
+ *
+ * qlora_loftq_init: `iters` (>= 1) alternations, t = 1..iters:
+ *   R = fl32(W - W'_{t-1}) with W'_0 = 0 (the first SVD is of W itself);
+ *   a rank-r SVD R ~ U S V^T by randomized subspace iteration (Halko,
+ *   Martinsson, Tropp 2011): Y = R Omega, Q = orth(Y), then `power_iters`
+ *   times Z = orth(R^T Q), Q = orth(R Z); finally the SVD of Q^T R; every
+ *   orth is CholeskyQR twice (float64 Gram), the products accumulate in
+ *   float32, the small SVD is a float64 Jacobi eigen-decomposition;
+ *   A = bf16(sqrt(S) V^T), B = bf16(U sqrt(S) / s), so s B A ~ U S V^T;
+ *   out = NF4 of bf16(W - s B A) (as qlora_nf4_quantize_residual), W'_t its
+ *   dequantised weight.
+ * omega: k x r float32 test matrix (row-major; the caller draws it, e.g.
+ * standard normal), read-only. A (r x k), B (d x r): bf16 outputs; sigma:
+ * r float32 singular values of the last SVD (descending), may be NULL.
+ * Directions with sigma below 1e-12 sigma_0 (a rank-deficient R) give zero
+ * rows of A and zero columns of B. 1 <= r <= 64, 0 <= power_iters <= 64,
+ * 1 <= iters <= 64. Workspace: qlora_workspace_bytes(QLORA_OP_LOFTQ, d, k,
+ * 0, r, dq) bytes (about 6 d k bytes plus split partial products of a few
+ * MB). All outputs are written
+ * on `stream`; results are deterministic.
+ */
+qlora_status qlora_nf4_quantize_residual(const uint16_t *W, const uint16_t *A,
+                                         const uint16_t *B, int32_t r, float lora_alpha,
+                                         const qlora_nf4_weight *out, void *ws,
+                                         size_t ws_bytes, void *stream);
+qlora_status qlora_loftq_init(const uint16_t *W, const float *omega, int32_t r,
+                              float lora_alpha, int32_t iters, int32_t power_iters,
+                              const qlora_nf4_weight *out, uint16_t *A, uint16_t *B,
+                              float *sigma, void *ws, size_t ws_bytes, void *stream);
+
 /* Bytes of the quantised record for d x k: d*k/2 + 4*nb (no double quant)
  * or d*k/2 + nb + 4*ceil(nb/256) + 4 (double quant), nb = d*k/64.
  * Returns 0 for an unsupported shape. */
@@ -284,7 +329,8 @@ enum {
   QLORA_K_GEMM_FWD = 3, QLORA_K_GEMM_DX = 4, QLORA_K_GEMV = 5, QLORA_K_GEMV_EPILOGUE = 6,
   QLORA_K_LORA_DOWN = 7, QLORA_K_LORA_REDUCE = 8, QLORA_K_LORA_COLACC = 9,
   QLORA_K_LORA_COLACC_REDUCE = 10, QLORA_K_MERGE = 11, QLORA_K_LAYOUT = 12,
-  QLORA_K_ADAMW = 13, QLORA_K_COUNT = 14
+  QLORA_K_ADAMW = 13, QLORA_K_LOFTQ_PRODUCT = 14, QLORA_K_LOFTQ_SMALL = 15,
+  QLORA_K_RESIDUAL = 16, QLORA_K_COUNT = 17
 };
 qlora_status qlora_profile_begin(int32_t cap, uint32_t mask);
 qlora_status qlora_profile_end(void);

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     ops = _ops()
     L = ops.lib()
     names = _declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for name in names:
         assert hasattr(L, name), name
         assert name in ops.SIGNATURES, name
@@ -151,6 +151,23 @@ def bx(name, rate):
     dr = DR(rate, 0, 7)
     out[name] = L.qlora_linear_bwd_ex(ctypes.byref(w), P, 16, P, P, 8, 16.0, ctypes.addressof(dr),
                                       P, None, P, P, P, P, 1 << 30, None)
+def lq(name, **kw):
+    a = dict(W=P, om=P, r=16, alpha=32.0, it=1, pit=2, A=P, B=P, sg=P, ws=P, wsb=1 << 34)
+    a.update(kw)
+    out[name] = L.qlora_loftq_init(a["W"], a["om"], a["r"], a["alpha"], a["it"], a["pit"],
+                                   ctypes.byref(w), a["A"], a["B"], a["sg"], a["ws"], a["wsb"],
+                                   None)
+lq("loftq_r0", r=0)
+lq("loftq_r65", r=65)
+lq("loftq_iters0", it=0)
+lq("loftq_neg_power", pit=-1)
+lq("loftq_null_omega", om=None)
+lq("loftq_alpha0", alpha=0.0)
+lq("loftq_ws_small", wsb=1024)
+out["resq_null_A"] = L.qlora_nf4_quantize_residual(P, None, P, 8, 16.0, ctypes.byref(w), P,
+                                                   1 << 34, None)
+out["resq_r65"] = L.qlora_nf4_quantize_residual(P, P, P, 65, 16.0, ctypes.byref(w), P, 1 << 34,
+                                                None)
 fx("fwd_drop_one", 1.0)
 fx("fwd_drop_neg", -0.25)
 fx("fwd_drop_nan", float("nan"))
@@ -189,7 +206,9 @@ EXPECTED = {
     "fwd_inf_alpha": -1, "fwd_M0": -1, "fwd_null_X": -1, "fwd_misaligned_B": -1,
     "fwd_ws_small": -3, "bwd_null_dY": -1, "bwd_null_dA": -1, "bwd_ws_small": -3,
     "bwd_r0": -1, "fwd_drop_one": -1, "fwd_drop_neg": -1, "fwd_drop_nan": -1,
-    "bwd_drop_one": -1, "bwd_drop_inf": -1, "merge_null_out": -1, "merge_r_big": -2, "deq_null_out": -1,
+    "bwd_drop_one": -1, "bwd_drop_inf": -1, "loftq_r0": -1, "loftq_r65": -2,
+    "loftq_iters0": -1, "loftq_neg_power": -1, "loftq_null_omega": -1, "loftq_alpha0": -1,
+    "loftq_ws_small": -3, "resq_null_A": -1, "resq_r65": -2, "merge_null_out": -1, "merge_r_big": -2, "deq_null_out": -1,
     "codebook_null": -1, "adam_null_param": -1, "adam_null_grad": -1, "adam_n0": -1,
     "adam_step0": -1, "adam_misaligned_m": -1, "adam_misaligned_out": -1,
     "adam_beta1_one": -1, "adam_neg_lr": -1, "adam_nan_eps": -1, "adam_unknown_pointer": -1,
