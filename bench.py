@@ -409,6 +409,28 @@ def measure_rows(ops, synth, torch, dev):
                               **_row(hbytes, _rotated(fh, 1, 10), _kernel_us(ops, "adamw", fh, 1, 10))}
     del st, sth, ga, oa
     torch.cuda.empty_cache()
+    # LoftQ initialisation of one 4096x4096 weight, r = 16, four power
+    # iterations per SVD: one alternation and five; the products with the
+    # float32 residual (read 4dk bytes per launch) dominate
+    Wl = synth.normal_bf16_device((D, K), 0.02, 71, device=dev)
+    oml = torch.from_numpy(synth.normal_f32((K, R), 72)).to(dev)
+    wsl = torch.empty(ops.workspace_bytes(ops.OP_LOFTQ, D, K, 0, R, True) + 256,
+                      dtype=torch.uint8, device=dev)
+    wsl = wsl[(-wsl.data_ptr()) % 256:]
+    f1 = lambda i: ops.loftq_init(Wl, oml, ALPHA, 1, 4, True, ws=wsl)
+    f5 = lambda i: ops.loftq_init(Wl, oml, ALPHA, 5, 4, True, ws=wsl)
+    ms1, ms5 = _rotated(f1, 1, 5), _rotated(f5, 1, 2)
+    prod_us = _kernel_us(ops, "loftq_product", f1, 1, 2)
+    rbytes = 4 * D * K
+    out["loftq_init"] = {"shape": [D, K], "r": R, "power_iters": 4,
+                         "ms_1_alternation": round(ms1, 3), "ms_5_alternations": round(ms5, 3),
+                         "product_kernel_us": round(prod_us, 2),
+                         "product_GB_s": round(rbytes / (prod_us * 1e-6) / 1e9, 1),
+                         "product_frac_hbm": round(rbytes / (prod_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                         "residual_kernel_us": round(_kernel_us(ops, "residual", f1, 1, 2), 2),
+                         "small_kernels_us": round(_kernel_us(ops, "loftq_small", f1, 1, 2), 2)}
+    del Wl, wsl
+    torch.cuda.empty_cache()
     log(f"[bench] rows: {json.dumps(out)}")
     return out
 

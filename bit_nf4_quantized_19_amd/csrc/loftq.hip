@@ -14,13 +14,15 @@
 // Kernels:
 //   mul_right  Y_part = R[:, chunk] Z[chunk, :]   (fp32 MFMA 16x16x4, split over k)
 //   mul_left   Z_part = R[chunk, :]^T Y[chunk, :] (fp32 MFMA 16x16x4, split over d)
-//   reduce     sum of the split partials in a fixed order
-//   gram       float64 partial Gram matrices Y^T Y over 256-row chunks
-//   chol       one wave: Cholesky of the Gram matrix (float64) and L^{-T}
-//              (CholeskyQR; run twice per orthonormalisation)
-//   eig        one wave: cyclic Jacobi on (Q^T R)(Q^T R)^T (float64) giving
-//              the small SVD; writes the p x p maps to A^T and B
-//   apply      row-wise product with a p x p matrix (fp32 out, or bf16 A^T / B)
+//   reduce_gram  sum of the split partials in a fixed order, with the
+//              float64 partial Gram matrices Y^T Y of 256-row chunks
+//   orth_apply CholeskyQR: every workgroup factors the summed Gram matrix in
+//              one wave (float64, registers) and applies L^{-T} to its rows,
+//              optionally with the partial Gram matrices of its output (run
+//              twice per orthonormalisation: CholeskyQR2)
+//   eig        one wave: Jacobi (round-robin, float64) on (Q^T R)(Q^T R)^T
+//              giving the small SVD; writes the p x p maps to A^T and B
+//   apply      row-wise product with a p x p matrix (bf16 A^T / B)
 //   residual_f32, residual_bf16, pad: elementwise.
 // Every kernel is deterministic (fixed summation orders, no atomics).
 
@@ -122,19 +124,23 @@ __global__ __launch_bounds__(256) void residual_bf16_kernel(
 }
 
 // ---- products with the tall operands ----------------------------------------
+constexpr int kU = 4;   // 16-column (mul_right) or 4-row (mul_left) steps per load batch
+
 // part[ks] (d x P) = R[:, ks*kKC .. +kKC) Z[same rows of Z, :], Z k x P.
-// Wave = 16 rows of R; lane (m = l%16, q = l/16) loads R[row m][k0+4q..+3]
-// and MFMA j takes element j, pairing it with Z[k0 + 4q + j][column].
+// Workgroup = 16 rows of R; its 4 waves take the chunk's 64-column batches
+// in turn and add their sums in LDS (in wave order). Lane (m = l%16,
+// q = l/16) loads R[row m][k0+4q..+3] and MFMA j takes element j, pairing it
+// with Z[k0 + 4q + j][column]; a batch issues its kU loads before its MFMAs.
 template <int NB>
 __global__ __launch_bounds__(256) void mul_right_kernel(const float *__restrict__ R, int64_t d,
                                                         int64_t k, const float *__restrict__ Z,
                                                         float *__restrict__ part) {
   constexpr int P = 16 * NB;
+  __shared__ f32x4 red[4][NB][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t i0 = ((int64_t)blockIdx.x * 4 + wave) * 16;
-  if (i0 >= d) return;
+  const int64_t i0 = (int64_t)blockIdx.x * 16;
   const int64_t kb = (int64_t)blockIdx.y * kKC;
-  const int64_t ke = kb + kKC < k ? kb + kKC : k;
+  const int64_t ke = kb + kKC < k ? kb + kKC : k;   // ke - kb: a multiple of 64 = 16 kU
   const int m = lane & 15, q = lane >> 4;
   const int64_t row = i0 + m < d ? i0 + m : d - 1;
   const float *Rp = R + row * k + 4 * q;
@@ -142,40 +148,53 @@ __global__ __launch_bounds__(256) void mul_right_kernel(const float *__restrict_
   f32x4 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int64_t k0 = kb; k0 < ke; k0 += 16) {
-    const f32x4 a = *(const f32x4 *)(Rp + k0);
-    float b[4][NB];
+  for (int64_t k0 = kb + 16 * kU * wave; k0 < ke; k0 += 4 * 16 * kU) {
+    f32x4 a[kU];
+    float b[kU][4][NB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int u = 0; u < kU; ++u) a[u] = *(const f32x4 *)(Rp + k0 + 16 * u);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) b[j][nb] = Zp[(k0 + j) * P + nb * 16];
+    for (int u = 0; u < kU; ++u)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_f32(a[j], b[j][nb], acc[nb]);
+        for (int nb = 0; nb < NB; ++nb) b[u][j][nb] = Zp[(k0 + 16 * u + j) * P + nb * 16];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_f32(a[u][j], b[u][j][nb], acc[nb]);
   }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) red[wave][nb][lane] = acc[nb];
+  __syncthreads();
+  if (wave != 0) return;
   float *out = part + (int64_t)blockIdx.y * d * P;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int nb = 0; nb < NB; ++nb) {
+    const f32x4 t = red[0][nb][lane] + red[1][nb][lane] + red[2][nb][lane] + red[3][nb][lane];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t ro = i0 + 4 * q + v;
-      if (ro < d) out[ro * P + nb * 16 + m] = acc[nb][v];
+      if (ro < d) out[ro * P + nb * 16 + m] = t[v];
     }
+  }
 }
 
 // part[ds] (k x P) = R[ds*kDC .. +kDC, :]^T Y[same rows, :], Y d x P.
-// Wave = 64 columns of R; lane (m, q) loads R[r0 + q][c0 + 4m..+3]; MFMA j
-// covers the 16 columns c0 + 4m' + j (m' = 0..15), paired with Y[r0 + q][:].
+// Workgroup = 64 columns of R; its 4 waves take the chunk's 16-row batches
+// in turn and add their sums in LDS (in wave order). Lane (m, q) loads
+// R[r0 + q][c0 + 4m..+3]; MFMA j covers the 16 columns c0 + 4m' + j
+// (m' = 0..15), paired with Y[r0 + q][:]. Rows past the chunk read as zero.
 template <int NB>
 __global__ __launch_bounds__(256) void mul_left_kernel(const float *__restrict__ R, int64_t d,
                                                        int64_t k, const float *__restrict__ Y,
                                                        float *__restrict__ part) {
   constexpr int P = 16 * NB;
+  __shared__ f32x4 red[4][4][NB][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t c0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
-  if (c0 >= k) return;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
   const int64_t rb = (int64_t)blockIdx.y * kDC;
   const int64_t re = rb + kDC < d ? rb + kDC : d;
   const int m = lane & 15, q = lane >> 4;
@@ -184,125 +203,214 @@ __global__ __launch_bounds__(256) void mul_left_kernel(const float *__restrict__
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int64_t r0 = rb; r0 < re; r0 += 4) {
-    const bool ok = r0 + q < re;
-    const int64_t row = ok ? r0 + q : re - 1;
-    f32x4 a = *(const f32x4 *)(R + row * k + c0 + 4 * m);
-    float y[NB];
+  for (int64_t r0 = rb + 4 * kU * wave; r0 < re; r0 += 4 * 4 * kU) {
+    f32x4 a[kU];
+    float y[kU][NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) y[nb] = Y[row * P + nb * 16 + m];
-    if (!ok) {
-      a = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < kU; ++u) {
+      const int64_t rr = r0 + 4 * u + q;
+      const int64_t row = rr < re ? rr : re - 1;
+      a[u] = *(const f32x4 *)(R + row * k + c0 + 4 * m);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) y[nb] = 0.0f;
+      for (int nb = 0; nb < NB; ++nb) y[u][nb] = Y[row * P + nb * 16 + m];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int u = 0; u < kU; ++u)
+      if (r0 + 4 * u + q >= re) {
+        a[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[j][nb] = mfma_f32(a[j], y[nb], acc[j][nb]);
+        for (int nb = 0; nb < NB; ++nb) y[u][nb] = 0.0f;
+      }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[j][nb] = mfma_f32(a[u][j], y[u][nb], acc[j][nb]);
   }
-  float *out = part + (int64_t)blockIdx.y * k * P;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb) red[wave][j][nb][lane] = acc[j][nb];
+  __syncthreads();
+  // wave w writes the outputs of MFMA j = w
+  const int j = wave;
+  float *out = part + (int64_t)blockIdx.y * k * P;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        out[(c0 + 4 * (4 * q + v) + j) * P + nb * 16 + m] = acc[j][nb][v];
-}
-
-// out[e] = sum over s < ns of part[s * stride + e] (in order), 4 per thread.
-__global__ __launch_bounds__(256) void reduce_kernel(const float *__restrict__ part, int ns,
-                                                     int64_t stride4, float *__restrict__ out) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= stride4) return;
-  f32x4 acc = ((const f32x4 *)part)[e];
-  for (int s = 1; s < ns; ++s) acc += ((const f32x4 *)part)[(int64_t)s * stride4 + e];
-  ((f32x4 *)out)[e] = acc;
+  for (int nb = 0; nb < NB; ++nb) {
+    const f32x4 t = red[0][j][nb][lane] + red[1][j][nb][lane] + red[2][j][nb][lane] +
+                    red[3][j][nb][lane];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) out[(c0 + 4 * (4 * q + v) + j) * P + nb * 16 + m] = t[v];
+  }
 }
 
 // ---- small dense algebra -----------------------------------------------------
-// gpart[b] (P x P, float64) = sum over rows i of chunk b of Y[i][a] Y[i][c].
+// Partial Gram matrix of the rows staged in ys (rows x P, zero past n):
+// g[a][c] = sum_i ys[i][a] ys[i][c] in float64, written to gout.
+// rows is a multiple of 4; four partial sums over rows i % 4, added in order.
 template <int P>
-__global__ __launch_bounds__(256) void gram_kernel(const float *__restrict__ Y, int64_t n,
-                                                   double *__restrict__ gpart) {
+QL_DEV void gram_rows(const float (*ys)[P], int rows, double *gout) {
+  for (int e = threadIdx.x; e < P * P; e += 256) {
+    const int a = e / P, c = e % P;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    for (int i = 0; i < rows; i += 4) {
+      s0 = fma((double)ys[i][a], (double)ys[i][c], s0);
+      s1 = fma((double)ys[i + 1][a], (double)ys[i + 1][c], s1);
+      s2 = fma((double)ys[i + 2][a], (double)ys[i + 2][c], s2);
+      s3 = fma((double)ys[i + 3][a], (double)ys[i + 3][c], s3);
+    }
+    gout[e] = (s0 + s1) + (s2 + s3);
+  }
+}
+
+// Y (n x P) = sum over s < ns of part[s] (in order), and the partial Gram
+// matrix of each 256-row chunk (gout[block], float64).
+template <int P>
+__global__ __launch_bounds__(256) void reduce_gram_kernel(const float *__restrict__ part, int ns,
+                                                          int64_t n, float *__restrict__ Y,
+                                                          double *__restrict__ gout) {
   __shared__ float ys[kGramRows][P];
   const int64_t r0 = (int64_t)blockIdx.x * kGramRows;
-  const int t = threadIdx.x;
-  for (int e = t; e < kGramRows * P / 4; e += 256) {
+  const int64_t n4 = n * P / 4;
+  for (int e = threadIdx.x; e < kGramRows * P / 4; e += 256) {
     const int row = e / (P / 4), c4 = e % (P / 4);
+    const int64_t g = (r0 + row) * (P / 4) + c4;
     f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (r0 + row < n) v = ((const f32x4 *)(Y + (r0 + row) * P))[c4];
+    if (r0 + row < n) {
+      v = ((const f32x4 *)part)[g];
+#pragma unroll 8
+      for (int s = 1; s < ns; ++s) v += ((const f32x4 *)part)[(int64_t)s * n4 + g];
+      ((f32x4 *)Y)[g] = v;
+    }
     *(f32x4 *)&ys[row][4 * c4] = v;
   }
   __syncthreads();
-  for (int e = t; e < P * P; e += 256) {
-    const int a = e / P, c = e % P;
-    double s = 0.0;
-    for (int i = 0; i < kGramRows; ++i) s = fma((double)ys[i][a], (double)ys[i][c], s);
-    gpart[(int64_t)blockIdx.x * P * P + e] = s;
-  }
+  gram_rows<P>(ys, kGramRows, gout + (int64_t)blockIdx.x * P * P);
 }
 
-// Sum of nch partial Gram matrices in chunk order.
-template <int P>
-QL_DEV void load_gram(const double *gpart, int nch, double (*G)[P]) {
-  for (int e = threadIdx.x; e < P * P; e += 64) {
-    double s = 0.0;
-    for (int c = 0; c < nch; ++c) s += gpart[(int64_t)c * P * P + e];
-    G[e / P][e % P] = s;
-  }
-  __syncthreads();
+// 1/sqrt(x) for x > 0: the hardware estimate refined by two Newton steps
+// (relative error at the float64 rounding level).
+QL_DEV double rsqrt_f64(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  y = y * fma(-0.5 * x * y, y, 1.5);
+  y = y * fma(-0.5 * x * y, y, 1.5);
+  return y;
 }
 
-// One wave: G = L L^T (float64, left-looking by columns); a pivot not above
-// 1e-12 of its diagonal entry marks a dependent column, whose L column is
-// zero (its Q column comes out zero). Writes M = L^{-T} (fp32) so that
-// Q = Y M has orthonormal columns.
+QL_DEV double bcast(double x, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// One wave (all 64 lanes active): G = sum of nch partial Gram matrices
+// (float64), G = L L^T by columns with lane i holding row i of L in
+// registers (other rows by readlane); a pivot not above 1e-12 of its diagonal
+// entry marks a dependent column, whose L column is zero (its Q column comes
+// out zero). Lane j then computes column j of L^{-1}; Ms = L^{-T} (fp32), so
+// that Q = Y Ms has orthonormal columns.
 template <int P>
-__global__ __launch_bounds__(64) void chol_kernel(const double *__restrict__ gpart, int nch,
-                                                  float *__restrict__ M) {
-  __shared__ double G[P][P];
-  __shared__ double L[P][P];
-  __shared__ double piv;
-  const int lane = threadIdx.x;
-  load_gram<P>(gpart, nch, G);
-  for (int e = lane; e < P * P; e += 64) L[e / P][e % P] = 0.0;
-  __syncthreads();
+QL_DEV void chol_wave(const double *__restrict__ gin, int nch, float (*Ms)[P]) {
+  const int lane = threadIdx.x & 63;
+  double L[P];
+#pragma unroll
+  for (int c = 0; c < P; ++c) L[c] = 0.0;
+  constexpr int kUB = P <= 16 ? 4 : (P <= 32 ? 2 : 1);   // partial matrices per load batch
+  if (lane < P)
+#pragma unroll kUB
+    for (int b = 0; b < nch; ++b) {
+      const double *g = gin + (int64_t)b * P * P + lane * P;
+#pragma unroll
+      for (int c = 0; c < P; ++c) L[c] += g[c];
+    }
+  // L[c] holds G[lane][c] until column c is computed; ri[j] = 1 / L[j][j]
+  // (0 for a dependent column)
+  double ri[P];
+#pragma unroll
   for (int j = 0; j < P; ++j) {
-    double v = 0.0;
-    if (lane < P && lane >= j) {
-      v = G[lane][j];
-      for (int t = 0; t < j; ++t) v -= L[lane][t] * L[j][t];
-    }
-    if (lane == j) piv = v;
-    __syncthreads();
-    const double pj = piv;
-    const bool dead = !(pj > 1e-12 * G[j][j]);
-    if (lane < P && lane >= j) L[lane][j] = dead ? 0.0 : v / sqrt(pj);
-    __syncthreads();
+    double v = L[j];
+#pragma unroll
+    for (int t = 0; t < j; ++t) v = fma(-L[t], bcast(L[t], j), v);
+    const double piv = bcast(v, j);
+    const double gjj = bcast(L[j], j);
+    const bool dead = !(piv > 1e-12 * gjj);
+    const double rs = dead ? 0.0 : rsqrt_f64(piv);
+    ri[j] = rs;
+    L[j] = lane >= j ? v * rs : 0.0;
   }
-  // column j of L^{-1} by forward substitution (lane j); stored in G
-  if (lane < P) {
-    const int j = lane;
-    for (int i = 0; i < P; ++i) {
-      double x = 0.0;
-      if (i >= j) {
-        double s = (i == j) ? 1.0 : 0.0;
-        for (int t = j; t < i; ++t) s -= L[i][t] * G[t][j];
-        x = L[i][i] != 0.0 ? s / L[i][i] : 0.0;
-      }
-      G[i][j] = x;
-    }
+  double x[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    double s = (lane == i) ? 1.0 : 0.0;
+#pragma unroll
+    for (int t = 0; t < i; ++t) s = fma(-bcast(L[t], i), x[t], s);
+    x[i] = s * ri[i];
   }
+  if (lane < P)
+#pragma unroll
+    for (int c = 0; c < P; ++c) Ms[lane][c] = (float)x[c];   // Ms[a][c] = Linv[c][a]
+}
+
+// Q = Y L^{-T} with L from the partial Gram matrices gin (each workgroup
+// recomputes the P x P factor in its first wave); with GRAM the partial Gram
+// matrix of the workgroup's output rows goes to gout[block]. A thread owns
+// one row and one 16-column block; a workgroup orth_rows(NB) rows (a multiple
+// of 4 with rows x NB <= 256; the other threads only take part in the
+// barriers and the Gram sums).
+constexpr int orth_rows(int nb) { return nb == 1 ? 256 : (nb == 2 ? 128 : 64); }
+template <int P, bool GRAM>
+__global__ __launch_bounds__(256) void orth_apply_kernel(const float *__restrict__ In, int64_t n,
+                                                         const double *__restrict__ gin, int nch,
+                                                         float *__restrict__ Out,
+                                                         double *__restrict__ gout) {
+  constexpr int NB = P / 16, RPB = orth_rows(NB);
+  static_assert(RPB % 4 == 0 && RPB * NB <= 256, "rows per workgroup");
+  __shared__ float Ms[P][P];
+  __shared__ float ys[GRAM ? RPB : 1][P];
+  if (threadIdx.x < 64) chol_wave<P>(gin, nch, Ms);
   __syncthreads();
-  for (int e = lane; e < P * P; e += 64) M[e] = (float)G[e % P][e / P];   // M[a][c] = Linv[c][a]
+  const int lr = threadIdx.x / NB, cb = threadIdx.x % NB;
+  const bool own = lr < RPB;
+  const int64_t i = (int64_t)blockIdx.x * RPB + lr;
+  float o[16];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) o[jj] = 0.0f;
+  if (own && i < n) {
+    float x[P];
+#pragma unroll
+    for (int a4 = 0; a4 < P / 4; ++a4) {
+      const f32x4 v = ((const f32x4 *)(In + i * P))[a4];
+      x[4 * a4] = v[0]; x[4 * a4 + 1] = v[1]; x[4 * a4 + 2] = v[2]; x[4 * a4 + 3] = v[3];
+    }
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int a = 0; a < P; ++a) acc = __builtin_fmaf(x[a], Ms[a][cb * 16 + jj], acc);
+      o[jj] = acc;
+    }
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4)
+      ((f32x4 *)(Out + i * P + cb * 16))[j4] =
+          f32x4{o[4 * j4], o[4 * j4 + 1], o[4 * j4 + 2], o[4 * j4 + 3]};
+  }
+  if (GRAM) {
+    if (own)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) ys[lr][cb * 16 + jj] = o[jj];
+    __syncthreads();
+    gram_rows<P>(ys, RPB, gout + (int64_t)blockIdx.x * P * P);
+  }
 }
 
 // One wave: eigen-decomposition of the symmetric P x P matrix C C^T (sum of
-// the partial Gram matrices of Z = R^T Q, so C = Q^T R) by cyclic Jacobi in
-// float64; eigenvalues sorted descending, sigma_j = sqrt(lambda_j). Writes
+// the partial Gram matrices of Z = R^T Q, so C = Q^T R) by Jacobi in float64
+// with the round-robin ordering: each of the P-1 steps of a sweep applies
+// P/2 disjoint rotations at once (their angles from the matrix at the start
+// of the step, which is exact since they touch disjoint rows and columns).
+// Eigenvalues sorted descending, sigma_j = sqrt(lambda_j). Writes
 // MA = U_c diag(sigma^{-1/2}) (A^T = Z MA) and MB = U_c diag(sigma^{1/2}) / s
 // (B = Q MB); directions with lambda_j <= 1e-24 lambda_0 get zero columns.
 template <int P>
@@ -310,63 +418,107 @@ __global__ __launch_bounds__(64) void eig_kernel(const double *__restrict__ gpar
                                                  int r, float s, float *__restrict__ MA,
                                                  float *__restrict__ MB,
                                                  float *__restrict__ sigma) {
-  __shared__ double Am[P][P];
-  __shared__ double V[P][P];
+  constexpr int G = 64 / P;          // lane groups sharing the pairs of a step
+  constexpr int PPL = P / 2 / G;     // pairs per lane
+  __shared__ double Am[P][P + 1];
+  __shared__ double V[P][P + 1];
+  __shared__ double rc[P / 2], rs[P / 2];
+  __shared__ int rp[P / 2], rq[P / 2];
+  __shared__ double offp[P], dgp[P];
   __shared__ int order[P];
-  __shared__ int used[P];
-  __shared__ int done;
   const int lane = threadIdx.x;
-  load_gram<P>(gpart, nch, Am);
-  for (int e = lane; e < P * P; e += 64) V[e / P][e % P] = (e / P == e % P) ? 1.0 : 0.0;
+  for (int e = lane; e < P * P; e += 64) {
+    double sum = 0.0;
+#pragma unroll 8
+    for (int b = 0; b < nch; ++b) sum += gpart[(int64_t)b * P * P + e];
+    Am[e / P][e % P] = sum;
+    V[e / P][e % P] = (e / P == e % P) ? 1.0 : 0.0;
+  }
   __syncthreads();
+  const int row = lane % P, grp = lane / P;
   for (int sweep = 0; sweep < 60; ++sweep) {
-    if (lane == 0) {
-      double off = 0.0, dg = 0.0;
-      for (int p = 0; p < P; ++p)
-        for (int c = 0; c < P; ++c) {
-          const double x = Am[p][c] * Am[p][c];
-          if (p == c) dg += x; else off += x;
-        }
-      done = !(off > 1e-30 * dg);
+    if (lane < P) {   // squares of row `lane`, off the diagonal and on it
+      double off = 0.0;
+#pragma unroll
+      for (int c = 0; c < P; ++c) off += (c == lane) ? 0.0 : Am[lane][c] * Am[lane][c];
+      offp[lane] = off;
+      dgp[lane] = Am[lane][lane] * Am[lane][lane];
     }
     __syncthreads();
-    if (done) break;
-    for (int p = 0; p < P - 1; ++p)
-      for (int q = p + 1; q < P; ++q) {
-        const double apq = Am[p][q], app = Am[p][p], aqq = Am[q][q];
-        __syncthreads();
-        if (apq == 0.0) continue;
-        const double tau = (aqq - app) / (2.0 * apq);
-        const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
-        const double c = 1.0 / sqrt(1.0 + t * t), sn = t * c;
-        if (lane < P) {
-          const double tp = Am[lane][p], tq = Am[lane][q];
-          Am[lane][p] = c * tp - sn * tq;
-          Am[lane][q] = sn * tp + c * tq;
-          const double vp = V[lane][p], vq = V[lane][q];
-          V[lane][p] = c * vp - sn * vq;
-          V[lane][q] = sn * vp + c * vq;
+    double off = 0.0, dg = 0.0;
+#pragma unroll
+    for (int c = 0; c < P; ++c) { off += offp[c]; dg += dgp[c]; }
+    if (!(off > 1e-30 * dg)) break;   // uniform: every lane sums the same values
+    for (int step = 0; step < P - 1; ++step) {
+      if (lane < P / 2) {
+        // circle method: player 0 meets 1 + step; the others pair around it
+        int p, q;
+        if (lane == 0) {
+          p = 0;
+          q = 1 + step;
+        } else {
+          p = 1 + (step + lane) % (P - 1);
+          q = 1 + (step + P - 1 - lane) % (P - 1);
         }
-        __syncthreads();
-        if (lane < P) {
-          const double tp = Am[p][lane], tq = Am[q][lane];
-          Am[p][lane] = c * tp - sn * tq;
-          Am[q][lane] = sn * tp + c * tq;
+        if (p > q) { const int t = p; p = q; q = t; }
+        const double apq = Am[p][q], dd = Am[q][q] - Am[p][p];
+        double c = 1.0, sn = 0.0;
+        if (apq != 0.0) {
+          // t = tan(theta) of the rotation that zeroes A[p][q] (smaller root)
+          const double t = (dd >= 0.0 ? 2.0 * apq : -2.0 * apq) /
+                           (fabs(dd) + sqrt(fma(dd, dd, 4.0 * apq * apq)));
+          c = rsqrt_f64(fma(t, t, 1.0));
+          sn = t * c;
         }
-        __syncthreads();
+        rp[lane] = p; rq[lane] = q; rc[lane] = c; rs[lane] = sn;
       }
-  }
-  if (lane < P) used[lane] = 0;
-  __syncthreads();
-  if (lane == 0) {
-    // selection order by descending eigenvalue (lower index first on ties)
-    for (int j = 0; j < P; ++j) {
-      int best = -1;
-      for (int c = 0; c < P; ++c)
-        if (!used[c] && (best < 0 || Am[c][c] > Am[best][best])) best = c;
-      used[best] = 1;
-      order[j] = best;
+      __syncthreads();
+      if (grp < G) {   // A <- A J and V <- V J: row `row`, columns p, q of this lane's pairs
+        double ap[PPL], aq[PPL], vp[PPL], vq[PPL];
+#pragma unroll
+        for (int h = 0; h < PPL; ++h) {
+          const int hh = grp * PPL + h;
+          ap[h] = Am[row][rp[hh]]; aq[h] = Am[row][rq[hh]];
+          vp[h] = V[row][rp[hh]]; vq[h] = V[row][rq[hh]];
+        }
+#pragma unroll
+        for (int h = 0; h < PPL; ++h) {
+          const int hh = grp * PPL + h;
+          const double c = rc[hh], sn = rs[hh];
+          Am[row][rp[hh]] = c * ap[h] - sn * aq[h];
+          Am[row][rq[hh]] = sn * ap[h] + c * aq[h];
+          V[row][rp[hh]] = c * vp[h] - sn * vq[h];
+          V[row][rq[hh]] = sn * vp[h] + c * vq[h];
+        }
+      }
+      __syncthreads();
+      if (grp < G) {   // A <- J^T A: column `row`, rows p, q of this lane's pairs
+        double ap[PPL], aq[PPL];
+#pragma unroll
+        for (int h = 0; h < PPL; ++h) {
+          const int hh = grp * PPL + h;
+          ap[h] = Am[rp[hh]][row]; aq[h] = Am[rq[hh]][row];
+        }
+#pragma unroll
+        for (int h = 0; h < PPL; ++h) {
+          const int hh = grp * PPL + h;
+          const double c = rc[hh], sn = rs[hh];
+          Am[rp[hh]][row] = c * ap[h] - sn * aq[h];
+          Am[rq[hh]][row] = sn * ap[h] + c * aq[h];
+        }
+      }
+      __syncthreads();
     }
+  }
+  if (lane < P) {   // rank by descending eigenvalue, lower index first on ties
+    const double lj = Am[lane][lane];
+    int rank = 0;
+#pragma unroll
+    for (int c = 0; c < P; ++c) {
+      const double lc = Am[c][c];
+      rank += (lc > lj || (lc == lj && c < lane)) ? 1 : 0;
+    }
+    order[rank] = lane;
   }
   __syncthreads();
   const double lmax = Am[order[0]][order[0]];
@@ -385,13 +537,12 @@ __global__ __launch_bounds__(64) void eig_kernel(const double *__restrict__ gpar
   }
 }
 
-// out = In (n x P) M (P x P): MODE 0 fp32 n x P; MODE 1 bf16 n x r (row i,
-// column j < r); MODE 2 bf16 r x n (the transpose). Thread = one row and one
-// 16-column block.
+// out = In (n x P) M (P x P) as bf16: MODE 1 n x r (row i, column j < r);
+// MODE 2 r x n (the transpose). Thread = one row and one 16-column block.
 template <int P, int MODE>
 __global__ __launch_bounds__(256) void apply_kernel(const float *__restrict__ In, int64_t n,
                                                     const float *__restrict__ M, int r,
-                                                    void *__restrict__ out) {
+                                                    uint16_t *__restrict__ out) {
   constexpr int NB = P / 16;
   __shared__ float Ms[P][P];
   for (int e = threadIdx.x; e < P * P; e += 256) Ms[e / P][e % P] = M[e];
@@ -412,20 +563,18 @@ __global__ __launch_bounds__(256) void apply_kernel(const float *__restrict__ In
     float acc = 0.0f;
 #pragma unroll
     for (int a = 0; a < P; ++a) acc = __builtin_fmaf(x[a], Ms[a][j], acc);
-    if (MODE == 0) {
-      ((float *)out)[i * P + j] = acc;
-    } else if (j < r) {
+    if (j < r) {
       const uint16_t b = ql::f_to_bf16(acc);
-      if (MODE == 1) ((uint16_t *)out)[i * r + j] = b;
-      else ((uint16_t *)out)[(int64_t)j * n + i] = b;
+      if (MODE == 1) out[i * r + j] = b;
+      else out[(int64_t)j * n + i] = b;
     }
   }
 }
 
 // ---- host side -----------------------------------------------------------------
 struct LoftqWs {
-  float *R, *Op, *Yd, *Td, *Zk, *Tk, *part, *MA, *MB, *Mc;
-  double *gpart;
+  float *R, *Op, *Yd, *Td, *Zk, *Tk, *part, *MA, *MB;
+  double *g1, *g2;
   uint16_t *Wb;      // W~ (and the dequantised base W' before it)
   void *qws;         // quantiser workspace
   int64_t bytes;
@@ -440,9 +589,10 @@ T *carve(char *base, int64_t &off, int64_t bytes) {
 }
 
 LoftqWs loftq_layout(char *base, int64_t d, int64_t k, int r, int dq) {
-  const int64_t P = ql_rup(r, 16);
+  const int64_t P = ql_rup(r, 16), NB = P / 16;
   const int64_t ks = ql_cdiv(k, kKC), ds = ql_cdiv(d, kDC);
-  const int64_t nch = ql_cdiv(d > k ? d : k, kGramRows);
+  const int64_t nmax = d > k ? d : k;
+  const int64_t nch1 = ql_cdiv(nmax, kGramRows), nch2 = ql_cdiv(nmax, orth_rows((int)NB));
   int64_t off = 0;
   LoftqWs L{};
   L.R = carve<float>(base, off, 4 * d * k);
@@ -454,10 +604,10 @@ LoftqWs loftq_layout(char *base, int64_t d, int64_t k, int r, int dq) {
   L.Zk = carve<float>(base, off, 4 * k * P);
   L.Tk = carve<float>(base, off, 4 * k * P);
   L.part = carve<float>(base, off, 4 * P * (ks * d > ds * k ? ks * d : ds * k));
-  L.gpart = carve<double>(base, off, 8 * nch * P * P);
+  L.g1 = carve<double>(base, off, 8 * nch1 * P * P);
+  L.g2 = carve<double>(base, off, 8 * nch2 * P * P);
   L.MA = carve<float>(base, off, 4 * P * P);
   L.MB = carve<float>(base, off, 4 * P * P);
-  L.Mc = carve<float>(base, off, 4 * P * P);
   L.bytes = off;
   return L;
 }
@@ -469,52 +619,40 @@ struct Loftq {
   int64_t d, k;
   hipStream_t st;
 
+  // Y (n x P) from the split partial products, and its partial Gram matrices
+  qlora_status reduce_gram(int ns, int64_t n, float *Y) {
+    QlProf pf(QLORA_K_LOFTQ_SMALL, st);
+    reduce_gram_kernel<P><<<(unsigned)ql_cdiv(n, kGramRows), 256, 0, st>>>(L.part, ns, n, Y, L.g1);
+    QL_LAUNCH_CHECK();
+    return QLORA_OK;
+  }
   qlora_status right(const float *Z, float *Y) {   // Y (d x P) = R Z
     {
       QlProf pf(QLORA_K_LOFTQ_PRODUCT, st);
-      mul_right_kernel<NB><<<dim3((unsigned)ql_cdiv(d, 64), (unsigned)ql_cdiv(k, kKC)), 256, 0, st>>>(
+      mul_right_kernel<NB><<<dim3((unsigned)ql_cdiv(d, 16), (unsigned)ql_cdiv(k, kKC)), 256, 0, st>>>(
           L.R, d, k, Z, L.part);
     }
     QL_LAUNCH_CHECK();
-    return reduce(L.part, (int)ql_cdiv(k, kKC), d, Y);
+    return reduce_gram((int)ql_cdiv(k, kKC), d, Y);
   }
   qlora_status left(const float *Y, float *Z) {    // Z (k x P) = R^T Y
     {
       QlProf pf(QLORA_K_LOFTQ_PRODUCT, st);
-      mul_left_kernel<NB><<<dim3((unsigned)ql_cdiv(k, 256), (unsigned)ql_cdiv(d, kDC)), 256, 0, st>>>(
+      mul_left_kernel<NB><<<dim3((unsigned)(k / 64), (unsigned)ql_cdiv(d, kDC)), 256, 0, st>>>(
           L.R, d, k, Y, L.part);
     }
     QL_LAUNCH_CHECK();
-    return reduce(L.part, (int)ql_cdiv(d, kDC), k, Z);
+    return reduce_gram((int)ql_cdiv(d, kDC), k, Z);
   }
-  qlora_status reduce(const float *part, int ns, int64_t n, float *out) {
-    const int64_t n4 = n * P / 4;
-    QlProf pf(QLORA_K_LOFTQ_SMALL, st);
-    reduce_kernel<<<(unsigned)ql_cdiv(n4, 256), 256, 0, st>>>(part, ns, n4, out);
-    QL_LAUNCH_CHECK();
-    return QLORA_OK;
-  }
-  qlora_status gram(const float *Y, int64_t n) {
-    QlProf pf(QLORA_K_LOFTQ_SMALL, st);
-    gram_kernel<P><<<(unsigned)ql_cdiv(n, kGramRows), 256, 0, st>>>(Y, n, L.gpart);
-    QL_LAUNCH_CHECK();
-    return QLORA_OK;
-  }
-  // CholeskyQR2: the orthonormal basis of Y's columns ends in Y (T: scratch)
+  // CholeskyQR2 of Y (whose partial Gram matrices are in g1): the orthonormal
+  // basis ends in Y (T: scratch)
   qlora_status orth(float *Y, float *T, int64_t n) {
-    qlora_status s;
-    float *src = Y, *dst = T;
-    for (int pass = 0; pass < 2; ++pass) {
-      if ((s = gram(src, n)) != QLORA_OK) return s;
-      {
-        QlProf pf(QLORA_K_LOFTQ_SMALL, st);
-        chol_kernel<P><<<1, 64, 0, st>>>(L.gpart, (int)ql_cdiv(n, kGramRows), L.Mc);
-        QL_LAUNCH_CHECK();
-        apply_kernel<P, 0><<<(unsigned)ql_cdiv(n * NB, 256), 256, 0, st>>>(src, n, L.Mc, P, dst);
-        QL_LAUNCH_CHECK();
-      }
-      float *t = src; src = dst; dst = t;
-    }
+    const unsigned grid = (unsigned)ql_cdiv(n, orth_rows(NB));
+    QlProf pf(QLORA_K_LOFTQ_SMALL, st);
+    orth_apply_kernel<P, true><<<grid, 256, 0, st>>>(Y, n, L.g1, (int)ql_cdiv(n, kGramRows), T, L.g2);
+    QL_LAUNCH_CHECK();
+    orth_apply_kernel<P, false><<<grid, 256, 0, st>>>(T, n, L.g2, (int)grid, Y, nullptr);
+    QL_LAUNCH_CHECK();
     return QLORA_OK;
   }
   // rank-P SVD of R; writes A (r x k), B (d x r) bf16 and sigma (r)
@@ -528,10 +666,9 @@ struct Loftq {
       if ((e = right(L.Zk, L.Yd)) != QLORA_OK) return e;
       if ((e = orth(L.Yd, L.Td, d)) != QLORA_OK) return e;
     }
-    if ((e = left(L.Yd, L.Zk)) != QLORA_OK) return e;   // Z = R^T Q = C^T
-    if ((e = gram(L.Zk, k)) != QLORA_OK) return e;
+    if ((e = left(L.Yd, L.Zk)) != QLORA_OK) return e;   // Z = R^T Q = C^T, Gram C C^T in g1
     QlProf pf(QLORA_K_LOFTQ_SMALL, st);
-    eig_kernel<P><<<1, 64, 0, st>>>(L.gpart, (int)ql_cdiv(k, kGramRows), r, s, L.MA, L.MB, sigma);
+    eig_kernel<P><<<1, 64, 0, st>>>(L.g1, (int)ql_cdiv(k, kGramRows), r, s, L.MA, L.MB, sigma);
     QL_LAUNCH_CHECK();
     apply_kernel<P, 2><<<(unsigned)ql_cdiv(k * NB, 256), 256, 0, st>>>(L.Zk, k, L.MA, r, A);
     QL_LAUNCH_CHECK();

@@ -140,6 +140,14 @@ def test_alternations_match_oracle(ops, d, k, r, iters, q, dq, exact):
     assert e < np.linalg.norm(bf16_f64(W) - bf16_f64(plain))
 
 
+@pytest.mark.parametrize("d,k,r", [(320, 576, 40), (128, 256, 33)])
+def test_three_column_blocks(ops, d, k, r):
+    # r in 33..48: the factorisation runs on 48 columns
+    W = synth.normal_bf16((d, k), 0.02, 8700 + r)
+    got, want = _run(ops, W, r, 2.0 * r, 1, 3)
+    _compare(got, want, W, r, olora.lora_scale(2.0 * r, r), per_rank=False)
+
+
 def test_llama_q_proj_shape(ops):
     # 4096 x 4096, r = 16, one alternation with two power iterations
     d = k = 4096
