@@ -195,6 +195,9 @@ def main():
             "lora_colacc_us_dropout": round(_kernel_us(ops, "lora_colacc", step_drop, 4, 8), 2),
             "lora_down_us_dropout": round(_kernel_us(ops, "lora_down", step_drop, 4, 8), 2)}
         log(f"[bench] dropout row: {json.dumps(rows['lora_dropout_step'])}")
+    probes = measure_probes(torch, dev) if args.rows == "on" else None
+    if probes:
+        roofline["frac_of_measured_gemm_probe"] = round(achieved / probes["bf16_gemm_8192_TFLOP_s"], 4)
     cpu = cpu_baseline(inp, flops) if args.cpu_baseline == "on" else None
 
     line = {
@@ -210,6 +213,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "rows": rows,
+        "probes": probes,
     }
     print(json.dumps(line), flush=True)
 
@@ -435,6 +439,49 @@ def measure_rows(ops, synth, torch, dev):
     return out
 
 
+def measure_probes(torch, dev):
+    """Measured ceilings beside the published peaks: a device-to-device copy
+    streaming 2 GiB (and one of the 32 MiB a 4096x4096 bf16 weight occupies,
+    the size of the quantise / dequantise rows), and a large bf16 GEMM
+    (8192^3, the vendor library) for the matrix cores."""
+    def copy_rate(nbytes, iters):
+        src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        srcs = [src] if nbytes > (1 << 30) else \
+            [torch.empty_like(src).fill_(1.0) for _ in range(16)]   # past the 256 MB cache
+        dsts = [dst] if nbytes > (1 << 30) else [torch.empty_like(src) for _ in range(16)]
+        for i in range(3):
+            dsts[i % len(dsts)].copy_(srcs[i % len(srcs)])
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for i in range(iters):
+            dsts[i % len(dsts)].copy_(srcs[i % len(srcs)])
+        s1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * s0.elapsed_time(s1) / iters
+        return round(2 * nbytes / (us * 1e-6) / 1e9, 1)
+    out = {"hbm_copy_2GiB_GB_s": copy_rate(2 << 30, 10),
+           "hbm_copy_32MiB_GB_s": copy_rate(32 << 20, 64)}
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(10):
+        torch.matmul(a, b)
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / 10
+    out["bf16_gemm_8192_TFLOP_s"] = round(2 * 8192 ** 3 / (ms * 1e-3) / 1e12, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    log(f"[bench] probes: {json.dumps(out)}")
+    return out
+
+
 def cpu_baseline(inp, flops):
     """The CPU oracle (as it stands) on the host cores: one full step of the
     workload (oracle dequantisation of W0 plus float64 forward and backward on
@@ -461,8 +508,17 @@ def cpu_baseline(inp, flops):
         olora.backward(Wd, X, A, B, s, dY)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(flops / t / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
             "sample": "one full step of the workload (oracle dequantise + float64 forward "
                       f"and backward, 2048 tokens), median of 3 runs: {t:.2f} s"}
 
