@@ -191,7 +191,7 @@ struct Tile {
       srow = e >> 1;                      // scale entry 2r + b
       const int64_t c0 = n0 + 64 * (e & 1);
       sblk = (int)(c0 < g.k ? c0 : g.k - 64);
-      const int64_t dc = n0 + 64 * ((tid & 31) >> 4);
+      const int64_t dc = n0 + 64 * (((tid >> 1) & 31) >> 4);
       dcol = (int)(dc < g.k ? dc : g.k - 64);
     }
 #pragma unroll
@@ -263,9 +263,12 @@ struct Tile {
   // ---- decode: the codes of one step into a W' tile ----------------------
   // Forward (two parts): thread t owns code words 2(t%2), +1 of code entry
   // t/2, i.e. 16 weights of tile row t/4; part i turns one word (8 weights)
-  // into one 16-byte fragment. dX (four parts): thread (jg = t/32,
-  // kg = t%32) owns rows 4jg..4jg+3, columns 4kg..4kg+3 of the stage's codes
-  // (row r at bytes 64r..64r+63); part i writes column 4kg+i, 4 rows (8 bytes).
+  // into one 16-byte fragment. dX (four parts): thread t (jg = 2(t/64) +
+  // t%2, kg = (t/2)%32) owns rows 4jg..4jg+3, columns 4kg..4kg+3 of the
+  // stage's codes (row r at bytes 64r..64r+63); part i writes column 4kg+i,
+  // 4 rows (8 bytes). Neighbouring lanes take the two halves of one 16-byte
+  // fragment slot, so the 8-byte writes of 16 lanes fall on 16 distinct
+  // slots (the row permutation alone gives 8).
   static constexpr int kParts = MODE == 0 ? 2 : 4;
   struct DecIn {
     uint32_t c[4];   // forward: 2 code words; dX: 4 rows' 2-byte code pairs
@@ -281,14 +284,15 @@ struct Tile {
       const int64_t blk = (drow64 * g.k + kk) >> 6;
       di.a[0] = scale_of<DQ>(sQ<CS>()[tid >> 2], sS<CS>()[tid >> 2], blk, mu);
     } else {
-      const int jg = tid >> 5, kg = tid & 31, bsel = kg >> 4;
+      const int jg = 2 * (tid >> 6) + (tid & 1), kg = (tid >> 1) & 31, bsel = kg >> 4;
       const uint16_t *raw = (const uint16_t *)sC<CS>();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         di.c[i] = raw[(4 * jg + i) * 32 + kg];
         const int64_t j = kk + 4 * jg + i;
         const int64_t jc = j < g.d ? j : g.d - 1;
-        const int64_t blk = (jc * g.k + dcol) >> 6;
+        // only blk % 4 is used (the int8 code's byte in its dword): 32-bit math
+        const int64_t blk = (int64_t)((uint32_t)jc * (uint32_t)(g.k >> 6) + (uint32_t)(dcol >> 6));
         const float v = scale_of<DQ>(sQ<CS>()[8 * jg + 2 * i + bsel],
                                      sS<CS>()[8 * jg + 2 * i + bsel], blk, mu);
         di.a[i] = j < g.d ? v : 0.0f;  // rows past d: zero
@@ -322,11 +326,11 @@ struct Tile {
       // column 4kg+i: nibble at bit 4, 0, 12, 8 of the 2-byte pair
       const int sh = i == 0 ? 4 : i == 1 ? 0 : i == 2 ? 12 : 8;
       const float *lv = s_lv;
-      const int jg = tid >> 5;
+      const int jg = 2 * (tid >> 6) + (tid & 1), kg = (tid >> 1) & 31;
       uint2 o;
       o.x = ql::pack_bf16x2(lv[(di.c[0] >> sh) & 15] * di.a[0], lv[(di.c[1] >> sh) & 15] * di.a[1]);
       o.y = ql::pack_bf16x2(lv[(di.c[2] >> sh) & 15] * di.a[2], lv[(di.c[3] >> sh) & 15] * di.a[3]);
-      ((uint2 *)sW<WS>())[2 * swz(4 * (tid & 31) + i, jg >> 1) + (jg & 1)] = o;
+      ((uint2 *)sW<WS>())[2 * swz(4 * kg + i, jg >> 1) + (jg & 1)] = o;
     }
   }
 
