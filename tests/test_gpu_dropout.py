@@ -107,3 +107,32 @@ def test_invalid_rate_is_rejected(ops):
     for bad in (1.0, -0.1, float("nan")):
         with pytest.raises(ops.QLoRAError):
             ops.linear_fwd(w, X, A, B, 32.0, dropout=bad, seed=1)
+
+
+def test_q_proj_shape_with_dropout(ops):
+    # 4096 x 4096 NF4 + DQ, 2048 tokens, r = 16, alpha = 32, p = 0.05: the
+    # training step's shape, every output compared in full
+    d = k = 4096
+    M, r, p, seed = 2048, 16, 0.05, 2024
+    print(f"[dropout] q_proj shape p={p}", flush=True)
+    inp = synth.linear_inputs(d, k, M, r, idx=31)
+    w = ops.quantize(to_dev(inp["W0"]), True)
+    X, A, B, dY = (to_dev(inp[n]) for n in ("X", "A", "B", "dY"))
+    Y, H = ops.linear_fwd(w, X, A, B, 32.0, dropout=p, seed=seed)
+    dX, dA, dB = ops.linear_bwd(w, X, A, B, 32.0, dY, H=H, dropout=p, seed=seed)
+    torch.cuda.synchronize()
+    keep = od.keep_mask(seed, M, k, p)
+    assert abs(keep.mean() - (1 - p)) < 1e-3
+    s = olora.lora_scale(32.0, r)
+    Wd = oracle_wdeq(oracle_quant(inp["W0"], True), d, k)
+    Xf, Af, Bf, dYf = (bf16_f64(inp[n]) for n in ("X", "A", "B", "dY"))
+    Yo, Ho = od.forward(Wd, Xf, Af, Bf, s, keep, p)
+    dXo, dAo, dBo, _ = od.backward(Wd, Xf, Af, Bf, s, dYf, keep, p)
+    assert rel_frob(H.cpu().numpy().astype(np.float64), Ho) < 1e-5
+    for name, got, want in (("Y", Y, Yo), ("dX", dX, dXo), ("dA", dA, dAo), ("dB", dB, dBo)):
+        err = rel_frob(bf16_f64(to_host_bits(got)), want)
+        assert err <= TOL, f"{name}: {err:.3e}"
+    # the rank-r part of Y alone (about 4% of |Y|) against the oracle's
+    Yb = Wd @ Xf.T
+    lora_got = bf16_f64(to_host_bits(Y)) - Yb.T
+    assert rel_frob(lora_got, Yo - Yb.T) < 0.1
