@@ -238,3 +238,28 @@ def test_half_gaps_leave_room_for_the_packed_threshold_index():
     assert len(bits) == 15
     for b in bits:
         assert b & 0x7FFFFF == 0 and 0 < (b >> 23) < 255
+
+
+def test_no_cpu_fallback():
+    # the binding only marshals device tensors: host tensors are refused
+    # before anything reaches the library, and a missing library raises
+    import torch
+    ops = _ops()
+    W = torch.zeros(64, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ops.quantize(W, True)
+    w = ops.NF4Weight(64, 128, True, torch.zeros(64 * 128 // 2, dtype=torch.uint8))
+    X = torch.zeros(4, 128, dtype=torch.bfloat16)
+    A = torch.zeros(16, 128, dtype=torch.bfloat16)
+    B = torch.zeros(64, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ops.linear_fwd(w, X, A, B, 32.0)
+    with pytest.raises(ValueError):
+        ops.linear_bwd(w, X, A, B, 32.0, torch.zeros(4, 64, dtype=torch.bfloat16))
+    saved_path, saved_lib = ops.LIB_PATH, ops._lib
+    try:
+        ops.LIB_PATH, ops._lib = os.path.join(ROOT, "no_such_lib.so"), None
+        with pytest.raises(ImportError):
+            ops.lib()
+    finally:
+        ops.LIB_PATH, ops._lib = saved_path, saved_lib
