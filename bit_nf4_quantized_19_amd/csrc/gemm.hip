@@ -273,6 +273,8 @@ struct Tile {
   struct DecIn {
     uint32_t c[4];   // forward: 2 code words; dX: 4 rows' 2-byte code pairs
     float a[4];      // forward: a[0] = the row's a'; dX: a' of each row
+    float f[16];     // dX: the 16 levels, read as soon as the codes are in (their
+                     // LDS latency then overlaps the step's first matrix ops)
   };
 
   template <int CS>
@@ -296,6 +298,12 @@ struct Tile {
         const float v = scale_of<DQ>(sQ<CS>()[8 * jg + 2 * i + bsel],
                                      sS<CS>()[8 * jg + 2 * i + bsel], blk, mu);
         di.a[i] = j < g.d ? v : 0.0f;  // rows past d: zero
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int sh = i == 0 ? 4 : i == 1 ? 0 : i == 2 ? 12 : 8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) di.f[4 * i + q] = s_lv[(di.c[q] >> sh) & 15];
       }
     }
     return di;
@@ -324,12 +332,11 @@ struct Tile {
       sW<WS>()[swz(tid >> 2, 4 * ((tid >> 1) & 1) + 2 * (tid & 1) + i)] = o;
     } else {
       // column 4kg+i: nibble at bit 4, 0, 12, 8 of the 2-byte pair
-      const int sh = i == 0 ? 4 : i == 1 ? 0 : i == 2 ? 12 : 8;
-      const float *lv = s_lv;
       const int jg = 2 * (tid >> 6) + (tid & 1), kg = (tid >> 1) & 31;
+      const float *f = &di.f[4 * i];
       uint2 o;
-      o.x = ql::pack_bf16x2(lv[(di.c[0] >> sh) & 15] * di.a[0], lv[(di.c[1] >> sh) & 15] * di.a[1]);
-      o.y = ql::pack_bf16x2(lv[(di.c[2] >> sh) & 15] * di.a[2], lv[(di.c[3] >> sh) & 15] * di.a[3]);
+      o.x = ql::pack_bf16x2(f[0] * di.a[0], f[1] * di.a[1]);
+      o.y = ql::pack_bf16x2(f[2] * di.a[2], f[3] * di.a[3]);
       ((uint2 *)sW<WS>())[2 * swz(4 * kg + i, jg >> 1) + (jg & 1)] = o;
     }
   }
