@@ -107,6 +107,8 @@ def test_lora_branch_alone(ops, M):
     (8, 64, 2, 5, 10.0),          # smallest legal weight
     (200, 320, 100, 32, 64.0),    # GEMM path, two rank blocks, B read in place
     (96, 128, 40, 64, 16.0),      # GEMM path, four rank blocks, ragged m tile
+    (136, 256, 300, 128, 32.0),   # GEMM path, the largest rank (eight rank blocks)
+    (264, 320, 4, 128, 32.0),     # GEMV path, the largest rank
 ])
 def test_ragged_shapes(ops, d, k, M, r, alpha):
     g, o = _case(ops, d, k, M, r, alpha, True, seed=d + k + M + r)
