@@ -208,6 +208,7 @@ def main():
     probes = measure_probes(torch, dev) if args.rows == "on" else None
     if probes:
         roofline["frac_of_measured_gemm_probe"] = round(achieved / probes["bf16_gemm_8192_TFLOP_s"], 4)
+        probes["nf4_step_over_bf16_lora_step"] = round(ms_step / probes["bf16_lora_step_ms"], 4)
     cpu = cpu_baseline(inp, flops) if args.cpu_baseline == "on" else None
 
     line = {
@@ -488,6 +489,38 @@ def measure_probes(torch, dev):
     ms = s0.elapsed_time(s1) / 10
     out["bf16_gemm_8192_TFLOP_s"] = round(2 * 8192 ** 3 / (ms * 1e-3) / 1e12, 1)
     del a, b
+    # the same layer step with a 16-bit base (plain bf16 W, vendor matmuls,
+    # 2-D products with contiguous right operands): the pages put QLoRA's
+    # training slowdown against 16-bit LoRA at 15-30%
+    g = torch.Generator(device=dev)
+    g.manual_seed(81)
+    rn = lambda *sh: torch.randn(*sh, generator=g, device=dev, dtype=torch.float32)
+    Wb = (rn(D, K) * 0.02).bfloat16()
+    WbT = Wb.t().contiguous()
+    Xb, dYb = rn(M, K).bfloat16(), rn(M, D).bfloat16()
+    Ab, Bb = (rn(R, K) * 0.01).bfloat16(), (rn(D, R) * 0.01).bfloat16()
+    AbT, BbT = Ab.t().contiguous(), Bb.t().contiguous()
+    sc = ALPHA / R
+
+    def lora16_step():
+        Hb = Xb @ AbT
+        Yb = torch.addmm(Xb @ WbT, Hb, BbT, alpha=sc)
+        Gb = dYb @ Bb
+        dXb = torch.addmm(dYb @ Wb, Gb, Ab, alpha=sc)
+        dAb = (Gb.t() @ Xb) * sc
+        dBb = (dYb.t() @ Hb) * sc
+        return Yb, dXb, dAb, dBb
+    for _ in range(20):
+        lora16_step()
+    torch.cuda.synchronize()
+    s0.record()
+    for _ in range(100):
+        lora16_step()
+    s1.record()
+    torch.cuda.synchronize()
+    out["bf16_lora_step_ms"] = round(s0.elapsed_time(s1) / 100, 4)
+    del Wb, WbT, Xb, dYb
+    torch.cuda.empty_cache()
     torch.cuda.empty_cache()
     log(f"[bench] probes: {json.dumps(out)}")
     return out
