@@ -190,11 +190,13 @@ def main():
     if rows is not None:
         # the same step with dropout 0.05 on the adapter input (mask drawn in
         # the kernels from a per-step seed) against the step without
-        def step_drop(i):
+        dmask = ops.dropout_mask(M, K, dev)
+
+        def step_drop(i):   # the forward stores the keep bits, the backward reads them
             ops.linear_fwd(w, X, A, B, ALPHA, save_h=True, Y=Y, H=H, ws=ws_f,
-                           dropout=0.05, seed=1000 + i)
+                           dropout=0.05, seed=1000 + i, mask=dmask)
             ops.linear_bwd(w, X, A, B, ALPHA, dY, H=H, dX=dX, dA=dA, dB=dB, ws=ws_b,
-                           dropout=0.05, seed=1000 + i)
+                           dropout=0.05, seed=1000 + i, mask=dmask)
         ms_plain = _rotated(lambda i: step(), 1, 20)
         ms_drop = _rotated(step_drop, 4, 20)
         rows["lora_dropout_step"] = {

@@ -119,11 +119,13 @@ DropParams drop_params(const qlora_lora_dropout *dr, int i) {
     dp.thr = (uint32_t)floor((double)dr->p * 4294967296.0);
     dp.inv_keep = (float)(1.0 / (1.0 - (double)dr->p));
     dp.on = 1;
+    dp.mask = i == 0 ? dr->mask : nullptr;
   }
   return dp;
 }
 bool drop_ok(const qlora_lora_dropout *dr) {
-  return !dr || (isfinite(dr->p) && dr->p >= 0.0f && dr->p < 1.0f);
+  return !dr || (isfinite(dr->p) && dr->p >= 0.0f && dr->p < 1.0f &&
+                 ((uintptr_t)dr->mask & 15u) == 0);
 }
 
 BwdWs bwd_layout(char *base, int64_t d, int64_t k, int64_t M, int r, bool need_h, bool need_dx) {
@@ -315,9 +317,11 @@ static qlora_status linear_fwd_group(const qlora_nf4_weight *const *w, int nw, c
   // H_i = X A_i^T (float32, M x rp) and s*H_i as bf16 hi/lo for every weight
   // in one launch; H_save gets the M x r copies
   SkinnyOut so[kMaxGroup];
-  for (int i = 0; i < nw; ++i)
+  for (int i = 0; i < nw; ++i) {
     so[i] = SkinnyOut{A[i], L.H[i], H_save ? H_save[i] : nullptr, L.Hs_hi[i], L.Hs_lo[i],
                       drop_params(drop, i)};
+    so[i].dp.mask_write = 1;   // the drawn bits go to the caller's mask, if any
+  }
   if ((s = launch_skinny(X, M, k, nw, so, false, r, rp, r, sc, st)) != QLORA_OK) return s;
   if (nw == 1)
     return launch_gemm_fwd(w[0]->codes, scale_src(w[0]), d[0], k, X, M, B[0], r, L.Hs_hi[0],
@@ -425,14 +429,22 @@ qlora_status qlora_linear_bwd_ex(const qlora_nf4_weight *w, const uint16_t *X, i
   if (s != QLORA_OK) return s;
   // dB = s dY^T H (d x r) and dA = s G^T X (r x k), one launch
   const DropParams none{0u, 0u, 0u, 1.0f, 0};
+  // with a mask stored by the forward (M > 16) colacc reads the bits from it
+  // and the dX epilogue uses it directly; otherwise colacc draws them and
+  // keeps a copy in the workspace for the dX epilogue
+  DropParams dpa = dp;
+  dpa.mask_write = 0;
+  if (M <= 16) dpa.mask = nullptr;
+  uint8_t *keep = dp.on ? (dpa.mask ? dpa.mask : L.keep) : nullptr;
   if ((s = launch_colacc2(ColaccReq{dY, d, Hq, dB, 0, none, nullptr},
-                          ColaccReq{X, k, L.G, dA, 1, dp, (dp.on && need_dx) ? L.keep : nullptr},
+                          ColaccReq{X, k, L.G, dA, 1, dpa,
+                                    (dp.on && need_dx && !dpa.mask) ? L.keep : nullptr},
                           M, rp, r, sc,
                           L.cpart, st)) != QLORA_OK)
     return s;
   if (need_dx) {
     if ((s = launch_gemm_dx(w->codes, scale_src(w), d, k, dY, M, A, r, L.Gs_hi, L.Gs_lo, rp, dX,
-                            dp.on ? L.keep : nullptr, dp.inv_keep, st)) != QLORA_OK)
+                            keep, dp.inv_keep, st)) != QLORA_OK)
       return s;
   }
   return QLORA_OK;

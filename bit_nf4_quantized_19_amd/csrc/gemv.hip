@@ -108,6 +108,8 @@ QL_DEV GemvW wsel(const GemvArgs &g, int i) {
   W.dp.thr = QL_PICK(g.w, i, dp.thr);
   W.dp.inv_keep = QL_PICK(g.w, i, dp.inv_keep);
   W.dp.on = QL_PICK(g.w, i, dp.on);
+  W.dp.mask_write = 0;   // the decode path never stores the mask
+  W.dp.mask = nullptr;
   return W;
 }
 QL_DEV int weight_of(const GemvArgs &g, int64_t rg) {

@@ -115,6 +115,8 @@ __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
   dp.thr = QL_SKPICK(dp.thr);
   dp.inv_keep = QL_SKPICK(dp.inv_keep);
   dp.on = !PCOL && QL_SKPICK(dp.on);
+  dp.mask_write = QL_SKPICK(dp.mask_write);
+  dp.mask = QL_SKPICK(dp.mask);
   constexpr int PQ = 272;   // bytes per lane group in the transposition slot (256 + pad)
   __shared__ f32x4 red[SK_W][64];
   __shared__ __align__(16) unsigned char pst[PCOL ? SK_W : 1][4 * PQ];
@@ -144,7 +146,12 @@ __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
       }
       if (dp.on) {   // dropped elements of X (token m, columns cc + 8kq ..) read as 0
         const uint64_t e = (uint64_t)(m_ok ? m : 0) * (uint64_t)C + (uint64_t)(cc + 8 * kq);
-        a[u] = mask_bf16x8(a[u], keep4(dp, e) | (keep4(dp, e + 4) << 4));
+        const uint32_t k8 = keep4(dp, e) | (keep4(dp, e + 4) << 4);
+        a[u] = mask_bf16x8(a[u], k8);
+        // stored for the backward once (first rank block), by the lanes whose
+        // chunk lies in the row
+        if (dp.mask_write && dp.mask && t0 == 0 && m_ok && cc + 8 * kq < c_hi)
+          *(uint16_t *)(dp.mask + (e >> 2)) = (uint16_t)((k8 & 15u) | ((k8 >> 4) << 8));
       }
       if (PCOL) {
         const int64_t row = cc + 8 * kq + rho;   // B row, t = t0 + 8 hf .. +7
@@ -217,17 +224,31 @@ struct ColaccProb {
 // Batch of CA_TOK tokens of one wave: this lane's 4 columns of each token
 // row and its float4 of the batch's Q block (token l/4, t = t0 + 4(l%4)..);
 // tokens past the wave's range read as zero.
+template <bool MK>
 struct CaBatch {
   uint2 v[CA_TOK];
   float4 q;
+  uint32_t kb[MK ? CA_TOK / 4 : 1];   // stored keep nibbles of the batch's tokens (4 per word)
 };
 
-QL_DEV void ca_load(CaBatch &b, const uint16_t *inc, int64_t C, bool c_ok, const float *Q, int rp,
-                    int t0, int64_t m, int64_t m_hi, int lane) {
+template <bool MK>
+QL_DEV void ca_load(CaBatch<MK> &b, const uint16_t *inc, int64_t C, bool c_ok, const float *Q,
+                    int rp, int t0, int64_t m, int64_t m_hi, int lane, const uint8_t *mk) {
 #pragma unroll
   for (int u = 0; u < CA_TOK; ++u) {
     const int64_t mm = m + u < m_hi ? m + u : m_hi - 1;  // clamped; not accumulated
     b.v[u] = c_ok ? *(const uint2 *)(inc + mm * C) : make_uint2(0u, 0u);
+  }
+  // with a stored mask, its bytes travel with the batch's loads (mk: the
+  // lane's column byte of row 0, or NULL)
+#pragma unroll
+  for (int j = 0; j < (MK ? CA_TOK / 4 : 1); ++j) b.kb[j] = 0u;
+  if (MK && mk) {
+#pragma unroll
+    for (int u = 0; u < CA_TOK; ++u) {
+      const int64_t mm = m + u < m_hi ? m + u : m_hi - 1;
+      b.kb[u >> 2] |= (uint32_t)mk[mm * (C >> 2)] << (8 * (u & 3));
+    }
   }
   const int64_t mq = m + (lane >> 2);
   b.q = mq < m_hi ? *(const float4 *)(Q + mq * rp + t0 + 4 * (lane & 3))
@@ -236,12 +257,15 @@ QL_DEV void ca_load(CaBatch &b, const uint16_t *inc, int64_t C, bool c_ok, const
 
 // Dropout of the batch's first n tokens: their dropped elements become 0,
 // and the keep bits (4 per lane and token) are stored for the dX epilogue.
-QL_DEV void ca_drop(CaBatch &b, const DropParams &dp, int64_t m, int n, int64_t C, int64_t c0,
+template <bool MK>
+QL_DEV void ca_drop(CaBatch<MK> &b, const DropParams &dp, int64_t m, int n, int64_t C, int64_t c0,
                     uint8_t *keep) {
 #pragma unroll
   for (int u = 0; u < CA_TOK; ++u) {
     if (u >= n) continue;  // wave-uniform
-    const uint32_t bits = keep4(dp, (uint64_t)(m + u) * (uint64_t)C + (uint64_t)c0);
+    // the bits the forward stored (loaded with the batch), or drawn here
+    const uint32_t bits = MK ? (b.kb[MK ? u >> 2 : 0] >> (8 * (u & 3))) & 15u
+                             : keep4(dp, (uint64_t)(m + u) * (uint64_t)C + (uint64_t)c0);
     b.v[u].x &= ((bits & 1u) ? 0x0000FFFFu : 0u) | ((bits & 2u) ? 0xFFFF0000u : 0u);
     b.v[u].y &= ((bits & 4u) ? 0x0000FFFFu : 0u) | ((bits & 8u) ? 0xFFFF0000u : 0u);
     if (keep) keep[(m + u) * (C >> 2) + (c0 >> 2)] = (uint8_t)bits;
@@ -250,8 +274,8 @@ QL_DEV void ca_drop(CaBatch &b, const DropParams &dp, int64_t m, int n, int64_t 
 
 // acc[c][t] += x[token][c] * Q[token][t] over the batch's tokens (the first
 // n of them when PART)
-template <bool PART>
-QL_DEV void ca_batch(float (&acc)[4][16], const CaBatch &b, const float4 *qs, int n) {
+template <bool PART, bool MK>
+QL_DEV void ca_batch(float (&acc)[4][16], const CaBatch<MK> &b, const float4 *qs, int n) {
 #pragma unroll
   for (int u = 0; u < CA_TOK; ++u) {
     if (PART && u >= n) continue;  // wave-uniform
@@ -276,6 +300,7 @@ QL_DEV void ca_batch(float (&acc)[4][16], const CaBatch &b, const float4 *qs, in
 // tokens with the next batch's loads in flight; the Q block of a batch is
 // staged in the wave's own LDS slot and read back as broadcasts. The waves'
 // sums are added in LDS in a fixed order.
+template <bool MK>
 __global__ __launch_bounds__(64 * CA_W) void colacc_kernel(ColaccProb p0, ColaccProb p1,
                                                            int64_t M, int rp, int64_t mps) {
   __shared__ float4 qst[CA_W][64];
@@ -300,20 +325,26 @@ __global__ __launch_bounds__(64 * CA_W) void colacc_kernel(ColaccProb p0, Colacc
     for (int t = 0; t < 16; ++t) acc[c][t] = 0.0f;
   const bool c_ok = c0 < P.C;  // C % 64 == 0: the 4 columns are all in or all out
   const uint16_t *inc = P.In + (c_ok ? c0 : 0);
+  // only the problem that drops (the adapter input) has a mask; the other
+  // problem of the launch (dY for dB) reads none
+  const uint8_t *mk = (MK && P.dp.on && P.dp.mask && !P.dp.mask_write && c_ok)
+                          ? P.dp.mask + (c0 >> 2)
+                          : nullptr;
   if (w_lo < w_hi) {
-    CaBatch cur, nxt;
-    ca_load(nxt, inc, P.C, c_ok, P.Q, rp, t0, w_lo, w_hi, lane);
+    CaBatch<MK> cur, nxt;
+    ca_load(nxt, inc, P.C, c_ok, P.Q, rp, t0, w_lo, w_hi, lane, mk);
     for (int64_t m = w_lo; m < w_hi; m += CA_TOK) {
       cur = nxt;
-      if (m + CA_TOK < w_hi) ca_load(nxt, inc, P.C, c_ok, P.Q, rp, t0, m + CA_TOK, w_hi, lane);
+      if (m + CA_TOK < w_hi)
+        ca_load(nxt, inc, P.C, c_ok, P.Q, rp, t0, m + CA_TOK, w_hi, lane, mk);
       qst[wave][lane] = cur.q;   // this wave's previous reads of the slot precede (in order)
       if (P.dp.on && c_ok)
         ca_drop(cur, P.dp, m, (int)min<int64_t>(CA_TOK, w_hi - m), P.C, c0,
                 tb == 0 ? P.keep : nullptr);
       if (m + CA_TOK <= w_hi)
-        ca_batch<false>(acc, cur, qst[wave], CA_TOK);
+        ca_batch<false, MK>(acc, cur, qst[wave], CA_TOK);
       else
-        ca_batch<true>(acc, cur, qst[wave], (int)(w_hi - m));
+        ca_batch<true, MK>(acc, cur, qst[wave], (int)(w_hi - m));
     }
   }
   // the waves' sums in a fixed order: ((wave 0 + 1) + 2) + ... ; thread p of
@@ -457,7 +488,11 @@ qlora_status launch_colacc2(const ColaccReq &a, const ColaccReq &b, int64_t M, i
   dim3 grid((unsigned)((p0.groups + p1.groups) * tbs), (unsigned)S);
   {
     QlProf prof(QLORA_K_LORA_COLACC, st);
-    colacc_kernel<<<grid, 64 * CA_W, 0, st>>>(p0, p1, M, rp, mps);
+    // MK: the adapter input's keep bits come from the mask the forward stored
+    if (p1.dp.on && p1.dp.mask && !p1.dp.mask_write)
+      colacc_kernel<true><<<grid, 64 * CA_W, 0, st>>>(p0, p1, M, rp, mps);
+    else
+      colacc_kernel<false><<<grid, 64 * CA_W, 0, st>>>(p0, p1, M, rp, mps);
   }
   ColaccOut o0{p0.part, a.C, a.out, a.transpose_out, a.C * r, a.dp.on ? s * a.dp.inv_keep : s};
   ColaccOut o1{p1.part, b.C, b.out, b.transpose_out, b.C * r, b.dp.on ? s * b.dp.inv_keep : s};

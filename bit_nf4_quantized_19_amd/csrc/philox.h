@@ -17,6 +17,9 @@ struct DropParams {
   uint32_t thr;        // floor(p * 2^32)
   float inv_keep;      // fl32(1 / (1 - p))
   int on;              // p > 0
+  int mask_write;      // 1: the kernel that draws the bits also stores them in mask
+  uint8_t *mask;       // keep bits stored between forward and backward (one nibble per
+                       // four elements: byte (m*C + c)/4, bit c%4), or NULL
 };
 
 QL_DEV uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {

@@ -253,15 +253,32 @@ def dequantize(w: NF4Weight, out: torch.Tensor | None = None, stream=None) -> to
 
 
 class LoraDropoutC(ctypes.Structure):
-    _fields_ = [("p", ctypes.c_float), ("reserved", ctypes.c_uint32), ("seed", ctypes.c_uint64)]
+    _fields_ = [("p", ctypes.c_float), ("reserved", ctypes.c_uint32), ("seed", ctypes.c_uint64),
+                ("mask", ctypes.c_void_p)]
+
+
+def dropout_mask(M: int, k: int, device="cuda") -> torch.Tensor:
+    """Buffer for the keep bits a forward stores for its backward (M*k/4 bytes)."""
+    return torch.empty(M * k // 4, dtype=torch.uint8, device=device)
+
+
+def _check_mask(mask, M: int, k: int):
+    if mask is None:
+        return
+    if (mask.dtype != torch.uint8 or not mask.is_cuda or not mask.is_contiguous()
+            or mask.numel() < M * k // 4):
+        raise ValueError(f"mask: contiguous uint8 device tensor of at least {M * k // 4} "
+                         "bytes (M*k/4) expected")
 
 
 def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                lora_alpha: float, save_h: bool = True, Y: torch.Tensor | None = None,
                H: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None,
-               dropout: float = 0.0, seed: int = 0):
+               dropout: float = 0.0, seed: int = 0, mask: torch.Tensor | None = None):
     """Y = X W'^T + (alpha/r) (X~ A^T) B^T with X~ the adapter input after
-    dropout at rate `dropout` (mask from `seed`; 0 = none). Returns (Y, H or None)."""
+    dropout at rate `dropout` (keep bits from `seed`; 0 = none); with more than
+    16 tokens the bits are also stored in `mask` (M*k/4 bytes, see
+    dropout_mask) when given. Returns (Y, H or None)."""
     for t, nm in ((X, "X"), (A, "A"), (B, "B")):
         _dev_bf16(t, nm)
     M = X.shape[0]
@@ -274,7 +291,8 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
     wst, wsn = _workspace(wsb, X.device, ws)
     cw = w.c_struct()
     if dropout:
-        dr = LoraDropoutC(float(dropout), 0, int(seed))
+        _check_mask(mask, M, w.k)
+        dr = LoraDropoutC(float(dropout), 0, int(seed), _ptr(mask))
         _check(lib().qlora_linear_fwd_ex(ctypes.byref(cw), X.data_ptr(), M, A.data_ptr(),
                                          B.data_ptr(), r, float(lora_alpha), ctypes.addressof(dr),
                                          Y.data_ptr(), _ptr(H) if save_h else None, _ptr(wst),
@@ -322,8 +340,11 @@ def linear_fwd_multi(ws_: list, X: torch.Tensor, As: list, Bs: list, lora_alpha:
 def linear_bwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                lora_alpha: float, dY: torch.Tensor, H: torch.Tensor | None = None,
                need_dx: bool = True, dX=None, dA=None, dB=None,
-               ws: torch.Tensor | None = None, stream=None, dropout: float = 0.0, seed: int = 0):
-    """Returns (dX or None, dA, dB); `dropout`/`seed` as given to the forward."""
+               ws: torch.Tensor | None = None, stream=None, dropout: float = 0.0, seed: int = 0,
+               mask: torch.Tensor | None = None):
+    """Returns (dX or None, dA, dB); `dropout`, `seed` and `mask` as given to the
+    forward (with more than 16 tokens the forward stored the keep bits in
+    `mask`, which the backward then reads instead of drawing them again)."""
     for t, nm in ((X, "X"), (A, "A"), (B, "B"), (dY, "dY")):
         _dev_bf16(t, nm)
     M = X.shape[0]
@@ -339,7 +360,8 @@ def linear_bwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
     wst, wsn = _workspace(wsb, dev, ws)
     cw = w.c_struct()
     if dropout:
-        dr = LoraDropoutC(float(dropout), 0, int(seed))
+        _check_mask(mask, M, w.k)
+        dr = LoraDropoutC(float(dropout), 0, int(seed), _ptr(mask))
         _check(lib().qlora_linear_bwd_ex(ctypes.byref(cw), X.data_ptr(), M, A.data_ptr(),
                                          B.data_ptr(), r, float(lora_alpha), ctypes.addressof(dr),
                                          dY.data_ptr(), _ptr(H), _ptr(dX) if need_dx else None,

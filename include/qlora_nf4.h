@@ -143,6 +143,14 @@ typedef struct qlora_lora_dropout {
   float p;
   uint32_t reserved;   /* set to 0 */
   uint64_t seed;
+  /* Optional (NULL: none), M > 16 only: M*k/4 bytes of device memory,
+   * 16-byte aligned, owned by the caller. The forward stores the keep bits it
+   * draws there (byte (m*k + c)/4, bit c%4) and the backward of the same step
+   * reads them instead of drawing them again; pass the same pointer to both
+   * and keep its contents between them. Ignored for M <= 16 (the backward
+   * then draws the bits itself). A pointer not 16-byte aligned:
+   * QLORA_ERR_INVALID_ARG. */
+  uint8_t *mask;
 } qlora_lora_dropout;
 
 /* qlora_linear_fwd with adapter-input dropout (workspace as for QLORA_OP_FWD). */

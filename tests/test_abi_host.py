@@ -142,7 +142,8 @@ b("bwd_null_dA", dA=None)
 b("bwd_ws_small", wsb=128)
 b("bwd_r0", r=0)
 class DR(ctypes.Structure):
-    _fields_ = [("p", ctypes.c_float), ("reserved", ctypes.c_uint32), ("seed", ctypes.c_uint64)]
+    _fields_ = [("p", ctypes.c_float), ("reserved", ctypes.c_uint32), ("seed", ctypes.c_uint64),
+                ("mask", ctypes.c_void_p)]
 def fx(name, rate):
     dr = DR(rate, 0, 7)
     out[name] = L.qlora_linear_fwd_ex(ctypes.byref(w), P, 16, P, P, 8, 16.0, ctypes.addressof(dr),
@@ -168,6 +169,11 @@ out["resq_null_A"] = L.qlora_nf4_quantize_residual(P, None, P, 8, 16.0, ctypes.b
                                                    1 << 34, None)
 out["resq_r65"] = L.qlora_nf4_quantize_residual(P, P, P, 65, 16.0, ctypes.byref(w), P, 1 << 34,
                                                 None)
+def fxm(name, mask):
+    dr = DR(0.1, 0, 7, mask)
+    out[name] = L.qlora_linear_fwd_ex(ctypes.byref(w), P, 16, P, P, 8, 16.0, ctypes.addressof(dr),
+                                      P, P, P, 1 << 30, None)
+fxm("fwd_drop_misaligned_mask", P + 2)
 fx("fwd_drop_one", 1.0)
 fx("fwd_drop_neg", -0.25)
 fx("fwd_drop_nan", float("nan"))
@@ -206,7 +212,7 @@ EXPECTED = {
     "fwd_inf_alpha": -1, "fwd_M0": -1, "fwd_null_X": -1, "fwd_misaligned_B": -1,
     "fwd_ws_small": -3, "bwd_null_dY": -1, "bwd_null_dA": -1, "bwd_ws_small": -3,
     "bwd_r0": -1, "fwd_drop_one": -1, "fwd_drop_neg": -1, "fwd_drop_nan": -1,
-    "bwd_drop_one": -1, "bwd_drop_inf": -1, "loftq_r0": -1, "loftq_r65": -2,
+    "bwd_drop_one": -1, "bwd_drop_inf": -1, "fwd_drop_misaligned_mask": -1, "loftq_r0": -1, "loftq_r65": -2,
     "loftq_iters0": -1, "loftq_neg_power": -1, "loftq_null_omega": -1, "loftq_alpha0": -1,
     "loftq_ws_small": -3, "resq_null_A": -1, "resq_r65": -2, "merge_null_out": -1, "merge_r_big": -2, "deq_null_out": -1,
     "codebook_null": -1, "adam_null_param": -1, "adam_null_grad": -1, "adam_n0": -1,

@@ -136,3 +136,49 @@ def test_q_proj_shape_with_dropout(ops):
     Yb = Wd @ Xf.T
     lora_got = bf16_f64(to_host_bits(Y)) - Yb.T
     assert rel_frob(lora_got, Yo - Yb.T) < 0.1
+
+
+def _packed_nibbles(keep):
+    M, k = keep.shape
+    return (keep.reshape(M, k // 4, 4).astype(np.uint32) * np.array([1, 2, 4, 8], np.uint32)
+            ).sum(-1).astype(np.uint8).reshape(-1)
+
+
+@pytest.mark.parametrize("d,k,M,r", [(264, 512, 300, 16), (200, 320, 40, 8), (128, 256, 17, 32)])
+def test_stored_mask_equals_redraw(ops, d, k, M, r):
+    # the forward stores the keep bits it draws (they are the oracle's bits),
+    # and the backward that reads them gives the same bits as one that draws
+    p, seed, alpha = 0.1, 77, 2.0 * r
+    inp = synth.linear_inputs(d, k, M, r, idx=40 + M)
+    w = ops.quantize(to_dev(inp["W0"]), True)
+    X, A, B, dY = (to_dev(inp[n]) for n in ("X", "A", "B", "dY"))
+    mask = ops.dropout_mask(M, k)
+    mask.fill_(0xEE)
+    Y1, H1 = ops.linear_fwd(w, X, A, B, alpha, dropout=p, seed=seed, mask=mask)
+    torch.cuda.synchronize()
+    stored = mask.cpu().numpy().copy()
+    dX1, dA1, dB1 = ops.linear_bwd(w, X, A, B, alpha, dY, H=H1, dropout=p, seed=seed, mask=mask)
+    Y0, H0 = ops.linear_fwd(w, X, A, B, alpha, dropout=p, seed=seed)
+    dX0, dA0, dB0 = ops.linear_bwd(w, X, A, B, alpha, dY, H=H0, dropout=p, seed=seed)
+    torch.cuda.synchronize()
+    assert np.array_equal(stored, _packed_nibbles(od.keep_mask(seed, M, k, p)))
+    assert np.array_equal(H0.cpu().numpy().view(np.uint32), H1.cpu().numpy().view(np.uint32))
+    for a, b in ((Y0, Y1), (dX0, dX1), (dA0, dA1), (dB0, dB1)):
+        assert np.array_equal(to_host_bits(a), to_host_bits(b))
+
+
+def test_mask_unused_on_the_decode_path(ops):
+    d, k, M, r = 256, 512, 4, 16
+    inp = synth.linear_inputs(d, k, M, r, idx=45)
+    w = ops.quantize(to_dev(inp["W0"]), True)
+    X, A, B, dY = (to_dev(inp[n]) for n in ("X", "A", "B", "dY"))
+    mask = ops.dropout_mask(M, k)
+    mask.fill_(0xEE)
+    Y1, H1 = ops.linear_fwd(w, X, A, B, 32.0, dropout=0.1, seed=5, mask=mask)
+    dX1, dA1, dB1 = ops.linear_bwd(w, X, A, B, 32.0, dY, H=H1, dropout=0.1, seed=5, mask=mask)
+    Y0, H0 = ops.linear_fwd(w, X, A, B, 32.0, dropout=0.1, seed=5)
+    dX0, dA0, dB0 = ops.linear_bwd(w, X, A, B, 32.0, dY, H=H0, dropout=0.1, seed=5)
+    torch.cuda.synchronize()
+    assert np.all(mask.cpu().numpy() == 0xEE)
+    for a, b in ((Y0, Y1), (dX0, dX1), (dA0, dA1), (dB0, dB1)):
+        assert np.array_equal(to_host_bits(a), to_host_bits(b))
