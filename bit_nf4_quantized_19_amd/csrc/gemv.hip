@@ -139,6 +139,7 @@ struct GUnit {
   int64_t row0;     // first row of the unit (in its weight)
   int64_t dlim;     // rows of its weight
   int64_t rbase;    // its weight's first column in the partial-sum rows
+  const uint8_t *crow;   // the lane's row codes of this slice
 };
 
 template <bool DQ, bool FULL, bool GRP>
@@ -170,13 +171,14 @@ QL_DEV void unit_load(const GemvArgs &g, GUnit &u, int64_t rg, int64_t b0, int n
   }
   // blocks past the end of a ragged slice re-read the last block; their X
   // chunks are zero
-  const uint8_t *crow = W.codes + row * (g.k >> 1) + b0 * 32;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int bb = FULL ? 4 * c + q : min(4 * c + q, nblk - 1);
-    u.cw[c][0] = *(const uint4 *)(crow + 32 * bb);
-    u.cw[c][1] = *(const uint4 *)(crow + 32 * bb + 16);
-  }
+  u.crow = W.codes + row * (g.k >> 1) + b0 * 32;
+}
+// codes of chunk c (blocks 4c + q) of a unit
+template <bool FULL>
+QL_DEV void unit_codes(GUnit &u, int c, int nblk, int q) {
+  const int bb = FULL ? 4 * c + q : min(4 * c + q, nblk - 1);
+  u.cw[c][0] = *(const uint4 *)(u.crow + 32 * bb);
+  u.cw[c][1] = *(const uint4 *)(u.crow + 32 * bb + 16);
 }
 
 // MFMA steps of NU units of a wave (same slice, so they share the A
@@ -358,6 +360,14 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
   GUnit ua, ub;
   unit_load<DQ, FULL, GRP>(g, ua, min(rga, g.ngroups - 1), b0, nblk, n, q);
   unit_load<DQ, FULL, GRP>(g, ub, min(rgb, g.ngroups - 1), b0, nblk, n, q);
+  // codes chunk by chunk, both units' chunk c before chunk c + 1: the
+  // compute of chunk c waits only for the loads up to it
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    unit_codes<FULL>(ua, c, nblk, q);
+    unit_codes<FULL>(ub, c, nblk, q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // 4. table (bf16 pair, even element in the low half), 32 copies per entry;
   //    X chunks; zero region
   {
