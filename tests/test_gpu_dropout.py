@@ -182,3 +182,18 @@ def test_mask_unused_on_the_decode_path(ops):
     assert np.all(mask.cpu().numpy() == 0xEE)
     for a, b in ((Y0, Y1), (dX0, dX1), (dA0, dA1), (dB0, dB1)):
         assert np.array_equal(to_host_bits(a), to_host_bits(b))
+
+
+def test_short_or_wrong_mask_buffer_is_rejected(ops):
+    # the binding checks the buffer before any launch: M*k/4 uint8 bytes
+    d, k, M, r = 128, 256, 40, 8
+    inp = synth.linear_inputs(d, k, M, r, idx=5)
+    t = {n: to_dev(inp[n]) for n in ("W0", "X", "A", "B", "dY")}
+    w = ops.quantize(t["W0"], True)
+    short = torch.empty(M * k // 4 - 1, dtype=torch.uint8, device="cuda")
+    wrong = torch.empty(M * k // 4, dtype=torch.int16, device="cuda")
+    for m in (short, wrong):
+        with pytest.raises(ValueError):
+            ops.linear_fwd(w, t["X"], t["A"], t["B"], 16.0, dropout=0.1, seed=1, mask=m)
+        with pytest.raises(ValueError):
+            ops.linear_bwd(w, t["X"], t["A"], t["B"], 16.0, t["dY"], dropout=0.1, seed=1, mask=m)

@@ -43,11 +43,13 @@ def _bufs(ops, d, k, M, r, dev):
 
 
 def _sequence(ops, t, b, alpha, dropout, stream=None):
+    mask = b.get("mask")
     ops.quantize(t["W0"], True, out=b["w"], ws=b["wsq"], stream=stream)
     ops.linear_fwd(b["w"], t["X"], t["A"], t["B"], alpha, Y=b["Y"], H=b["H"], ws=b["wsf"],
-                   stream=stream, dropout=dropout, seed=99)
+                   stream=stream, dropout=dropout, seed=99, mask=mask)
     ops.linear_bwd(b["w"], t["X"], t["A"], t["B"], alpha, t["dY"], H=b["H"], dX=b["dX"],
-                   dA=b["dA"], dB=b["dB"], ws=b["wsb"], stream=stream, dropout=dropout, seed=99)
+                   dA=b["dA"], dB=b["dB"], ws=b["wsb"], stream=stream, dropout=dropout, seed=99,
+                   mask=mask)
 
 
 def _snapshot(b):
@@ -56,20 +58,28 @@ def _snapshot(b):
             "dX": to_host_bits(b["dX"]), "dA": to_host_bits(b["dA"]), "dB": to_host_bits(b["dB"])}
 
 
-@pytest.mark.parametrize("d,k,M,r,dropout", [(512, 768, 96, 16, 0.0),    # GEMM path
-                                             (1024, 1088, 4, 16, 0.0),   # GEMV path
-                                             (512, 768, 96, 16, 0.1)])   # with dropout
-def test_graph_replays_match_eager(ops, d, k, M, r, dropout):
-    print(f"[graph] d={d} k={k} M={M} r={r} p={dropout}", flush=True)
+@pytest.mark.parametrize("d,k,M,r,dropout,mask", [
+    (512, 768, 96, 16, 0.0, False),    # GEMM path
+    (1024, 1088, 4, 16, 0.0, False),   # GEMV path
+    (512, 768, 96, 16, 0.1, False),    # with dropout (bits redrawn in the backward)
+    (512, 768, 96, 16, 0.1, True)])    # with dropout, bits stored by the forward
+def test_graph_replays_match_eager(ops, d, k, M, r, dropout, mask):
+    print(f"[graph] d={d} k={k} M={M} r={r} p={dropout} mask={mask}", flush=True)
     dev = torch.device("cuda")
     inp = synth.linear_inputs(d, k, M, r, idx=21)
     t = {n: to_dev(inp[n]) for n in ("W0", "X", "A", "B", "dY")}
     eager = _bufs(ops, d, k, M, r, dev)
+    if mask:
+        eager["mask"] = ops.dropout_mask(M, k, dev)
     _sequence(ops, t, eager, 32.0, dropout)
     torch.cuda.synchronize()
     want = _snapshot(eager)
+    if mask:
+        want["mask"] = eager["mask"].cpu().numpy()
 
     b = _bufs(ops, d, k, M, r, dev)
+    if mask:
+        b["mask"] = ops.dropout_mask(M, k, dev)
     _sequence(ops, t, b, 32.0, dropout)   # warm-up outside the capture
     torch.cuda.synchronize()
     for key in ("Y", "dX", "dA", "dB"):
@@ -87,11 +97,17 @@ def test_graph_replays_match_eager(ops, d, k, M, r, dropout):
         for key in ("Y", "dX", "dA", "dB", "H"):
             b[key].fill_(7.0)
         b["w"].codes.fill_(0)
+        if mask:
+            b["mask"].fill_(0)
         g.replay()
         torch.cuda.synchronize()
         got = _snapshot(b)
+        if mask:
+            got["mask"] = b["mask"].cpu().numpy()
         for key in want:
             assert np.array_equal(got[key], want[key]), (rep, key)
+        if mask:
+            other["mask"] = ops.dropout_mask(M, k, dev)
         _sequence(ops, t, other, 32.0, dropout)   # eager work between replays
         torch.cuda.synchronize()
 
