@@ -97,6 +97,7 @@ QL_DEV T pick4s(int i, T a0, T a1, T a2, T a3) {
 }
 #define QL_SKPICK(f) pick4s(wi, a.w[0].f, a.w[1].f, a.w[2].f, a.w[3].f)
 
+constexpr int SK_TOK = 8;   // tokens per workgroup (of the 16 MFMA rows)
 template <bool PCOL>
 __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
   const int wi = (int)blockIdx.y / a.tbw;   // uniform: fields picked by selects
@@ -124,8 +125,8 @@ __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
   const int r16 = lane & 15, kq = lane >> 4;
   const int64_t mb = blockIdx.x;
   const int t0 = 16 * ((int)blockIdx.y % a.tbw);
-  const int64_t m = mb * 16 + r16;
-  const bool m_ok = m < M;
+  const int64_t m = mb * SK_TOK + r16;
+  const bool m_ok = r16 < SK_TOK && m < M;   // MFMA rows past SK_TOK stay zero
   const uint16_t *inr = In + (m_ok ? m : 0) * C + 8 * kq;
   const int64_t c_lo = wave * cpw, c_hi = min(C, c_lo + cpw);
   const bool t_ok = t0 + r16 < r;
@@ -191,8 +192,8 @@ __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
   const int t = t0 + r16;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t mm = mb * 16 + 4 * kq + i;
-    if (mm >= M) continue;
+    const int64_t mm = mb * SK_TOK + 4 * kq + i;
+    if (4 * kq + i >= SK_TOK || mm >= M) continue;
     if (dp.on) v[i] *= dp.inv_keep;   // inverted dropout: kept elements scaled by 1/(1-p)
     out[mm * rp + t] = v[i];
     if (out2 && t < out2_ld) out2[mm * out2_ld + t] = v[i];
@@ -453,7 +454,7 @@ qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, int nw, con
   a.tbw = rp / 16;
   a.out2_ld = out2_ld;
   a.s = s;
-  const int64_t mbs = ql_cdiv(M, 16);
+  const int64_t mbs = ql_cdiv(M, SK_TOK);
   if (mbs > 0x7fffffff || (int64_t)nw * a.tbw > 65535) return QLORA_ERR_UNSUPPORTED;
   dim3 grid((unsigned)mbs, (unsigned)(nw * a.tbw));
   QlProf prof(QLORA_K_LORA_DOWN, st);
