@@ -8,7 +8,8 @@
 // Each reads one M x C activation once (X or dY) and is memory-bound; the
 // aim is to keep enough loads in flight and few launches.
 //   * skinny: out[m][t] = sum_c In[m][c] P[t][c] on MFMA 16x16x32, one
-//     launch: a workgroup owns a 16-token x 16-t block, its 16 waves split
+//     launch: a workgroup owns an 8-token x 16-t block (the MFMA tile's
+//     other 8 rows stay zero, so 2048 tokens fill the chip), its 16 waves split
 //     the c range and issue the loads of eight 32-wide K-slices before their
 //     MFMAs, and the waves' sums are added in LDS in a fixed order; it also
 //     emits s*out as bf16 hi/lo parts for the fused GEMM epilogue. P is A
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void layout_kernel(LayoutJobs jobs) {
 constexpr int SK_W = 16;       // waves per workgroup (column ranges of one token block)
 constexpr int SK_UNROLL = 8;   // K-slices of 32 whose loads are issued together
 
-// out[m][t] = sum_c In[m][c] P[t][c] for the 16 tokens of block blockIdx.x and
+// out[m][t] = sum_c In[m][c] P[t][c] for the SK_TOK tokens of block blockIdx.x and
 // t = 16 blockIdx.y + 0..15 (t < r; the rest are zero). P[t][c] is
 // Pm[t * C + c] (PCOL = false: A, r x C) or Pm[c * r + t] (PCOL = true: B,
 // C x r, r % 16 == 0). Wave w contracts columns [w cpw, (w+1) cpw) on
