@@ -23,6 +23,12 @@ key ``(seed mod 2^32, seed div 2^32)``, the element keeps when word
 ``e % 4`` of the output is >= ``floor(p * 2^32)`` (so it drops with
 probability p up to 2^-32). The GPU library implements the same generator
 from the same published definition.
+
+The rate is a float32 value: the library's interface takes it as a C
+``float``, so every function here first rounds the given p to float32
+(``rate32``) and uses that value for the threshold and for 1/(1 - p). The
+keep decision is an integer comparison, so both sides must start from the
+same rate; a float64 0.1 and its float32 rounding give thresholds 7 apart.
 """
 
 from __future__ import annotations
@@ -60,27 +66,42 @@ def philox4x32_10(ctr, key):
     return np.stack([c0, c1, c2, c3], axis=-1).astype(np.uint32)
 
 
+def rate32(p: float) -> float:
+    """The dropout rate as the library receives it: p rounded to float32."""
+    return float(np.float32(p))
+
+
 def drop_threshold(p: float) -> int:
-    """floor(p * 2^32): a random word below it drops the element."""
+    """floor(p32 * 2^32) for the float32 rate p32: a random word below it
+    drops the element (p32 * 2^32 is exact in float64, so is the floor)."""
+    p = rate32(p)
     if not (0.0 <= p < 1.0):
         raise ValueError("dropout rate must be in [0, 1)")
     return int(np.floor(p * 4294967296.0))
 
 
-def keep_mask(seed: int, M: int, k: int, p: float) -> np.ndarray:
-    """Boolean keep mask of X (M x k) for rate p and a 64-bit seed."""
-    n = M * k
-    blocks = (n + 3) // 4
-    idx = np.arange(blocks, dtype=np.uint64)
-    ctr = np.zeros((blocks, 4), dtype=np.uint32)
+def philox_words(seed: int, first: int, count: int) -> np.ndarray:
+    """The generator's words for flat element indices first .. first+count-1
+    (word e % 4 of the block with counter e // 4)."""
+    b0, b1 = first // 4, (first + count - 1) // 4 + 1
+    idx = np.arange(b0, b1, dtype=np.uint64)
+    ctr = np.zeros((b1 - b0, 4), dtype=np.uint32)
     ctr[:, 0] = (idx & _MASK32).astype(np.uint32)
     ctr[:, 1] = (idx >> np.uint64(32)).astype(np.uint32)
-    out = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)).reshape(-1)[:n]
+    out = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)).reshape(-1)
+    return out[first - 4 * b0:first - 4 * b0 + count]
+
+
+def keep_mask(seed: int, M: int, k: int, p: float) -> np.ndarray:
+    """Boolean keep mask of X (M x k) for rate p and a 64-bit seed."""
+    out = philox_words(seed, 0, M * k)
     return (out >= np.uint32(drop_threshold(p))).reshape(M, k)
 
 
 def forward(Wd, X, A, B, s, keep, p):
-    """Float64 forward with dropout on the adapter input. Returns (Y, H)."""
+    """Float64 forward with dropout on the adapter input (rate p taken as
+    float32, like the keep mask). Returns (Y, H)."""
+    p = rate32(p)
     Wd, X, A, B = (np.asarray(t, dtype=np.float64) for t in (Wd, X, A, B))
     Xd = X * keep / (1.0 - p)
     H = Xd @ A.T
@@ -90,6 +111,7 @@ def forward(Wd, X, A, B, s, keep, p):
 
 def backward(Wd, X, A, B, s, dY, keep, p):
     """Float64 gradients of <dY, Y> for the forward above: (dX, dA, dB, G)."""
+    p = rate32(p)
     Wd, X, A, B, dY = (np.asarray(t, dtype=np.float64) for t in (Wd, X, A, B, dY))
     s = float(s)
     Xd = X * keep / (1.0 - p)

@@ -4,6 +4,9 @@ the generator). H and the all-zero-base dX are sums over the masked inputs,
 so a single mask bit that differs between the two sides shows far above the
 tolerances used here."""
 
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -26,13 +29,16 @@ def ops():
     return o
 
 
+# rates are float32, as the library receives them (the oracle rounds any
+# rate to float32 as well)
+F = np.float32
 CASES = [
     # d, k, M, r, p, seed, w_zero
-    (264, 512, 300, 16, 0.1, 11, False),     # GEMM path
-    (264, 512, 300, 16, 0.1, 11, True),      # GEMM path, LoRA branch alone
-    (704, 1088, 4, 16, 0.05, 12, False),     # GEMV path (decode), ragged slice
-    (704, 1088, 4, 16, 0.05, 12, True),
-    (200, 320, 40, 8, 0.3, 2 ** 40 + 5, True),   # padded ranks, 64-bit seed
+    (264, 512, 300, 16, F(0.1), 11, False),     # GEMM path
+    (264, 512, 300, 16, F(0.1), 11, True),      # GEMM path, LoRA branch alone
+    (704, 1088, 4, 16, F(0.05), 12, False),     # GEMV path (decode), ragged slice
+    (704, 1088, 4, 16, F(0.05), 12, True),
+    (200, 320, 40, 8, F(0.3), 2 ** 40 + 5, True),   # padded ranks, 64-bit seed
 ]
 
 
@@ -113,7 +119,7 @@ def test_q_proj_shape_with_dropout(ops):
     # 4096 x 4096 NF4 + DQ, 2048 tokens, r = 16, alpha = 32, p = 0.05: the
     # training step's shape, every output compared in full
     d = k = 4096
-    M, r, p, seed = 2048, 16, 0.05, 2024
+    M, r, p, seed = 2048, 16, np.float32(0.05), 2024
     print(f"[dropout] q_proj shape p={p}", flush=True)
     inp = synth.linear_inputs(d, k, M, r, idx=31)
     w = ops.quantize(to_dev(inp["W0"]), True)
@@ -148,7 +154,7 @@ def _packed_nibbles(keep):
 def test_stored_mask_equals_redraw(ops, d, k, M, r):
     # the forward stores the keep bits it draws (they are the oracle's bits),
     # and the backward that reads them gives the same bits as one that draws
-    p, seed, alpha = 0.1, 77, 2.0 * r
+    p, seed, alpha = np.float32(0.1), 77, 2.0 * r
     inp = synth.linear_inputs(d, k, M, r, idx=40 + M)
     w = ops.quantize(to_dev(inp["W0"]), True)
     X, A, B, dY = (to_dev(inp[n]) for n in ("X", "A", "B", "dY"))
@@ -197,3 +203,33 @@ def test_short_or_wrong_mask_buffer_is_rejected(ops):
             ops.linear_fwd(w, t["X"], t["A"], t["B"], 16.0, dropout=0.1, seed=1, mask=m)
         with pytest.raises(ValueError):
             ops.linear_bwd(w, t["X"], t["A"], t["B"], 16.0, t["dY"], dropout=0.1, seed=1, mask=m)
+
+
+def _gap_cases():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "dropout_gap.json")
+    with open(path) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _gap_cases(), ids=lambda c: f"p{c['p']}")
+def test_gap_element_dropped_on_gpu(ops, case):
+    # element e's Philox word lies between the float64 and float32 readings
+    # of the threshold (tests/golden/dropout_gap.py): the library takes the
+    # rate as a float, so the keep bit the forward stores there is 0, as the
+    # oracle's; every other stored bit equals the oracle's too
+    M, k, d, r = case["M"], case["k"], 64, 16
+    p, seed, e = np.float32(case["p"]), case["seed"], case["index"]
+    print(f"[dropout-gap] p={case['p']} seed={seed} e={e}", flush=True)
+    inp = synth.linear_inputs(d, k, M, r, idx=50)
+    w = ops.quantize(to_dev(inp["W0"]), True)
+    X, A, B = (to_dev(inp[n]) for n in ("X", "A", "B"))
+    mask = ops.dropout_mask(M, k)
+    mask.fill_(0xFF)
+    ops.linear_fwd(w, X, A, B, 32.0, dropout=p, seed=seed, mask=mask)
+    torch.cuda.synchronize()
+    stored = mask.cpu().numpy()
+    assert (stored[e // 4] >> (e % 4)) & 1 == 0
+    keep = od.keep_mask(seed, M, k, p)
+    assert not keep.reshape(-1)[e]
+    assert np.array_equal(stored, _packed_nibbles(keep))

@@ -3,6 +3,9 @@ known-answer values its authors publish with the generator, the keep rate
 and independence of the mask, gradients by finite differences, and the
 p = 0 case against plain LoRA."""
 
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -46,12 +49,38 @@ def test_keep_rate_and_seed_independence():
 
 
 def test_threshold_and_p_zero():
+    # the rate is the float32 the library receives: fl32(0.05) = 13421773 *
+    # 2^-28, so its threshold is 13421773 * 2^4 (not floor(0.05 * 2^32) =
+    # 214748364); fl32(0.1) = 13421773 * 2^-27, fl32(0.3) = 10066330 * 2^-25
     assert od.drop_threshold(0.0) == 0
-    assert od.drop_threshold(0.05) == 214748364
+    assert od.drop_threshold(0.05) == 13421773 * 16 == 214748368
+    assert od.drop_threshold(0.1) == 13421773 * 32 == 429496736
+    assert od.drop_threshold(0.3) == 10066330 * 128 == 1288490240
     assert od.drop_threshold(0.5) == 2147483648
+    assert od.drop_threshold(np.float32(0.1)) == od.drop_threshold(0.1)
     assert od.keep_mask(7, 3, 64, 0.0).all()
     with pytest.raises(ValueError):
         od.drop_threshold(1.0)
+
+
+def _gap_cases():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "dropout_gap.json")
+    with open(path) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _gap_cases(), ids=lambda c: f"p{c['p']}")
+def test_gap_element_is_dropped(case):
+    # an element whose word lies between the float64 and float32 thresholds
+    # (found by tests/golden/dropout_gap.py): dropped at the float32 rate
+    p, seed, e = case["p"], case["seed"], case["index"]
+    w = int(od.philox_words(seed, e, 1)[0])
+    assert w == case["word"]
+    assert int(np.floor(p * 4294967296.0)) <= w < od.drop_threshold(p)
+    keep = od.keep_mask(seed, case["M"], case["k"], p).reshape(-1)
+    assert not keep[e]
+    assert keep.mean() > 1 - p - 0.01
 
 
 def test_gradients_by_finite_differences():
