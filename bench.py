@@ -141,38 +141,50 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
-    # timed region: HIP events only around the two fused GEMMs (the
-    # candidates for the dominant kernel), on the stream they run on
-    ops.profile_begin(8 * max(1, args.steps), kernels=("gemm_fwd", "gemm_dx"))
+    # timed region: the product library, nothing but the K steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ops.profile_end()
     ms_step = (t1 - t0) * 1e3 / args.steps
     flops = step_flops(M, D, K, R)
     tflops = flops / (ms_step * 1e-3) / 1e12
     log(f"[bench] {ms_step:.3f} ms/step, {tflops:.1f} TFLOP/s")
 
+    # kernel durations: the same K steps again through the timing build of
+    # the same sources (identical kernels; HIP events recorded on the launch
+    # stream around the two fused GEMMs, the candidates for the dominant
+    # kernel), then one more pass with events around every kernel
     kern = {}
-    for name in ("gemm_fwd", "gemm_dx"):
-        cnt, tot = ops.profile_query(name)
-        if cnt:
-            kern[name] = {"launches": cnt, "avg_us": 1e3 * tot / cnt}
-    # per-kernel breakdown of the other kernels: a separate, untimed pass
-    ops.profile_begin(64 * max(1, args.steps))
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ops.profile_end()
-    for name in ops.KERNELS:
-        if name in kern:
-            continue
-        cnt, tot = ops.profile_query(name)
-        if cnt:
-            kern[name] = {"launches": cnt, "avg_us": 1e3 * tot / cnt}
+    with ops.timing_build():
+        for _ in range(25):
+            step()
+        torch.cuda.synchronize()
+        ops.profile_begin(8 * max(1, args.steps), kernels=("gemm_fwd", "gemm_dx"))
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        ops.profile_end()
+        ms_step_timed = (t3 - t2) * 1e3 / args.steps
+        for name in ("gemm_fwd", "gemm_dx"):
+            cnt, tot = ops.profile_query(name)
+            if cnt:
+                kern[name] = {"launches": cnt, "avg_us": 1e3 * tot / cnt}
+        ops.profile_begin(64 * max(1, args.steps))
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        ops.profile_end()
+        for name in ops.KERNELS:
+            if name in kern:
+                continue
+            cnt, tot = ops.profile_query(name)
+            if cnt:
+                kern[name] = {"launches": cnt, "avg_us": 1e3 * tot / cnt}
     fwd_gemm_flops = 2 * M * D * K + 2 * M * R * D
     dx_gemm_flops = 2 * M * D * K + 2 * M * R * K
     cand = [("gemm_fwd", fwd_gemm_flops, "gemm.hip"), ("gemm_dx", dx_gemm_flops, "gemm.hip")]
@@ -184,7 +196,8 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic_for(dom[0], digest),
-                "algorithmic_flops_per_launch": dom[1], "avg_launch_us": round(avg_s * 1e6, 2)}
+                "algorithmic_flops_per_launch": dom[1], "avg_launch_us": round(avg_s * 1e6, 2),
+                "events_pass_ms_per_step": round(ms_step_timed, 4)}
 
     rows = measure_rows(ops, synth, torch, dev) if args.rows == "on" else None
     if rows is not None:
@@ -302,10 +315,13 @@ def _row(nbytes, call_ms, kernel_us):
 
 def _kernel_us(ops, name, fn, n_sets, iters):
     """Average event-bracketed duration of library kernel `name` over iters
-    calls of fn (a separate pass from the call timing)."""
-    ops.profile_begin(64 * iters, kernels=(name,))
-    _rotated(fn, n_sets, iters)
-    ops.profile_end()
+    calls of fn (a separate pass from the call timing, through the timing
+    build of the library)."""
+    with ops.timing_build():
+        _rotated(fn, n_sets, 2)
+        ops.profile_begin(64 * iters, kernels=(name,))
+        _rotated(fn, n_sets, iters)
+        ops.profile_end()
     c, t = ops.profile_query(name)
     return 1e3 * t / c if c else float("nan")
 
@@ -528,6 +544,25 @@ def measure_probes(torch, dev):
     return out
 
 
+def _oracle_threads(n):
+    """Context in which the oracle's BLAS/OpenMP pools use n threads."""
+    from threadpoolctl import threadpool_limits
+    return threadpool_limits(limits=n)
+
+
+def _cpu_model():
+    """The host CPU's model name as lscpu reports it."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for ln in out.splitlines():
+        if ln.strip().startswith("Model name:"):
+            return ln.split(":", 1)[1].strip()
+    return None
+
+
 def cpu_baseline(inp, flops):
     """The CPU oracle (as it stands) on the host cores: one full step of the
     workload (oracle dequantisation of W0 plus float64 forward and backward on
@@ -536,35 +571,28 @@ def cpu_baseline(inp, flops):
     import numpy as np
     from oracle import lora as olora
     from oracle import nf4 as onf4
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    log(f"[bench] cpu oracle baseline on {cores} threads")
+    # the CPUs this process may run on; the pools are capped at the share a
+    # launcher grants through OMP_NUM_THREADS, and `cores` is what was used
+    affinity = len(os.sched_getaffinity(0))
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    cores = min(affinity, share) if share > 0 else affinity
+    log(f"[bench] cpu oracle baseline on {cores} threads ({affinity} CPUs in the affinity set)")
     qw = onf4.quantize_weight(inp["W0"], True)
     s = olora.lora_scale(ALPHA, R)
     widen = lambda b: onf4.bf16_bits_to_f32(b).astype(np.float64)
     X, A, B, dY = (widen(inp[n]) for n in ("X", "A", "B", "dY"))
     times = []
-    for _ in range(3):
-        t0 = time.perf_counter()
-        Wd = widen(onf4.dequantize_weight(qw)).reshape(D, K)
-        Yo, Ho = olora.forward(Wd, X, A, B, s)
-        olora.backward(Wd, X, A, B, s, dY)
-        times.append(time.perf_counter() - t0)
+    with _oracle_threads(cores):
+        for _ in range(3):
+            t0 = time.perf_counter()
+            Wd = widen(onf4.dequantize_weight(qw)).reshape(D, K)
+            Yo, Ho = olora.forward(Wd, X, A, B, s)
+            olora.backward(Wd, X, A, B, s, dY)
+            times.append(time.perf_counter() - t0)
     t = statistics.median(times)
-    model = None
-    try:
-        with open("/proc/cpuinfo") as f:
-            for ln in f:
-                if ln.startswith("model name"):
-                    model = ln.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
+    model = _cpu_model()
     return {"value": round(flops / t / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle", "cpu_model": model,
+            "affinity_cpus": affinity, "kind": "oracle", "cpu_model": model,
             "sample": "one full step of the workload (oracle dequantise + float64 forward "
                       f"and backward, 2048 tokens), median of 3 runs: {t:.2f} s"}
 

@@ -1,6 +1,12 @@
-"""Build libqlora_nf4.so for gfx950 from csrc/*.hip (in-tree).
+"""Build the gfx950 HIP libraries from csrc/ (in-tree).
 
     python -m bit_nf4_quantized_19_amd.build        # or build() from Python
+
+libqlora_nf4.so is the product: csrc/*.hip, declared in include/qlora_nf4.h.
+libqlora_nf4_timing.so is a measurement build of the same sources compiled
+with QLORA_KERNEL_TIMING plus csrc/timing/*.hip: identical kernels and entry
+points, each launch bracketed by HIP events on request
+(include/qlora_nf4_timing.h). Only the benchmark loads it.
 
 Each translation unit is compiled by hipcc in parallel, then linked into one
 shared library next to this file. Floating-point contraction is disabled
@@ -21,39 +27,53 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqlora_nf4.so")
+TIMING_LIB = os.path.join(HERE, "libqlora_nf4_timing.so")
 OBJ = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-fvisibility=hidden",
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+def _compile(job) -> str:
+    src, variant, extra = job
+    os.makedirs(os.path.join(OBJ, variant), exist_ok=True)
+    obj = os.path.join(OBJ, variant, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{p.stdout}\n{p.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
-    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stdout}\n{p.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, timing: bool = True) -> str:
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    jobs = [(s, "product", []) for s in srcs]
+    if timing:
+        tsrcs = srcs + sorted(glob.glob(os.path.join(CSRC, "timing", "*.hip")))
+        jobs += [(s, "timing", ["-DQLORA_KERNEL_TIMING"]) for s in tsrcs]
+    workers = max(1, min(len(jobs), 8, os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(srcs)], LIB)
     if verbose:
         print("built", LIB)
+    if timing:
+        _link(objs[len(srcs):], TIMING_LIB)
+        if verbose:
+            print("built", TIMING_LIB)
     return LIB
 
 

@@ -142,15 +142,18 @@ struct AdamScalars {
 qlora_status launch_adamw(float *p, float *m, float *v, const uint16_t *g, uint16_t *out,
                           int64_t n, const AdamScalars &s, hipStream_t st);
 
-// compute units of the current device (capi.hip; queried once, 256 if the
-// query fails)
+// compute units of the current device (capi.hip; queried on every call, 256
+// if the query fails)
 int ql_num_cus();
 
 // tables (quantize.hip)
 void host_codebook(float levels[16], float thresholds[15]);
 
-// Event bracketing of kernel launches (capi.hip). prof_begin returns a slot
-// (or -1 when profiling is off/full); prof_end records the closing event.
+// Kernel timing. The product library compiles QlProf to nothing; the timing
+// build (QLORA_KERNEL_TIMING, libqlora_nf4_timing.so) brackets each launch
+// with HIP events (timing/hooks.hip, API in include/qlora_nf4_timing.h).
+#include "../../include/qlora_nf4_timing.h"
+#ifdef QLORA_KERNEL_TIMING
 int ql_prof_begin(int kernel_id, hipStream_t st);
 void ql_prof_end(int slot, hipStream_t st);
 struct QlProf {
@@ -159,3 +162,8 @@ struct QlProf {
   QlProf(int kid, hipStream_t s) : slot(ql_prof_begin(kid, s)), st(s) {}
   ~QlProf() { ql_prof_end(slot, st); }
 };
+#else
+struct QlProf {
+  QlProf(int, hipStream_t) {}
+};
+#endif

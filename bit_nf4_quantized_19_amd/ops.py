@@ -10,8 +10,8 @@ bf16 tensors are ``torch.bfloat16`` (passed as their uint16 bit patterns).
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 
@@ -19,6 +19,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
+#: measurement build of the same sources with per-launch HIP events
+#: (include/qlora_nf4_timing.h); loaded only inside ``timing_build()``
+TIMING_LIB_PATH = os.path.join(_HERE, "libqlora_nf4_timing.so")
 
 QLORA_OK, QLORA_ERR_INVALID_ARG, QLORA_ERR_UNSUPPORTED, QLORA_ERR_WORKSPACE, QLORA_ERR_HIP = (
     0, -1, -2, -3, -4)
@@ -43,6 +46,8 @@ class NF4WeightC(ctypes.Structure):
 
 
 _lib = None
+_timing_lib = None
+_use_timing = False
 _vp, _i64, _i32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                               ctypes.c_float, ctypes.c_size_t)
 _PW = ctypes.POINTER(NF4WeightC)
@@ -71,34 +76,65 @@ SIGNATURES = {
     "qlora_nf4_codebook": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float),
                                           ctypes.POINTER(ctypes.c_float)]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "qlora_adamw_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
+}
+
+#: the timing build's extra symbols; mirrors include/qlora_nf4_timing.h
+TIMING_SIGNATURES = {
     "qlora_profile_begin": (ctypes.c_int, [_i32, ctypes.c_uint32]),
     "qlora_profile_end": (ctypes.c_int, []),
     "qlora_profile_query": (ctypes.c_int, [_i32, ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_double)]),
     "qlora_profile_release": (ctypes.c_int, []),
-    "qlora_adamw_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
 }
 
-#: kernel ids of the timing hooks (QLORA_K_* in the header)
+#: kernel ids of the timing hooks (QLORA_K_* in include/qlora_nf4_timing.h)
 KERNELS = ["quantize", "double_quant", "dequantize", "gemm_fwd", "gemm_dx", "gemv",
            "gemv_epilogue", "lora_down", "lora_reduce", "lora_colacc", "lora_colacc_reduce",
            "merge", "layout", "adamw", "loftq_product", "loftq_small", "residual"]
 
 
+def _load(path: str, signatures: dict) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing; build it with "
+                          "`python -m bit_nf4_quantized_19_amd.build`")
+    L = ctypes.CDLL(path)
+    for name, (res, args) in signatures.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
 def lib() -> ctypes.CDLL:
-    """Load the shared library (once). Raises if it is not built."""
+    """The library every call goes through: the product build, or the timing
+    build inside ``timing_build()``. Loaded once; raises if it is not built."""
     global _lib
+    if _use_timing:
+        return timing_lib()
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing; build it with "
-                              "`python -m bit_nf4_quantized_19_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(L, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = L
+        _lib = _load(LIB_PATH, SIGNATURES)
     return _lib
+
+
+def timing_lib() -> ctypes.CDLL:
+    """The timing build (same kernels and entry points plus qlora_profile_*)."""
+    global _timing_lib
+    if _timing_lib is None:
+        _timing_lib = _load(TIMING_LIB_PATH, {**SIGNATURES, **TIMING_SIGNATURES})
+    return _timing_lib
+
+
+@contextlib.contextmanager
+def timing_build():
+    """Route every call of this module to the timing build while inside."""
+    global _use_timing
+    prev = _use_timing
+    _use_timing = True
+    try:
+        yield timing_lib()
+    finally:
+        _use_timing = prev
 
 
 def status_string(status: int) -> str:
@@ -420,35 +456,31 @@ def adamw_step(param: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Ten
 
 
 def profile_begin(cap: int = 4096, kernels=None):
-    """Start bracketing kernel launches with HIP events (see the header);
+    """Start bracketing kernel launches of the timing build with HIP events
+    (include/qlora_nf4_timing.h); only calls made inside ``timing_build()``
+    are seen;
     ``kernels`` (names from KERNELS) limits the bracketing to those kernels."""
     mask = 0
     for name in kernels or ():
         mask |= 1 << KERNELS.index(name)
-    _check(lib().qlora_profile_begin(int(cap), mask), "qlora_profile_begin")
+    _check(timing_lib().qlora_profile_begin(int(cap), mask), "qlora_profile_begin")
 
 
 def profile_end():
-    _check(lib().qlora_profile_end(), "qlora_profile_end")
+    _check(timing_lib().qlora_profile_end(), "qlora_profile_end")
 
 
 def profile_query(kernel: str):
     """(launch count, total milliseconds) of a kernel since profile_begin."""
     cnt = ctypes.c_int32(0)
     ms = ctypes.c_double(0.0)
-    _check(lib().qlora_profile_query(KERNELS.index(kernel), ctypes.byref(cnt),
+    _check(timing_lib().qlora_profile_query(KERNELS.index(kernel), ctypes.byref(cnt),
                                      ctypes.byref(ms)), "qlora_profile_query")
     return int(cnt.value), float(ms.value)
 
 
-def lora_scale(alpha: float, r: int) -> float:
-    """fl32(alpha / r), the scale the kernels apply."""
-    import numpy as np
-    return float(np.float32(np.float32(alpha) / np.float32(r)))
-
-
 __all__ = ["NF4Weight", "QLoRAError", "quantize", "dequantize", "linear_fwd", "linear_bwd",
-           "merge", "storage_bytes", "workspace_bytes", "codebook", "lib", "lora_scale",
+           "merge", "storage_bytes", "workspace_bytes", "codebook", "lib",
            "OP_QUANTIZE", "OP_FWD", "OP_BWD", "SIGNATURES", "LIB_PATH", "KERNELS",
-           "profile_begin", "profile_end", "profile_query"]
-_ = math
+           "profile_begin", "profile_end", "profile_query", "timing_build", "timing_lib",
+           "TIMING_LIB_PATH"]

@@ -35,6 +35,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Symbols of the C ABI; everything else in the library is hidden. */
+#if defined(__GNUC__) || defined(__clang__)
+#define QLORA_API __attribute__((visibility("default")))
+#else
+#define QLORA_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -99,7 +106,7 @@ enum { QLORA_OP_QUANTIZE = 0, QLORA_OP_FWD = 1, QLORA_OP_BWD = 2, QLORA_OP_FWD_M
  * Non-finite weights are outside the method's domain; their codes are
  * unspecified.
  */
-qlora_status qlora_nf4_quantize(const uint16_t *W0, const qlora_nf4_weight *w,
+QLORA_API qlora_status qlora_nf4_quantize(const uint16_t *W0, const qlora_nf4_weight *w,
                                 void *ws, size_t ws_bytes, void *stream);
 
 /*
@@ -108,7 +115,7 @@ qlora_status qlora_nf4_quantize(const uint16_t *W0, const qlora_nf4_weight *w,
  * before the matrix product; LLM tutorial ch. 3, 3.8: dequantise to bf16
  * before merging). Bit-exact.
  */
-qlora_status qlora_nf4_dequantize(const qlora_nf4_weight *w, uint16_t *W_out,
+QLORA_API qlora_status qlora_nf4_dequantize(const qlora_nf4_weight *w, uint16_t *W_out,
                                   void *stream);
 
 /*
@@ -119,7 +126,7 @@ qlora_status qlora_nf4_dequantize(const qlora_nf4_weight *w, uint16_t *W_out,
  * memory-bound GEMV kernel, larger M the fused dequant-GEMM.
  * Workspace: qlora_workspace_bytes(QLORA_OP_FWD, d, k, M, r, dq) bytes.
  */
-qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X,
+QLORA_API qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X,
                               int64_t M, const uint16_t *A, const uint16_t *B,
                               int32_t r, float lora_alpha, uint16_t *Y,
                               float *H_save, void *ws, size_t ws_bytes,
@@ -154,7 +161,7 @@ typedef struct qlora_lora_dropout {
 } qlora_lora_dropout;
 
 /* qlora_linear_fwd with adapter-input dropout (workspace as for QLORA_OP_FWD). */
-qlora_status qlora_linear_fwd_ex(const qlora_nf4_weight *w, const uint16_t *X,
+QLORA_API qlora_status qlora_linear_fwd_ex(const qlora_nf4_weight *w, const uint16_t *X,
                                  int64_t M, const uint16_t *A, const uint16_t *B,
                                  int32_t r, float lora_alpha,
                                  const qlora_lora_dropout *dropout, uint16_t *Y,
@@ -177,7 +184,7 @@ qlora_status qlora_linear_fwd_ex(const qlora_nf4_weight *w, const uint16_t *X,
  * separate qlora_linear_fwd calls.
  * Workspace: qlora_workspace_bytes(QLORA_OP_FWD_MULTI, sum of d_i, k, M, r, dq).
  */
-qlora_status qlora_linear_fwd_multi(const qlora_nf4_weight *const *w, int32_t nw,
+QLORA_API qlora_status qlora_linear_fwd_multi(const qlora_nf4_weight *const *w, int32_t nw,
                                     const uint16_t *X, int64_t M,
                                     const uint16_t *const *A, const uint16_t *const *B,
                                     int32_t r, float lora_alpha, uint16_t *const *Y,
@@ -195,7 +202,7 @@ qlora_status qlora_linear_fwd_multi(const qlora_nf4_weight *const *w, int32_t nw
  * H is the float32 X A^T saved by the forward, or NULL to recompute it.
  * Workspace: qlora_workspace_bytes(QLORA_OP_BWD, d, k, M, r, dq) bytes.
  */
-qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X,
+QLORA_API qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X,
                               int64_t M, const uint16_t *A, const uint16_t *B,
                               int32_t r, float lora_alpha, const uint16_t *dY,
                               const float *H, uint16_t *dX, uint16_t *dA,
@@ -205,7 +212,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X,
 /* qlora_linear_bwd for a forward run with adapter-input dropout (same p and
  * seed); H, if passed, is the H_save of that forward. Workspace as for
  * QLORA_OP_BWD. */
-qlora_status qlora_linear_bwd_ex(const qlora_nf4_weight *w, const uint16_t *X,
+QLORA_API qlora_status qlora_linear_bwd_ex(const qlora_nf4_weight *w, const uint16_t *X,
                                  int64_t M, const uint16_t *A, const uint16_t *B,
                                  int32_t r, float lora_alpha,
                                  const qlora_lora_dropout *dropout, const uint16_t *dY,
@@ -218,7 +225,7 @@ qlora_status qlora_linear_bwd_ex(const qlora_nf4_weight *w, const uint16_t *X,
  * in float32 (Day-25 notes 2.6 and 6.2; LLM tutorial ch. 3, 3.8: a 4-bit base
  * is dequantised to bf16 and then merged).
  */
-qlora_status qlora_merge(const qlora_nf4_weight *w, const uint16_t *A,
+QLORA_API qlora_status qlora_merge(const qlora_nf4_weight *w, const uint16_t *A,
                          const uint16_t *B, int32_t r, float lora_alpha,
                          uint16_t *W_merged, void *stream);
 
@@ -256,7 +263,7 @@ qlora_status qlora_merge(const qlora_nf4_weight *w, const uint16_t *A,
 typedef struct qlora_adamw_hparams {
   double lr, beta1, beta2, eps, weight_decay;
 } qlora_adamw_hparams;
-qlora_status qlora_adamw_step(float *param, float *exp_avg, float *exp_avg_sq,
+QLORA_API qlora_status qlora_adamw_step(float *param, float *exp_avg, float *exp_avg_sq,
                               const uint16_t *grad, uint16_t *param_bf16, int64_t n,
                               const qlora_adamw_hparams *hp, int64_t step, void *stream);
 
@@ -294,11 +301,11 @@ qlora_status qlora_adamw_step(float *param, float *exp_avg, float *exp_avg_sq,
  * MB). All outputs are written
  * on `stream`; results are deterministic.
  */
-qlora_status qlora_nf4_quantize_residual(const uint16_t *W, const uint16_t *A,
+QLORA_API qlora_status qlora_nf4_quantize_residual(const uint16_t *W, const uint16_t *A,
                                          const uint16_t *B, int32_t r, float lora_alpha,
                                          const qlora_nf4_weight *out, void *ws,
                                          size_t ws_bytes, void *stream);
-qlora_status qlora_loftq_init(const uint16_t *W, const float *omega, int32_t r,
+QLORA_API qlora_status qlora_loftq_init(const uint16_t *W, const float *omega, int32_t r,
                               float lora_alpha, int32_t iters, int32_t power_iters,
                               const qlora_nf4_weight *out, uint16_t *A, uint16_t *B,
                               float *sigma, void *ws, size_t ws_bytes, void *stream);
@@ -306,44 +313,20 @@ qlora_status qlora_loftq_init(const uint16_t *W, const float *omega, int32_t r,
 /* Bytes of the quantised record for d x k: d*k/2 + 4*nb (no double quant)
  * or d*k/2 + nb + 4*ceil(nb/256) + 4 (double quant), nb = d*k/64.
  * Returns 0 for an unsupported shape. */
-size_t qlora_nf4_storage_bytes(int64_t d, int64_t k, int32_t double_quant);
+QLORA_API size_t qlora_nf4_storage_bytes(int64_t d, int64_t k, int32_t double_quant);
 
 /* Device workspace in bytes for `op` (QLORA_OP_*); 0 means none needed.
  * Returns (size_t)-1 for an unsupported shape. */
-size_t qlora_workspace_bytes(int32_t op, int64_t d, int64_t k, int64_t M,
+QLORA_API size_t qlora_workspace_bytes(int32_t op, int64_t d, int64_t k, int64_t M,
                              int32_t r, int32_t double_quant);
 
 /* Host copy of the constant tables compiled into the kernels: the 16 NF4
  * levels (ascending) and the 15 code thresholds T_i (code = #{i: x > T_i}).
  * Touches no device; for inspection and tests. Returns QLORA_OK. */
-qlora_status qlora_nf4_codebook(float levels[16], float thresholds[15]);
+QLORA_API qlora_status qlora_nf4_codebook(float levels[16], float thresholds[15]);
 
 /* Static text for a status code. */
-const char *qlora_status_string(int status);
-
-/*
- * Kernel timing with HIP events (measurement support; not part of the
- * method). Between qlora_profile_begin(cap, mask) and qlora_profile_end(),
- * every launch of a kernel whose id bit is set in `mask` (bit QLORA_K_* ;
- * 0 = all) is bracketed by two hipEvents recorded on the launch stream, up
- * to `cap` launches; other launches get no events. qlora_profile_query
- * waits for the recorded events and returns the number of launches of
- * kernel `kernel_id` (QLORA_K_*) and their summed duration in milliseconds.
- * Not thread-safe; intended for one benchmarking thread. begin() creates the
- * events (host call, may allocate); release() destroys them.
- */
-enum {
-  QLORA_K_QUANTIZE = 0, QLORA_K_DOUBLE_QUANT = 1, QLORA_K_DEQUANTIZE = 2,
-  QLORA_K_GEMM_FWD = 3, QLORA_K_GEMM_DX = 4, QLORA_K_GEMV = 5, QLORA_K_GEMV_EPILOGUE = 6,
-  QLORA_K_LORA_DOWN = 7, QLORA_K_LORA_REDUCE = 8, QLORA_K_LORA_COLACC = 9,
-  QLORA_K_LORA_COLACC_REDUCE = 10, QLORA_K_MERGE = 11, QLORA_K_LAYOUT = 12,
-  QLORA_K_ADAMW = 13, QLORA_K_LOFTQ_PRODUCT = 14, QLORA_K_LOFTQ_SMALL = 15,
-  QLORA_K_RESIDUAL = 16, QLORA_K_COUNT = 17
-};
-qlora_status qlora_profile_begin(int32_t cap, uint32_t mask);
-qlora_status qlora_profile_end(void);
-qlora_status qlora_profile_query(int32_t kernel_id, int32_t *count, double *total_ms);
-qlora_status qlora_profile_release(void);
+QLORA_API const char *qlora_status_string(int status);
 
 #ifdef __cplusplus
 }

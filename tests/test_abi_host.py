@@ -16,6 +16,7 @@ from oracle import nf4
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+TIMING_HEADER = os.path.join(ROOT, "include", "qlora_nf4_timing.h")
 
 
 def _ops():
@@ -25,20 +26,52 @@ def _ops():
     return ops
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+def _exported(path):
+    """Dynamic symbols a shared library defines (nm -D --defined-only)."""
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
+                         text=True, check=True).stdout
+    return {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
 
 
 def test_library_exports_every_declared_symbol():
     ops = _ops()
     L = ops.lib()
     names = _declared_functions()
-    assert len(names) == 19
+    assert len(names) == 15
     for name in names:
         assert hasattr(L, name), name
         assert name in ops.SIGNATURES, name
+
+
+def test_product_library_has_no_timing_state():
+    # the event-timing hooks live only in the measurement build
+    ops = _ops()
+    timing = _declared_functions(TIMING_HEADER)
+    assert timing == ["qlora_profile_begin", "qlora_profile_end", "qlora_profile_query",
+                      "qlora_profile_release"]
+    prod = _exported(ops.LIB_PATH)
+    assert not any(n.startswith("qlora_profile") or "prof" in n for n in prod), \
+        sorted(n for n in prod if "prof" in n)
+    if not os.path.exists(ops.TIMING_LIB_PATH):
+        pytest.fail("libqlora_nf4_timing.so is not built (run __graft_entry__.build())")
+    tsyms = _exported(ops.TIMING_LIB_PATH)
+    for name in _declared_functions() + timing:
+        assert name in tsyms, name
+        assert name in {**ops.SIGNATURES, **ops.TIMING_SIGNATURES}, name
+    # the timing calls need no device: begin with an empty mask range, query, end
+    T = ops.timing_lib()
+    cnt, ms = ctypes.c_int32(-1), ctypes.c_double(-1.0)
+    assert T.qlora_profile_begin(0, 0) == ops.QLORA_ERR_INVALID_ARG
+    assert T.qlora_profile_query(3, None, ctypes.byref(ms)) == ops.QLORA_ERR_INVALID_ARG
+    assert T.qlora_profile_end() == 0
+    assert T.qlora_profile_query(3, ctypes.byref(cnt), ctypes.byref(ms)) == 0
+    assert cnt.value == 0 and ms.value == 0.0
 
 
 def test_compiled_levels_equal_oracle_levels():
