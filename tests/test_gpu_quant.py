@@ -125,6 +125,42 @@ def test_quantize_exhaustive_bf16_sweep_dq(ops):
     _check_exact(ops, _sweep_weight(), True)
 
 
+def _significand_sweep():
+    """For every bf16 significand of the block absmax a (the 128 normal ones
+    at exponents 2^-126 (smallest normal), 2^-100, 2^-91 (rescaled before the
+    code search), 2^-90 (the first exponent that is not), 2^0 and 2^127
+    (largest), and the 127 subnormal ones), every finite bf16 w with
+    |w| <= a, both signs, in blocks of 64 led by a itself. The kernel's code
+    decision depends on the significand of a and, through the rescale and
+    the float32 range, on its exponent; at 2^0 and 2^127 the w run over every
+    exponent below a's."""
+    all_bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = all_bits[(all_bits & 0x7F80) != 0x7F80]
+    mags = np.abs(onf4.bf16_bits_to_f32(vals))
+    order = np.argsort(mags, kind="stable")
+    vals, mags = vals[order], mags[order]
+    a_list = [((e + 127) << 7) | m for e in (-126, -100, -91, -90, 0, 127) for m in range(128)]
+    a_list += list(range(1, 128))                 # subnormal significands
+    rows = []
+    for a_bits in a_list:
+        a = onf4.bf16_bits_to_f32(np.array([a_bits], np.uint16))[0]
+        sel = vals[:np.searchsorted(mags, a, side="right")]
+        n63 = -(-sel.size // 63) * 63
+        body = np.concatenate([sel, np.zeros(n63 - sel.size, np.uint16)]).reshape(-1, 63)
+        rows.append(np.concatenate([np.full((body.shape[0], 1), a_bits, np.uint16), body], 1))
+    blocks = np.concatenate(rows)
+    nblk = -(-blocks.shape[0] // 64) * 64         # rows of 512: d % 8 == 0
+    blocks = np.concatenate([blocks, np.zeros((nblk - blocks.shape[0], 64), np.uint16)])
+    return blocks.reshape(-1, 512)
+
+
+@pytest.mark.parametrize("dq", [False, True])
+def test_quantize_every_absmax_significand(ops, dq):
+    W = _significand_sweep()
+    print(f"[quant-sweep] {W.size} weights, {W.size // 64} blocks", flush=True)
+    _check_exact(ops, W, dq)
+
+
 def test_quantize_is_deterministic(ops):
     W = synth.normal_bf16((4096, 4096), 0.02, synth.SEED_W0 + 1)
     a = _gpu_quant(ops, W, True)
