@@ -15,6 +15,16 @@ a LoRA path that drops a rank or a slice of H. These tests isolate it:
 * H (the float32 X A^T the forward saves) directly, at 1e-5;
 * an all-zero base at full size, where Y = bf16(s H B^T) and
   dX = bf16(s G A) are the rank-r term alone.
+
+The decode GEMV (M <= 16) applies each block's scale a' to the 64-term
+partial sum of bf16 levels times X instead of multiplying by the bf16-rounded
+w' = bf16(level * a'), so its base differs from the oracle's by ~0.1-0.2% of
+|Y| (well inside 2e-2) and the two roundings of its delta no longer cancel
+against the oracle's. There the rank-r term is pinned by H at 1e-5 (every
+slice of k contributes to it), by the all-zero base at full size at 2e-2,
+and, where Y has at least 4096 outputs, by the delta against the unrounded
+s H B^T at 0.15, a bar set by the two bf16 roundings (measured 6-9% on these
+shapes; one of 16 ranks dropped gives ~0.25).
 """
 
 import numpy as np
@@ -125,25 +135,43 @@ def test_q_proj_zero_base(ops):
 
 # ---- decode-shaped GEMV: gate/up 4096 -> 11008, down 11008 -> 4096 --------
 _W = {}
+GEMV_DELTA_BAR = 0.15
 
 
 def _gemv_weight(ops, d, k):
     if (d, k) not in _W:
         W0 = synth.normal_bf16((d, k), 0.02, synth.SEED_W0 + 7 + d)
         _W[(d, k)] = (ops.quantize(to_dev(W0), True),
-                      oracle_wdeq(oracle_quant(W0, True), d, k))
+                      oracle_wdeq(oracle_quant(W0, True), d, k),
+                      ops.quantize(torch.zeros(d, k, dtype=torch.bfloat16, device="cuda"), True))
     return _W[(d, k)]
+
+
+def _check_gemv_term(ops, w, wz, Wd, inp, alpha, r):
+    g = _gpu_pair(ops, w, inp, alpha, bwd=False)
+    X, A, B = (to_dev(inp[n]) for n in ("X", "A", "B"))
+    Yz, _ = ops.linear_fwd(wz, X, A, B, alpha)
+    torch.cuda.synchronize()
+    o = _oracle_parts(Wd, inp, alpha, r, False)
+    errs = {"H": rel_frob(g["H"], o["H"]),
+            "Y": rel_frob(g["Y"], o["Ybase"] + o["Ylora"]),
+            "zero_base": rel_frob(_host(Yz), o["Ylora"]),
+            "delta_unrounded": rel_frob(g["Y"] - g["Y0"], o["Ylora"])}
+    print("  ", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert errs["H"] < 1e-5, errs
+    assert np.array_equal(g["H"], g["H0"])
+    assert errs["Y"] <= TOL and errs["zero_base"] <= TOL, errs
+    if g["Y"].size >= 4096:   # the noise bar is an rms over many outputs
+        assert errs["delta_unrounded"] <= GEMV_DELTA_BAR, errs
 
 
 @pytest.mark.parametrize("d,k", [(11008, 4096), (4096, 11008)])
 @pytest.mark.parametrize("M", [1, 4, 16])
-def test_decode_gemv_lora_delta(ops, d, k, M):
-    print(f"[lora-delta gemv] d={d} k={k} M={M}", flush=True)
-    w, Wd = _gemv_weight(ops, d, k)
+def test_decode_gemv_lora_term(ops, d, k, M):
+    print(f"[lora-term gemv] d={d} k={k} M={M}", flush=True)
+    w, Wd, wz = _gemv_weight(ops, d, k)
     inp = synth.linear_inputs(d, k, M, 16, idx=M + 3, with_dy=False)
-    g = _gpu_pair(ops, w, inp, 32.0, bwd=False)
-    o = _oracle_parts(Wd, inp, 32.0, 16, False)
-    _check_delta(g, o, bwd=False)
+    _check_gemv_term(ops, w, wz, Wd, inp, 32.0, 16)
 
 
 # ---- GEMV slices of 1024 columns: full, ragged last slice, absmax path ----
@@ -155,10 +183,10 @@ def test_decode_gemv_lora_delta(ops, d, k, M):
     (8, 960, 16, True),           # one partial slice of 15 blocks
     (64, 11008, 4, True),         # eleven slices, the last one ragged
 ])
-def test_gemv_slices_lora_delta(ops, d, k, M, dq):
-    print(f"[lora-delta slices] d={d} k={k} M={M} dq={dq}", flush=True)
+def test_gemv_slices_lora_term(ops, d, k, M, dq):
+    print(f"[lora-term slices] d={d} k={k} M={M} dq={dq}", flush=True)
     inp = synth.linear_inputs(d, k, M, 16, idx=d + k + M, with_dy=False)
     w = ops.quantize(to_dev(inp["W0"]), dq)
-    g = _gpu_pair(ops, w, inp, 32.0, bwd=False)
-    o = _oracle_parts(oracle_wdeq(oracle_quant(inp["W0"], dq), d, k), inp, 32.0, 16, False)
-    _check_delta(g, o, bwd=False)
+    wz = ops.quantize(torch.zeros(d, k, dtype=torch.bfloat16, device="cuda"), dq)
+    Wd = oracle_wdeq(oracle_quant(inp["W0"], dq), d, k)
+    _check_gemv_term(ops, w, wz, Wd, inp, 32.0, 16)
