@@ -66,6 +66,8 @@ SIGNATURES = {
                                            _vp, _vp, _vp, _vp, _sz, _vp]),
     "qlora_linear_fwd_multi": (ctypes.c_int, [_vp, _i32, _vp, _i64, _vp, _vp, _i32, _f32, _vp,
                                               _vp, _vp, _sz, _vp]),
+    "qlora_linear_fwd_noalloc": (ctypes.c_int, [_PW, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp,
+                                                _vp]),
     "qlora_merge": (ctypes.c_int, [_PW, _vp, _vp, _i32, _f32, _vp, _vp]),
     "qlora_nf4_quantize_residual": (ctypes.c_int, [_vp, _vp, _vp, _i32, _f32, _PW, _vp, _sz,
                                                    _vp]),
@@ -339,6 +341,25 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                                       _ptr(H) if save_h else None, _ptr(wst), wsn,
                                       _stream(stream)), "qlora_linear_fwd")
     return Y, (H if save_h else None)
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def linear_fwd_noalloc(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                       lora_alpha: float, Y: torch.Tensor, H: torch.Tensor | None = None,
+                       stream=None):
+    """qlora_linear_fwd_noalloc: the forward into caller-given Y (and H)
+    with the library's own 16 MiB device scratch instead of a workspace
+    (nothing is allocated by the library or here)."""
+    for t, nm in ((X, "X"), (A, "A"), (B, "B"), (Y, "Y")):
+        _dev_bf16(t, nm)
+    cw = w.c_struct()
+    _check(lib().qlora_linear_fwd_noalloc(ctypes.byref(cw), X.data_ptr(), X.shape[0],
+                                          A.data_ptr(), B.data_ptr(), A.shape[0],
+                                          float(lora_alpha), Y.data_ptr(), _ptr(H),
+                                          _stream(stream)), "qlora_linear_fwd_noalloc")
+    return Y, H
 
 
 def linear_fwd_multi(ws_: list, X: torch.Tensor, As: list, Bs: list, lora_alpha: float,

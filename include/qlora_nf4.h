@@ -192,6 +192,32 @@ QLORA_API qlora_status qlora_linear_fwd_multi(const qlora_nf4_weight *const *w, 
                                     void *stream);
 
 /*
+ * qlora_linear_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same computation, arguments and results as qlora_linear_fwd (bit-identical
+ * outputs), but without a workspace argument: the scratch comes from a
+ * device array of QLORA_NOALLOC_SCRATCH_BYTES (16 MiB) inside the library,
+ * one per device, allocated when the library is loaded and held until the
+ * process ends. The call allocates nothing (no hipMalloc, no library
+ * allocation). It uses the array of the current device (hipGetDevice); the
+ * stream must belong to that device. Every call on a device shares its
+ * array, so calls on one device that overlap in time (different streams,
+ * threads, or graphs replayed concurrently) race and give undefined results;
+ * calls ordered on one stream do not. Each call writes every scratch word it
+ * reads; nothing carries over between calls.
+ * Returns QLORA_ERR_WORKSPACE, before any launch, when the forward's
+ * workspace for this shape (qlora_workspace_bytes(QLORA_OP_FWD, ...)) exceeds
+ * 16 MiB -- every decode shape (M <= 16) up to 22016 x 8192 at r = 128 and
+ * the GEMM path up to M * ceil(r/16)*16 <= 2^21 fit; QLORA_ERR_HIP if the
+ * device or the array's address cannot be queried.
+ */
+#define QLORA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+QLORA_API qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight *w, const uint16_t *X,
+                                                int64_t M, const uint16_t *A, const uint16_t *B,
+                                                int32_t r, float lora_alpha, uint16_t *Y,
+                                                float *H_save, void *stream);
+
+/*
  * Backward of the forward above for upstream gradient dY (M x d, bf16)
  * (chain rule; QLoRA glossary forward paragraph: gradients pass through the
  * dequantised weight, only A and B are updated):

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
     ops = _ops()
     L = ops.lib()
     names = _declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for name in names:
         assert hasattr(L, name), name
         assert name in ops.SIGNATURES, name
@@ -302,3 +302,21 @@ def test_no_cpu_fallback():
             ops.lib()
     finally:
         ops.LIB_PATH, ops._lib = saved_path, saved_lib
+
+
+def test_noalloc_rejects_oversized_shapes_on_the_host():
+    # the size check runs before any device query or launch, so it needs no
+    # GPU: a GEMM-path forward whose workspace (M * 128 * 8 bytes = 32 MiB)
+    # exceeds the 16 MiB static scratch returns QLORA_ERR_WORKSPACE
+    ops = _ops()
+    L = ops.lib()
+    assert ops.workspace_bytes(ops.OP_FWD, 8, 64, 32768, 128, True) > ops.NOALLOC_SCRATCH_BYTES
+    w = ops.NF4WeightC(8, 64, 64, 1, 256, 0, 256, None, 256, 256, 256)
+    st = L.qlora_linear_fwd_noalloc(ctypes.byref(w), 256, 32768, 256, 256, 128, 32.0, 256,
+                                    None, None)
+    assert st == ops.QLORA_ERR_WORKSPACE
+    assert L.qlora_linear_fwd_noalloc(None, 256, 4, 256, 256, 16, 32.0, 256, None,
+                                      None) == ops.QLORA_ERR_INVALID_ARG
+    w2 = ops.NF4WeightC(8, 100, 64, 1, 256, 0, 256, None, 256, 256, 256)   # k % 64 != 0
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(w2), 256, 4, 256, 256, 16, 32.0, 256, None,
+                                      None) == ops.QLORA_ERR_UNSUPPORTED
