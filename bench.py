@@ -81,6 +81,8 @@ def main():
                          "steps run at the settled clock (0 = none)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--rows", choices=["on", "off"], default="on")
+    ap.add_argument("--configs", choices=["on", "off"], default="on",
+                    help="the seven-linear Llama-7B block and the 80-layer 65B-shaped stack")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized bf16 buffer 4 times (a plain copy kernel of "
                          "known size, to scale HBM byte counters) and exit")
@@ -220,6 +222,10 @@ def main():
             "lora_colacc_us_dropout": round(_kernel_us(ops, "lora_colacc", step_drop, 4, 8), 2),
             "lora_down_us_dropout": round(_kernel_us(ops, "lora_down", step_drop, 4, 8), 2)}
         log(f"[bench] dropout row: {json.dumps(rows['lora_dropout_step'])}")
+    configs = None
+    if args.configs == "on":
+        configs = {"llama7b_block": measure_block7b(ops, torch, dev, args.cpu_baseline == "on"),
+                   "stack65b": measure_stack65b(ops, torch, dev, args.cpu_baseline == "on")}
     probes = measure_probes(torch, dev) if args.rows == "on" else None
     if probes:
         roofline["frac_of_measured_gemm_probe"] = round(achieved / probes["bf16_gemm_8192_TFLOP_s"], 4)
@@ -241,6 +247,7 @@ def main():
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "rows": rows,
         "probes": probes,
+        "configs": configs,
     }
     print(json.dumps(line), flush=True)
 
@@ -469,6 +476,216 @@ def measure_rows(ops, synth, torch, dev):
     return out
 
 
+def _aligned(torch, dev, nbytes):
+    if nbytes == 0:
+        return None
+    t = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    return t[(-t.data_ptr()) % 256:][:nbytes]
+
+
+class LayerRun:
+    """The seven linears of one decoder layer at M tokens: forward with the
+    sibling projections grouped (q/k/v on the attention input, gate/up on the
+    MLP input), then the backward of each linear. Activations (one X per
+    sibling group, one dY per linear) are synthetic and shared by all layers;
+    A and B are drawn per layer; H of every linear of every layer is kept from
+    the forward for the backward."""
+
+    def __init__(self, ops, torch, dev, shapes, M, r, alpha, layers):
+        from bit_nf4_quantized_19_amd import synth, workloads
+        self.ops, self.shapes, self.M, self.r, self.alpha = ops, shapes, M, r, alpha
+        names = [n for n, _, _ in shapes]
+        self.groups = [[names.index(n) for n in g] for g in workloads.SIBLINGS]
+        self.X = {}
+        for gi, g in enumerate(self.groups):
+            k = shapes[g[0]][2]
+            self.X[gi] = synth.normal_bf16_device((M, k), 1.0, synth.SEED_X + gi, device=dev)
+        self.dY = [synth.normal_bf16_device((M, d), 1.0, synth.SEED_DY + i, device=dev)
+                   for i, (_, d, _) in enumerate(shapes)]
+        self.A = [[synth.normal_bf16_device((r, k), 0.01, synth.SEED_A + 16 * L + i, device=dev)
+                   for i, (_, _, k) in enumerate(shapes)] for L in range(layers)]
+        self.B = [[synth.normal_bf16_device((d, r), 0.01, synth.SEED_B + 16 * L + i, device=dev)
+                   for i, (_, d, _) in enumerate(shapes)] for L in range(layers)]
+        self.H = [[torch.empty(M, r, dtype=torch.float32, device=dev) for _ in shapes]
+                  for _ in range(layers)]
+        self.Y = [torch.empty(M, d, dtype=torch.bfloat16, device=dev) for _, d, _ in shapes]
+        self.dX = [torch.empty(M, k, dtype=torch.bfloat16, device=dev) for _, _, k in shapes]
+        self.dA = [torch.empty(r, k, dtype=torch.bfloat16, device=dev) for _, _, k in shapes]
+        self.dB = [torch.empty(d, r, dtype=torch.bfloat16, device=dev) for _, d, _ in shapes]
+        fw = max(ops.workspace_bytes(ops.OP_FWD_MULTI, sum(shapes[i][1] for i in g),
+                                     shapes[g[0]][2], M, r, True) for g in self.groups)
+        bw = max(ops.workspace_bytes(ops.OP_BWD, d, k, M, r, True) for _, d, k in shapes)
+        self.wsf, self.wsb = _aligned(torch, dev, fw), _aligned(torch, dev, bw)
+
+    def forward(self, L, weights):
+        ops = self.ops
+        for gi, g in enumerate(self.groups):
+            ops.linear_fwd_multi([weights[i] for i in g], self.X[gi], [self.A[L][i] for i in g],
+                                 [self.B[L][i] for i in g], self.alpha, save_h=True,
+                                 Ys=[self.Y[i] for i in g], Hs=[self.H[L][i] for i in g],
+                                 ws=self.wsf)
+
+    def backward(self, L, weights):
+        ops = self.ops
+        for gi, g in enumerate(self.groups):
+            for i in g:
+                ops.linear_bwd(weights[i], self.X[gi], self.A[L][i], self.B[L][i], self.alpha,
+                               self.dY[i], H=self.H[L][i], dX=self.dX[i], dA=self.dA[i],
+                               dB=self.dB[i], ws=self.wsb)
+
+
+def _oracle_linear_seconds(d, k, M, r, alpha, rows=None):
+    """One oracle step of a d x k linear at M tokens (dequantise + float64
+    forward and backward), on the first `rows` output rows if given; the
+    quantised record is prepared untimed. Returns (seconds, flops timed)."""
+    import numpy as np
+    from bit_nf4_quantized_19_amd import synth
+    from oracle import lora as olora
+    from oracle import nf4 as onf4
+    dd = d if rows is None else rows
+    inp = synth.linear_inputs(dd, k, M, r, idx=90)
+    qw = onf4.quantize_weight(inp["W0"], True)
+    s = olora.lora_scale(alpha, r)
+    widen = lambda b: onf4.bf16_bits_to_f32(b).astype(np.float64)
+    X, A, B, dY = (widen(inp[n]) for n in ("X", "A", "B", "dY"))
+    t0 = time.perf_counter()
+    Wd = widen(onf4.dequantize_weight(qw)).reshape(dd, k)
+    olora.forward(Wd, X, A, B, s)
+    olora.backward(Wd, X, A, B, s, dY)
+    return time.perf_counter() - t0, 4 * M * dd * k + 6 * M * r * (dd + k)
+
+
+def measure_block7b(ops, torch, dev, with_cpu):
+    """The seven linears of a Llama-7B-shaped block (q,k,v,o 4096^2; gate, up
+    4096 -> 11008; down 11008 -> 4096), NF4 + double quant, r = 16,
+    alpha = 32, 2048 tokens: forward (q/k/v and gate/up as sibling calls) and
+    backward of all seven per block step."""
+    from bit_nf4_quantized_19_amd import workloads
+    shapes, M, r, alpha = workloads.LLAMA7B, 2048, 16, 32.0
+    layer = [ops.quantize(_w0(torch, dev, d, k, workloads.w0_seed(0, i)), True)
+             for i, (_, d, k) in enumerate(shapes)]
+    run = LayerRun(ops, torch, dev, shapes, M, r, alpha, 1)
+
+    def block():
+        run.forward(0, layer)
+        run.backward(0, layer)
+    for _ in range(10):
+        block()
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(20):
+        block()
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / 20
+    fl = workloads.layer_flops(shapes, M, r)
+    out = {"workload": "llama7b_block_7_linears_nf4_dq_tokens2048_r16_fwd_bwd",
+           "gflop_per_block": round(fl / 1e9, 1), "ms_per_block": round(ms, 4),
+           "TFLOP_s": round(fl / (ms * 1e-3) / 1e12, 1),
+           "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "nf4_dq_bytes": sum(ops.storage_bytes(d, k, True) for _, d, k in shapes)}
+    if with_cpu:
+        # oracle: one linear per distinct shape, summed with multiplicity
+        cores = _oracle_cores()
+        tot = 0.0
+        with _oracle_threads(cores):
+            for (d, k), mult in (((4096, 4096), 4), ((11008, 4096), 2), ((4096, 11008), 1)):
+                sec, _ = _oracle_linear_seconds(d, k, M, r, alpha)
+                tot += mult * sec
+        out["cpu_oracle"] = {"seconds_per_block": round(tot, 2),
+                             "TFLOP_s": round(fl / tot / 1e12, 4), "cores": cores,
+                             "sample": "one linear per distinct shape (4096^2, 11008x4096, "
+                                       "4096x11008), dequantise + float64 fwd + bwd at 2048 "
+                                       "tokens, summed with multiplicity 4, 2, 1"}
+    del layer, run
+    torch.cuda.empty_cache()
+    log(f"[bench] llama7b block: {json.dumps(out)}")
+    return out
+
+
+def _w0(torch, dev, d, k, seed):
+    from bit_nf4_quantized_19_amd import synth
+    return synth.normal_bf16_device((d, k), 0.02, seed, device=dev)
+
+
+def measure_stack65b(ops, torch, dev, with_cpu):
+    """The 65B-shaped stack: 80 layers of q,k,v,o 8192^2, gate, up 8192 ->
+    22016, down 22016 -> 8192. Every base weight is drawn on the device,
+    quantised (NF4 + double quant) and its bf16 copy freed, so the whole NF4
+    stack is resident at once; then one training pass over all 80 layers at
+    2048 tokens, r = 64, alpha = 16 (forward of every layer, then backward in
+    reverse layer order), and the quantiser's rate at the two weight shapes."""
+    from bit_nf4_quantized_19_amd import workloads
+    shapes, M, r, alpha, nl = workloads.L65B, 2048, 64, 16.0, workloads.L65B_LAYERS
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    stack = workloads.build_quantized_stack(ops, shapes, nl, dev, True)
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
+    resident = stack.resident_bytes()
+    params = nl * sum(d * k for _, d, k in shapes)
+    run = LayerRun(ops, torch, dev, shapes, M, r, alpha, nl)
+
+    def train_pass(layers):
+        for L in range(layers):
+            run.forward(L, stack.weights[L])
+        for L in reversed(range(layers)):
+            run.backward(L, stack.weights[L])
+    train_pass(2)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    train_pass(nl)
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1)
+    fl = nl * workloads.layer_flops(shapes, M, r)
+    out = {"workload": "stack65b_80_layers_nf4_dq_tokens2048_r64_fwd_bwd",
+           "layers": nl, "params": params, "resident_nf4_dq_bytes": resident,
+           "resident_GB": round(resident / 1e9, 3),
+           "bits_per_param": round(8 * resident / params, 5),
+           "draw_and_quantize_all_s": round(build_s, 3),
+           "tflop_per_pass": round(fl / 1e12, 2), "ms_per_pass": round(ms, 2),
+           "TFLOP_s": round(fl / (ms * 1e-3) / 1e12, 1),
+           "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del run
+    torch.cuda.empty_cache()
+    # the quantiser alone at the two weight shapes, 12 distinct weights each
+    out["quantize"] = {}
+    for (d, k) in ((8192, 8192), (22016, 8192)):
+        Ws = [_w0(torch, dev, d, k, 9500 + i) for i in range(12)]
+        qs = [ops.NF4Weight.empty(d, k, True, dev) for _ in range(12)]
+        wsq = _aligned(torch, dev, ops.workspace_bytes(ops.OP_QUANTIZE, d, k, 0, 0, True))
+        fq = lambda i: ops.quantize(Ws[i], True, out=qs[i], ws=wsq)
+        qbytes = 2 * d * k + ops.storage_bytes(d, k, True)
+        out["quantize"][f"{d}x{k}"] = _row(qbytes, _call_ms(fq, 12, 48),
+                                           _kernel_us(ops, "quantize", fq, 12, 48))
+        del Ws, qs
+        torch.cuda.empty_cache()
+    if with_cpu:
+        # oracle: one linear per distinct shape on its first 2048 output rows
+        # (a bounded sample), its rate applied to the whole stack's flops
+        cores = _oracle_cores()
+        sec = fls = 0.0
+        with _oracle_threads(cores):
+            for (d, k), mult in (((8192, 8192), 4), ((22016, 8192), 2), ((8192, 22016), 1)):
+                t, f = _oracle_linear_seconds(d, k, M, r, alpha, rows=2048)
+                sec += mult * t
+                fls += mult * f
+        rate = fls / sec
+        out["cpu_oracle"] = {"TFLOP_s": round(rate / 1e12, 4), "cores": cores,
+                             "seconds_per_pass_extrapolated": round(fl / rate, 1),
+                             "sample": "one linear per distinct shape (8192^2, 22016x8192, "
+                                       "8192x22016) on its first 2048 output rows, dequantise "
+                                       "+ float64 fwd + bwd at 2048 tokens, weighted 4, 2, 1; "
+                                       "the rate is extrapolated to 80 layers"}
+    del stack
+    torch.cuda.empty_cache()
+    log(f"[bench] 65B stack: {json.dumps(out)}")
+    return out
+
+
 def measure_probes(torch, dev):
     """Measured ceilings beside the published peaks: a device-to-device copy
     streaming 2 GiB (and one of the 32 MiB a 4096x4096 bf16 weight occupies,
@@ -544,6 +761,14 @@ def measure_probes(torch, dev):
     return out
 
 
+def _oracle_cores():
+    """Threads for the oracle: the CPUs this process may run on, capped at the
+    share a launcher grants through OMP_NUM_THREADS."""
+    affinity = len(os.sched_getaffinity(0))
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    return min(affinity, share) if share > 0 else affinity
+
+
 def _oracle_threads(n):
     """Context in which the oracle's BLAS/OpenMP pools use n threads."""
     from threadpoolctl import threadpool_limits
@@ -571,11 +796,8 @@ def cpu_baseline(inp, flops):
     import numpy as np
     from oracle import lora as olora
     from oracle import nf4 as onf4
-    # the CPUs this process may run on; the pools are capped at the share a
-    # launcher grants through OMP_NUM_THREADS, and `cores` is what was used
     affinity = len(os.sched_getaffinity(0))
-    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
-    cores = min(affinity, share) if share > 0 else affinity
+    cores = _oracle_cores()
     log(f"[bench] cpu oracle baseline on {cores} threads ({affinity} CPUs in the affinity set)")
     qw = onf4.quantize_weight(inp["W0"], True)
     s = olora.lora_scale(ALPHA, R)

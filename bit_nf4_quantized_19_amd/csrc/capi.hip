@@ -323,14 +323,14 @@ static qlora_status linear_fwd_group(const qlora_nf4_weight *const *w, int nw, c
     so[i].dp.mask_write = 1;   // the drawn bits go to the caller's mask, if any
   }
   if ((s = launch_skinny(X, M, k, nw, so, false, r, rp, r, sc, st)) != QLORA_OK) return s;
-  if (nw == 1)
-    return launch_gemm_fwd(w[0]->codes, scale_src(w[0]), d[0], k, X, M, B[0], r, L.Hs_hi[0],
-                           L.Hs_lo[0], rp, Y[0], st);
-  // the weights' column tiles in one GEMM launch
-  GemmFwdIn gi[kMaxGroup];
+  // one fused dequant-GEMM launch per weight: a 4096-row weight at this size
+  // already fills the chip, and X is shared through L2 either way (one
+  // grouped launch over all weights' column tiles measured no faster)
   for (int i = 0; i < nw; ++i)
-    gi[i] = GemmFwdIn{w[i]->codes, scale_src(w[i]), d[i], B[i], L.Hs_hi[i], L.Hs_lo[i], Y[i]};
-  return launch_gemm_fwd_group(nw, gi, k, X, M, r, rp, st);
+    if ((s = launch_gemm_fwd(w[i]->codes, scale_src(w[i]), d[i], k, X, M, B[i], r, L.Hs_hi[i],
+                             L.Hs_lo[i], rp, Y[i], st)) != QLORA_OK)
+      return s;
+  return QLORA_OK;
 }
 
 qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,

@@ -93,16 +93,6 @@ qlora_status launch_gemm_fwd(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,
                              const uint16_t *B, int r, const uint16_t *Hs_hi,
                              const uint16_t *Hs_lo, int rp, uint16_t *Y,
                              hipStream_t st);
-// The forward for nw (1..4) weights that read the same X in one launch.
-struct GemmFwdIn {
-  const uint8_t *codes;
-  ql::ScaleSrc sc;
-  int64_t d;
-  const uint16_t *B, *Hs_hi, *Hs_lo;
-  uint16_t *Y;
-};
-qlora_status launch_gemm_fwd_group(int nw, const GemmFwdIn *in, int64_t k, const uint16_t *X,
-                                   int64_t M, int r, int rp, hipStream_t st);
 // keep (M x k/4 keep nibbles, or NULL): adapter-input dropout of the forward;
 // the rank-r term of dX is then kept per element and scaled by inv_keep.
 qlora_status launch_gemm_dx(const uint8_t *codes, ql::ScaleSrc sc, int64_t d,

@@ -364,7 +364,7 @@ def linear_fwd_noalloc(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.
 
 def linear_fwd_multi(ws_: list, X: torch.Tensor, As: list, Bs: list, lora_alpha: float,
                      save_h: bool = True, Ys: list | None = None, ws: torch.Tensor | None = None,
-                     stream=None):
+                     stream=None, Hs: list | None = None):
     """Sibling projections: Y_i = X W_i'^T + (alpha/r) (X A_i^T) B_i^T for up
     to four weights reading the same X, in one call. Returns (Ys, Hs)."""
     nw = len(ws_)
@@ -377,8 +377,10 @@ def linear_fwd_multi(ws_: list, X: torch.Tensor, As: list, Bs: list, lora_alpha:
     M, r = X.shape[0], As[0].shape[0]
     if Ys is None:
         Ys = [torch.empty(M, w.d, dtype=torch.bfloat16, device=X.device) for w in ws_]
-    Hs = ([torch.empty(M, r, dtype=torch.float32, device=X.device) for _ in range(nw)]
-          if save_h else None)
+    if save_h and Hs is None:
+        Hs = [torch.empty(M, r, dtype=torch.float32, device=X.device) for _ in range(nw)]
+    if not save_h:
+        Hs = None
     dtot = sum(w.d for w in ws_)
     wsb = workspace_bytes(OP_FWD_MULTI, dtot, ws_[0].k, M, r, ws_[0].double_quant)
     wst, wsn = _workspace(wsb, X.device, ws)

@@ -179,8 +179,8 @@ QLORA_API qlora_status qlora_linear_fwd_ex(const qlora_nf4_weight *w, const uint
  * lora_alpha and the double-quantisation mode. For M <= 16 the weights run
  * as one GEMV launch (row groups of all weights in one grid; X and the LoRA
  * down projections read once) plus one epilogue launch; for larger M as one
- * launch computing every H_i = X A_i^T plus one fused dequant-GEMM launch
- * over the column tiles of all weights. Results are bit-identical to nw
+ * launch computing every H_i = X A_i^T (X read once) plus one fused
+ * dequant-GEMM launch per weight. Results are bit-identical to nw
  * separate qlora_linear_fwd calls.
  * Workspace: qlora_workspace_bytes(QLORA_OP_FWD_MULTI, sum of d_i, k, M, r, dq).
  */
