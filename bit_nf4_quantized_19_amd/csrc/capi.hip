@@ -419,12 +419,17 @@ qlora_status qlora_linear_bwd_ex(const qlora_nf4_weight *w, const uint16_t *X, i
   }
   // G = dY B (float32, M x rp) and s*G as bf16 hi/lo for the dX epilogue; B
   // is read in place unless r % 16 != 0 (then from a zero-padded B^T)
+  // the G launch also clears the counters the dA/dB launch below uses
+  int *cnt = colacc_counters(L.cpart, M, d, k, rp);
+  const int64_t ncnt = colacc_counter_count(d, k);
   if (r % 16) {
     const LayoutReq req[1] = {{B, d, r, L.Bt, rp, d, 1}};
     if ((s = launch_layout(req, 1, st)) != QLORA_OK) return s;
-    s = launch_skinny(dY, M, d, L.Bt, false, rp, rp, L.G, nullptr, 0, sc, L.Gs_hi, L.Gs_lo, st);
+    s = launch_skinny(dY, M, d, L.Bt, false, rp, rp, L.G, nullptr, 0, sc, L.Gs_hi, L.Gs_lo, st,
+                      cnt, ncnt);
   } else {
-    s = launch_skinny(dY, M, d, B, true, r, rp, L.G, nullptr, 0, sc, L.Gs_hi, L.Gs_lo, st);
+    s = launch_skinny(dY, M, d, B, true, r, rp, L.G, nullptr, 0, sc, L.Gs_hi, L.Gs_lo, st, cnt,
+                      ncnt);
   }
   if (s != QLORA_OK) return s;
   // dB = s dY^T H (d x r) and dA = s G^T X (r x k), one launch

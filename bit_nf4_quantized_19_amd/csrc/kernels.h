@@ -57,9 +57,12 @@ qlora_status launch_layout(const LayoutReq *req, int nreq, hipStream_t st);
 // P[c * r + t] (p_col true: C x r, requires r % 16 == 0). out2 (optional)
 // receives the first out2_ld columns with leading dim out2_ld. Also writes
 // s*out split into bf16 hi/lo (M x rp each) when hi != NULL.
+// zero (optional): nzero ints cleared by the launch, for a later launch of
+// the same call (the colacc counters).
 qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, const uint16_t *P,
                            bool p_col, int r, int rp, float *out, float *out2, int out2_ld,
-                           float s, uint16_t *hi, uint16_t *lo, hipStream_t st);
+                           float s, uint16_t *hi, uint16_t *lo, hipStream_t st,
+                           int *zero = nullptr, int64_t nzero = 0);
 // The same for nw (1..4) contractions of one In (sibling projections) in one
 // launch: o[i] = {P, out, out2, hi, lo} of contraction i.
 struct SkinnyOut {
@@ -69,9 +72,10 @@ struct SkinnyOut {
   DropParams dp;   // dropout on In (row form only; dp.on == 0: none)
 };
 qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, int nw, const SkinnyOut *o,
-                           bool p_col, int r, int rp, int out2_ld, float s, hipStream_t st);
+                           bool p_col, int r, int rp, int out2_ld, float s, hipStream_t st,
+                           int *zero = nullptr, int64_t nzero = 0);
 // Two problems out = s * sum_m In[m][c] * Q[m][t] rounded to bf16 (In M x C,
-// Q M x rp fp32) in one launch plus one reduction launch.
+// Q M x rp fp32) in one launch, including the reduction of its token splits.
 // transpose_out == 0: out is C x r (ld r); == 1: out is r x C (ld C).
 struct ColaccReq {
   const uint16_t *In;
@@ -82,9 +86,15 @@ struct ColaccReq {
   DropParams dp;     // dropout of In (dp.on == 0: none); the result is scaled by 1/(1-p)
   uint8_t *keep;     // with dropout: M x C/4 keep nibbles written here (may be NULL)
 };
+// part: colacc_part_bytes(M, a.C, b.C, rp) bytes of workspace, holding the
+// split partial sums and colacc_counter_count(a.C, b.C) counters at
+// colacc_counters(part, ...), which must be zero when the launch starts (the
+// G launch of the same call clears them) and are zero when it ends.
 qlora_status launch_colacc2(const ColaccReq &a, const ColaccReq &b, int64_t M, int rp,
                             int r, float s, float *part, hipStream_t st);
 size_t colacc_part_bytes(int64_t M, int64_t C0, int64_t C1, int rp);
+int64_t colacc_counter_count(int64_t C0, int64_t C1);
+int *colacc_counters(float *part, int64_t M, int64_t C0, int64_t C1, int rp);
 
 // gemm.hip : fused dequant-GEMM, forward (Y) and input-gradient (dX) forms.
 // The rank-r epilogue reads B (d x r) resp. A (r x k) in place.

@@ -91,6 +91,8 @@ struct SkinnyArgs {
   int64_t M, C, cpw;
   int r, rp, tbw, out2_ld;
   float s;
+  int *zero;        // counters a later launch of the same call needs zeroed (or NULL)
+  int64_t nzero;
 };
 template <class T>
 QL_DEV T pick4s(int i, T a0, T a1, T a2, T a3) {
@@ -101,6 +103,8 @@ QL_DEV T pick4s(int i, T a0, T a1, T a2, T a3) {
 constexpr int SK_TOK = 8;   // tokens per workgroup (of the 16 MFMA rows)
 template <bool PCOL>
 __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
+  if (a.zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int64_t i = threadIdx.x; i < a.nzero; i += 64 * SK_W) a.zero[i] = 0;
   const int wi = (int)blockIdx.y / a.tbw;   // uniform: fields picked by selects
   const uint16_t *__restrict__ In = a.In;
   const uint16_t *__restrict__ Pm = QL_SKPICK(P);
@@ -208,211 +212,263 @@ __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
 }
 
 // ---- colacc -------------------------------------------------------------------
-constexpr int CA_COLS = 256;     // columns per workgroup (four per lane)
-constexpr int CA_MAXSPLIT = 16;
-constexpr int CA_TOK = 16;       // tokens per batch
-constexpr int CA_W = 8;          // waves per workgroup (token ranges)
+// out^T[t][c] = sum_m Q[m][t] In[m][c] on MFMA 16x16x32 with the tokens as
+// the contraction: A = Q^T (rows t, 8 consecutive tokens per lane), B = In
+// (8 consecutive tokens of one column per lane). In is token-major, so each
+// 32-token x 64-column chunk is staged in LDS row by row (16 coalesced bytes
+// per thread) and read back down the columns; Q is staged transposed and
+// split into bf16 hi + lo parts (two MFMAs per chunk, ~16 significant bits).
+// A workgroup (four waves, one 16-column tile each) owns 64 columns of one
+// problem, every rank block of them, and one of S token ranges; its partial
+// sums go to part[split][c][t]. The last workgroup of a column block to
+// finish (a counter per block, zero at launch) adds the S partials in split
+// order, scales and rounds them: dB and dA with one launch and no second
+// pass.
+constexpr int CM_COLS = 64;      // columns per workgroup
+constexpr int CM_MAXSPLIT = 16;
+constexpr int CM_MAXRP = 128;
+constexpr int CM_INS = CM_COLS / 2 + 1;   // dwords per staged In row (one pad dword)
+// A chunk is KS MFMA contraction steps of 32 tokens; a staged Q^T row holds
+// the chunk's 32 KS tokens plus a 16-byte pad.
+template <int KS> constexpr int cm_qs() { return 32 * KS + 8; }
 
 struct ColaccProb {
   const uint16_t *In;  // M x C
   int64_t C;
   const float *Q;      // M x rp
   float *part;         // S x C x rp
-  int64_t groups;      // column groups of CA_COLS
+  int64_t blocks;      // column blocks of CM_COLS
+  uint16_t *out;
+  int transpose_out;   // 0: out is C x r (ld r); 1: out is r x C (ld C)
+  float scale;         // s, times 1/(1-p) for a dropped input
   DropParams dp;       // dropout of In's elements (dp.on == 0: none)
-  uint8_t *keep;       // M x C/4 keep nibbles written when dropping (or NULL)
+  uint8_t *keep;       // M x C/4 keep nibbles written when drawing them (or NULL)
 };
 
-// Batch of CA_TOK tokens of one wave: this lane's 4 columns of each token
-// row and its float4 of the batch's Q block (token l/4, t = t0 + 4(l%4)..);
-// tokens past the wave's range read as zero.
-template <bool MK>
-struct CaBatch {
-  uint2 v[CA_TOK];
-  float4 q;
-  uint32_t kb[MK ? CA_TOK / 4 : 1];   // stored keep nibbles of the batch's tokens (4 per word)
+// Chunk staged through registers: this thread's 8 columns of one token row
+// (and their keep bits) and up to four float4 of the chunk's Q block.
+template <int RPM, int KS>
+struct CmRegs {
+  uint4 x[KS];
+  float4 q[RPM * KS / 32 > 0 ? RPM * KS / 32 : 1];
 };
 
-template <bool MK>
-QL_DEV void ca_load(CaBatch<MK> &b, const uint16_t *inc, int64_t C, bool c_ok, const float *Q,
-                    int rp, int t0, int64_t m, int64_t m_hi, int lane, const uint8_t *mk) {
+// Rows at or past M (here: the end of this workgroup's token range) read as 0.
+template <bool MK, int RPM, int KS>
+QL_DEV void cm_load(CmRegs<RPM, KS> &R, const ColaccProb &P, int64_t M, int rp, int64_t m0, int64_t c0,
+                    int tid) {
 #pragma unroll
-  for (int u = 0; u < CA_TOK; ++u) {
-    const int64_t mm = m + u < m_hi ? m + u : m_hi - 1;  // clamped; not accumulated
-    b.v[u] = c_ok ? *(const uint2 *)(inc + mm * C) : make_uint2(0u, 0u);
-  }
-  // with a stored mask, its bytes travel with the batch's loads (mk: the
-  // lane's column byte of row 0, or NULL)
-#pragma unroll
-  for (int j = 0; j < (MK ? CA_TOK / 4 : 1); ++j) b.kb[j] = 0u;
-  if (MK && mk) {
-#pragma unroll
-    for (int u = 0; u < CA_TOK; ++u) {
-      const int64_t mm = m + u < m_hi ? m + u : m_hi - 1;
-      b.kb[u >> 2] |= (uint32_t)mk[mm * (C >> 2)] << (8 * (u & 3));
+  for (int j = 0; j < KS; ++j) {
+    const int64_t m = m0 + 32 * j + (tid >> 3), c = c0 + 8 * (tid & 7);
+    const bool ok = m < M && c < P.C;   // C % 8 == 0: the 8 columns are all in or all out
+    R.x[j] = ok ? *(const uint4 *)(P.In + m * P.C + c) : ql::zero4();
+    if (P.dp.on && ok) {
+      const uint64_t e = (uint64_t)m * (uint64_t)P.C + (uint64_t)c;
+      uint32_t k8;
+      if (MK && P.dp.mask && !P.dp.mask_write) {
+        const uint32_t b2 = *(const uint16_t *)(P.dp.mask + (e >> 2));   // the forward's bits
+        k8 = (b2 & 15u) | (((b2 >> 8) & 15u) << 4);
+      } else {
+        k8 = keep4(P.dp, e) | (keep4(P.dp, e + 4) << 4);
+        if (P.keep) *(uint16_t *)(P.keep + (e >> 2)) = (uint16_t)((k8 & 15u) | ((k8 >> 4) << 8));
+      }
+      R.x[j] = mask_bf16x8(R.x[j], k8);
     }
   }
-  const int64_t mq = m + (lane >> 2);
-  b.q = mq < m_hi ? *(const float4 *)(Q + mq * rp + t0 + 4 * (lane & 3))
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-// Dropout of the batch's first n tokens: their dropped elements become 0,
-// and the keep bits (4 per lane and token) are stored for the dX epilogue.
-template <bool MK>
-QL_DEV void ca_drop(CaBatch<MK> &b, const DropParams &dp, int64_t m, int n, int64_t C, int64_t c0,
-                    uint8_t *keep) {
+  const int nq = 8 * KS * rp;   // float4 in the chunk's Q block
 #pragma unroll
-  for (int u = 0; u < CA_TOK; ++u) {
-    if (u >= n) continue;  // wave-uniform
-    // the bits the forward stored (loaded with the batch), or drawn here
-    const uint32_t bits = MK ? (b.kb[MK ? u >> 2 : 0] >> (8 * (u & 3))) & 15u
-                             : keep4(dp, (uint64_t)(m + u) * (uint64_t)C + (uint64_t)c0);
-    b.v[u].x &= ((bits & 1u) ? 0x0000FFFFu : 0u) | ((bits & 2u) ? 0xFFFF0000u : 0u);
-    b.v[u].y &= ((bits & 4u) ? 0x0000FFFFu : 0u) | ((bits & 8u) ? 0xFFFF0000u : 0u);
-    if (keep) keep[(m + u) * (C >> 2) + (c0 >> 2)] = (uint8_t)bits;
+  for (int u = 0; u < (RPM * KS + 31) / 32; ++u) {
+    const int f = tid + 256 * u;
+    if (f >= nq) break;
+    const int64_t mq = m0 + f / (rp / 4);
+    R.q[u] = mq < M ? *(const float4 *)(P.Q + mq * rp + 4 * (f % (rp / 4)))
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
-// acc[c][t] += x[token][c] * Q[token][t] over the batch's tokens (the first
-// n of them when PART)
-template <bool PART, bool MK>
-QL_DEV void ca_batch(float (&acc)[4][16], const CaBatch<MK> &b, const float4 *qs, int n) {
+template <int RPM, int KS>
+QL_DEV void cm_store(const CmRegs<RPM, KS> &R, uint32_t *sin, uint16_t *sqh, uint16_t *sql, int rp,
+                     int tid) {
 #pragma unroll
-  for (int u = 0; u < CA_TOK; ++u) {
-    if (PART && u >= n) continue;  // wave-uniform
-    float q[16];
+  for (int j = 0; j < KS; ++j) {
+    uint32_t *row = sin + (32 * j + (tid >> 3)) * CM_INS + 4 * (tid & 7);
+    row[0] = R.x[j].x; row[1] = R.x[j].y; row[2] = R.x[j].z; row[3] = R.x[j].w;
+  }
+  const int nq = 8 * KS * rp;
+#pragma unroll
+  for (int u = 0; u < (RPM * KS + 31) / 32; ++u) {
+    const int f = tid + 256 * u;
+    if (f >= nq) break;
+    const int tok = f / (rp / 4), t = 4 * (f % (rp / 4));
+    const float v[4] = {R.q[u].x, R.q[u].y, R.q[u].z, R.q[u].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float4 f = qs[4 * u + i];   // same address in every lane
-      q[4 * i] = f.x; q[4 * i + 1] = f.y; q[4 * i + 2] = f.z; q[4 * i + 3] = f.w;
+      const uint16_t hb = ql::f_to_bf16(v[i]);
+      sqh[(t + i) * cm_qs<KS>() + tok] = hb;
+      sql[(t + i) * cm_qs<KS>() + tok] = ql::f_to_bf16(v[i] - ql::bf16_to_f(hb));
     }
-    const float x[4] = {ql::bf16lo(b.v[u].x), ql::bf16hi(b.v[u].x), ql::bf16lo(b.v[u].y),
-                        ql::bf16hi(b.v[u].y)};
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int t = 0; t < 16; ++t) acc[c][t] = fmaf(x[c], q[t], acc[c][t]);
   }
 }
 
-// grid: x = column groups of problem 0 then problem 1 (times rp/16 t-blocks),
-// y = token split. The eight waves of a workgroup take the same 256 columns
-// over disjoint token ranges, each streaming its rows in batches of 16
-// tokens with the next batch's loads in flight; the Q block of a batch is
-// staged in the wave's own LDS slot and read back as broadcasts. The waves'
-// sums are added in LDS in a fixed order.
-template <bool MK>
-__global__ __launch_bounds__(64 * CA_W) void colacc_kernel(ColaccProb p0, ColaccProb p1,
-                                                           int64_t M, int rp, int64_t mps) {
-  __shared__ float4 qst[CA_W][64];
-  __shared__ float4 red[CA_W][16][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t tbs = rp / 16;
-  int64_t gx = blockIdx.x;
-  const bool second = gx >= p0.groups * tbs;
+// One chunk from LDS buffer `buf`: B = tokens 8g .. 8g+7 of column
+// 16 wave + cl, A = Q^T hi and lo of each rank block.
+template <int RPM, int KS>
+QL_DEV void cm_compute(f32x4 (&acc)[RPM / 16], const uint32_t *sin, const uint16_t *sqh,
+                       const uint16_t *sql, int tbs, int wave, int cl, int g) {
+  const unsigned char *colp = (const unsigned char *)sin + 2 * (16 * wave + cl);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      h[i] = *(const uint16_t *)(colp + (32 * ks + 8 * g + i) * CM_INS * 4);
+    const uint4 bop = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                 h[6] | (h[7] << 16));
+#pragma unroll
+    for (int b = 0; b < RPM / 16; ++b) {
+      if (b >= tbs) break;
+      const int qo = (16 * b + cl) * cm_qs<KS>() + 32 * ks + 8 * g;
+      const uint4 ah = *(const uint4 *)&sqh[qo];
+      const uint4 al = *(const uint4 *)&sql[qo];
+      acc[b] = ql::mfma16(ah, bop, acc[b]);
+      acc[b] = ql::mfma16(al, bop, acc[b]);
+    }
+  }
+}
+
+#ifndef QL_CM_PF
+#define QL_CM_PF 2
+#endif
+#ifndef QL_CM_WGS
+#define QL_CM_WGS 512
+#endif
+constexpr int CM_PF = QL_CM_PF;   // chunks whose loads are in flight per thread
+
+// Dynamic LDS: two buffers of the In chunk (32 KS x CM_INS dwords) and of
+// Q^T hi and lo (rp x cm_qs bf16 each).
+template <int KS>
+size_t cm_lds_bytes(int rp) {
+  return 2 * 32 * KS * CM_INS * 4 + 2 * 2 * (size_t)rp * cm_qs<KS>() * 2;
+}
+
+// RPM: the largest padded rank this instance handles (32, 64 or 128), which
+// sizes its registers.
+template <bool MK, int RPM, int KS>
+__global__ __launch_bounds__(256) void colacc_kernel(ColaccProb p0, ColaccProb p1, int64_t M,
+                                                     int rp, int r, int64_t mps, int S,
+                                                     int *cnt) {
+  extern __shared__ __align__(16) unsigned char cm_lds[];
+  constexpr int TOK = 32 * KS, QS = cm_qs<KS>();
+  uint32_t *s_in0 = (uint32_t *)cm_lds, *s_in1 = s_in0 + TOK * CM_INS;
+  uint16_t *s_q = (uint16_t *)(s_in1 + TOK * CM_INS);
+  uint16_t *s_qh0 = s_q, *s_ql0 = s_q + rp * QS, *s_qh1 = s_q + 2 * rp * QS,
+           *s_ql1 = s_q + 3 * rp * QS;
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cl = lane & 15, g = lane >> 4;
+  int64_t bx = blockIdx.x;
+  const bool second = bx >= p0.blocks;
   const ColaccProb &P = second ? p1 : p0;
-  if (second) gx -= p0.groups * tbs;
-  const int64_t cg = gx / tbs, tb = gx % tbs;
-  const int64_t c0 = cg * CA_COLS + 4 * lane;
-  const int t0 = (int)tb * 16;
-  const int64_t split = blockIdx.y;
+  if (second) bx -= p0.blocks;
+  const int64_t c0 = bx * CM_COLS;
+  const int split = blockIdx.y;
   const int64_t m_lo = split * mps, m_hi = min(M, m_lo + mps);
-  const int64_t span = m_hi - m_lo;
-  const int64_t w_lo = m_lo + (span * wave) / CA_W, w_hi = m_lo + (span * (wave + 1)) / CA_W;
-  float acc[4][16];
+  const int tbs = rp / 16;
+  f32x4 acc[RPM / 16];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int b = 0; b < RPM / 16; ++b)
 #pragma unroll
-    for (int t = 0; t < 16; ++t) acc[c][t] = 0.0f;
-  const bool c_ok = c0 < P.C;  // C % 64 == 0: the 4 columns are all in or all out
-  const uint16_t *inc = P.In + (c_ok ? c0 : 0);
-  // only the problem that drops (the adapter input) has a mask; the other
-  // problem of the launch (dY for dB) reads none
-  const uint8_t *mk = (MK && P.dp.on && P.dp.mask && !P.dp.mask_write && c_ok)
-                          ? P.dp.mask + (c0 >> 2)
-                          : nullptr;
-  if (w_lo < w_hi) {
-    CaBatch<MK> cur, nxt;
-    ca_load(nxt, inc, P.C, c_ok, P.Q, rp, t0, w_lo, w_hi, lane, mk);
-    for (int64_t m = w_lo; m < w_hi; m += CA_TOK) {
-      cur = nxt;
-      if (m + CA_TOK < w_hi)
-        ca_load(nxt, inc, P.C, c_ok, P.Q, rp, t0, m + CA_TOK, w_hi, lane, mk);
-      qst[wave][lane] = cur.q;   // this wave's previous reads of the slot precede (in order)
-      if (P.dp.on && c_ok)
-        ca_drop(cur, P.dp, m, (int)min<int64_t>(CA_TOK, w_hi - m), P.C, c0,
-                tb == 0 ? P.keep : nullptr);
-      if (m + CA_TOK <= w_hi)
-        ca_batch<false, MK>(acc, cur, qst[wave], CA_TOK);
-      else
-        ca_batch<true, MK>(acc, cur, qst[wave], (int)(w_hi - m));
+    for (int i = 0; i < 4; ++i) acc[b][i] = 0.0f;
+  const int nch = (int)ql_cdiv(m_hi - m_lo, TOK);
+  // a ring of CM_PF register sets, the loop unrolled by CM_PF so every set is
+  // named at compile time: chunk ch + CM_PF - 1 is loaded while chunk ch is
+  // stored to LDS and computed
+  CmRegs<RPM, KS> R[CM_PF];
+#pragma unroll
+  for (int i = 0; i < CM_PF - 1; ++i)
+    if (i < nch) cm_load<MK, RPM, KS>(R[i], P, m_hi, rp, m_lo + (int64_t)i * TOK, c0, tid);
+  for (int ch0 = 0; ch0 < nch; ch0 += CM_PF) {
+#pragma unroll
+    for (int u = 0; u < CM_PF; ++u) {
+      const int ch = ch0 + u;
+      if (ch >= nch) break;
+      if (ch + CM_PF - 1 < nch)
+        cm_load<MK, RPM, KS>(R[(u + CM_PF - 1) % CM_PF], P, m_hi, rp,
+                             m_lo + (int64_t)(ch + CM_PF - 1) * TOK, c0, tid);
+      uint32_t *sin = (u & 1) ? s_in1 : s_in0;
+      uint16_t *sqh = (u & 1) ? s_qh1 : s_qh0, *sql = (u & 1) ? s_ql1 : s_ql0;
+      cm_store<RPM, KS>(R[u], sin, sqh, sql, rp, tid);
+      __syncthreads();
+      cm_compute<RPM, KS>(acc, sin, sqh, sql, tbs, wave, cl, g);
     }
   }
-  // the waves' sums in a fixed order: ((wave 0 + 1) + 2) + ... ; thread p of
-  // the workgroup finishes float4 entries p and p + 512 of the 64 x 16 grid
+  // lane holds out^T[16 b + 4 g + i][c0 + 16 wave + cl]. The partials are
+  // published with agent-scope stores (written through to the level every
+  // XCD sees), so no L2 write-back or invalidation is needed: the barrier
+  // below waits for this workgroup's stores to complete before the counter
+  // moves, and the last workgroup reads them back with agent-scope loads.
+  const int64_t c = c0 + 16 * wave + cl;
+  if (c < P.C) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    red[wave][i][lane] = make_float4(acc[i >> 2][4 * (i & 3)], acc[i >> 2][4 * (i & 3) + 1],
-                                     acc[i >> 2][4 * (i & 3) + 2], acc[i >> 2][4 * (i & 3) + 3]);
+    for (int b = 0; b < RPM / 16; ++b) {
+      if (b >= tbs) break;
+      float *dst = P.part + ((int64_t)split * P.C + c) * rp + 16 * b + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __hip_atomic_store(dst + i, acc[b][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // the last workgroup of this column block adds the S partials in order
+  int *ctr = cnt + (second ? p0.blocks : 0) + bx;
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's stores have completed
   __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+  __syncthreads();
+  if (!s_last) return;
+  // four outputs per pass, all their S partial loads issued before any sum
+  for (int o0 = 0; o0 < CM_COLS * r; o0 += 4 * 256) {
+    float p[4][CM_MAXSPLIT];
+    int64_t oi[4];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int e = (int)threadIdx.x + 512 * h;
-    const int l = e & 63, i = e >> 6;
-    float4 o = red[0][i][l];
+    for (int j = 0; j < 4; ++j) {
+      const int o = o0 + 256 * j + tid;
+      int col, t;
+      if (P.transpose_out) {
+        t = o / CM_COLS;
+        col = o % CM_COLS;
+      } else {
+        col = o / r;
+        t = o % r;
+      }
+      const int64_t cc = c0 + col;
+      const bool ok = o < CM_COLS * r && cc < P.C;
+      oi[j] = ok ? (P.transpose_out ? (int64_t)t * P.C + cc : cc * r + t) : -1;
 #pragma unroll
-    for (int w = 1; w < CA_W; ++w) {
-      const float4 v = red[w][i][l];
-      o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
+      for (int sp = 0; sp < CM_MAXSPLIT; ++sp)
+        p[j][sp] = (ok && sp < S) ? __hip_atomic_load(P.part + ((int64_t)sp * P.C + cc) * rp + t,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                  : 0.0f;
     }
-    const int64_t c = cg * CA_COLS + 4 * l + (i >> 2);
-    if (c < P.C) *(float4 *)(P.part + (split * P.C + c) * rp + t0 + 4 * (i & 3)) = o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = 0.0f;
+#pragma unroll
+      for (int sp = 0; sp < CM_MAXSPLIT; ++sp)
+        if (sp < S) v += p[j][sp];
+      if (oi[j] >= 0) P.out[oi[j]] = ql::f_to_bf16(P.scale * v);
+    }
   }
+  if (tid == 0)   // left clear for the next call on this workspace
+    __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-struct ColaccOut {
-  const float *part;  // S x C x rp
-  int64_t C;
-  uint16_t *out;
-  int transpose_out;  // 0: out is C x r; 1: out is r x C
-  int64_t n;          // C * r
-  float scale;        // s, times 1/(1-p) for a dropped input
-};
-
-// one thread per output element of problem 0 then problem 1
-__global__ __launch_bounds__(256) void colacc_reduce_kernel(ColaccOut o0, ColaccOut o1, int S,
-                                                            int rp, int r) {
-  int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool second = idx >= o0.n;
-  const ColaccOut &O = second ? o1 : o0;
-  if (second) idx -= o0.n;
-  if (idx >= O.n) return;
-  int64_t c, t;
-  if (O.transpose_out) {
-    t = idx / O.C;
-    c = idx % O.C;
-  } else {
-    c = idx / r;
-    t = idx % r;
-  }
-  float p[CA_MAXSPLIT];
-#pragma unroll
-  for (int sp = 0; sp < CA_MAXSPLIT; ++sp)
-    if (sp < S) p[sp] = O.part[(sp * O.C + c) * rp + t];
-  float v = 0.0f;
-#pragma unroll
-  for (int sp = 0; sp < CA_MAXSPLIT; ++sp)
-    if (sp < S) v += p[sp];
-  O.out[idx] = ql::f_to_bf16(O.scale * v);
-}
-
-int64_t colacc_split(int64_t M, int64_t C, int rp) {
-  // about 256 workgroups of CA_W waves, each wave with at least 16 tokens
-  const int64_t wgs = ql_cdiv(C, CA_COLS) * (rp / 16);
-  int64_t S = ql_cdiv(256, wgs);
-  S = std::min<int64_t>(S, std::max<int64_t>(1, M / (CA_TOK * CA_W)));
-  return std::min<int64_t>(std::max<int64_t>(S, 1), CA_MAXSPLIT);
+int64_t colacc_split(int64_t M, int64_t C0, int64_t C1) {
+  // about four workgroups per compute unit, each split at least one chunk
+  const int64_t blocks = ql_cdiv(C0, CM_COLS) + ql_cdiv(C1, CM_COLS);
+  int64_t S = ql_cdiv(QL_CM_WGS, blocks);
+  S = std::min<int64_t>(S, ql_cdiv(M, 128));
+  return std::min<int64_t>(std::max<int64_t>(S, 1), CM_MAXSPLIT);
 }
 
 }  // namespace
@@ -438,7 +494,8 @@ qlora_status launch_layout(const LayoutReq *req, int nreq, hipStream_t st) {
 }
 
 qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, int nw, const SkinnyOut *o,
-                           bool p_col, int r, int rp, int out2_ld, float s, hipStream_t st) {
+                           bool p_col, int r, int rp, int out2_ld, float s, hipStream_t st,
+                           int *zero, int64_t nzero) {
   if (nw < 1 || nw > 4) return QLORA_ERR_INVALID_ARG;
   if (p_col && (r % 16 != 0 || r != rp)) return QLORA_ERR_UNSUPPORTED;
   SkinnyArgs a{};
@@ -455,6 +512,8 @@ qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, int nw, con
   a.tbw = rp / 16;
   a.out2_ld = out2_ld;
   a.s = s;
+  a.zero = zero;
+  a.nzero = nzero;
   const int64_t mbs = ql_cdiv(M, SK_TOK);
   if (mbs > 0x7fffffff || (int64_t)nw * a.tbw > 65535) return QLORA_ERR_UNSUPPORTED;
   dim3 grid((unsigned)mbs, (unsigned)(nw * a.tbw));
@@ -469,38 +528,56 @@ qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, int nw, con
 
 qlora_status launch_skinny(const uint16_t *In, int64_t M, int64_t C, const uint16_t *P,
                            bool p_col, int r, int rp, float *out, float *out2, int out2_ld,
-                           float s, uint16_t *hi, uint16_t *lo, hipStream_t st) {
+                           float s, uint16_t *hi, uint16_t *lo, hipStream_t st, int *zero,
+                           int64_t nzero) {
   const SkinnyOut o{P, out, out2, hi, lo, DropParams{0u, 0u, 0u, 1.0f, 0}};
-  return launch_skinny(In, M, C, 1, &o, p_col, r, rp, out2_ld, s, st);
+  return launch_skinny(In, M, C, 1, &o, p_col, r, rp, out2_ld, s, st, zero, nzero);
 }
 
 size_t colacc_part_bytes(int64_t M, int64_t C0, int64_t C1, int rp) {
-  const int64_t S = colacc_split(M, C0 + C1, rp);
-  return (size_t)(S * (C0 + C1) * rp * 4);
+  const int64_t S = colacc_split(M, C0, C1);
+  return (size_t)ql_rup(S * (C0 + C1) * rp * 4, 256) + colacc_counter_count(C0, C1) * 4;
+}
+
+int64_t colacc_counter_count(int64_t C0, int64_t C1) {
+  return ql_cdiv(C0, CM_COLS) + ql_cdiv(C1, CM_COLS);
+}
+
+int *colacc_counters(float *part, int64_t M, int64_t C0, int64_t C1, int rp) {
+  const int64_t S = colacc_split(M, C0, C1);
+  return (int *)((char *)part + ql_rup(S * (C0 + C1) * rp * 4, 256));
 }
 
 qlora_status launch_colacc2(const ColaccReq &a, const ColaccReq &b, int64_t M, int rp, int r,
                             float s, float *part, hipStream_t st) {
-  const int64_t S0 = colacc_split(M, a.C + b.C, rp);
-  const int64_t mps = ql_cdiv(M, S0);
+  if (rp % 16 || rp > CM_MAXRP) return QLORA_ERR_UNSUPPORTED;
+  const int64_t S0 = colacc_split(M, a.C, b.C);
+  const int64_t mps = ql_rup(ql_cdiv(M, S0), 128);   // a multiple of every chunk size
   const int64_t S = ql_cdiv(M, mps);
-  ColaccProb p0{a.In, a.C, a.Q, part, ql_cdiv(a.C, CA_COLS), a.dp, a.keep};
-  ColaccProb p1{b.In, b.C, b.Q, part + S * a.C * rp, ql_cdiv(b.C, CA_COLS), b.dp, b.keep};
-  const int64_t tbs = rp / 16;
-  dim3 grid((unsigned)((p0.groups + p1.groups) * tbs), (unsigned)S);
-  {
-    QlProf prof(QLORA_K_LORA_COLACC, st);
-    // MK: the adapter input's keep bits come from the mask the forward stored
-    if (p1.dp.on && p1.dp.mask && !p1.dp.mask_write)
-      colacc_kernel<true><<<grid, 64 * CA_W, 0, st>>>(p0, p1, M, rp, mps);
-    else
-      colacc_kernel<false><<<grid, 64 * CA_W, 0, st>>>(p0, p1, M, rp, mps);
+  const int64_t pbytes = ql_rup(S0 * (a.C + b.C) * rp * 4, 256);
+  int *cnt = (int *)((char *)part + pbytes);   // zeroed by the launch before (launch_skinny)
+  ColaccProb p0{a.In, a.C, a.Q, part, ql_cdiv(a.C, CM_COLS), a.out, a.transpose_out,
+                a.dp.on ? s * a.dp.inv_keep : s, a.dp, a.keep};
+  ColaccProb p1{b.In, b.C, b.Q, part + S * a.C * rp, ql_cdiv(b.C, CM_COLS), b.out,
+                b.transpose_out, b.dp.on ? s * b.dp.inv_keep : s, b.dp, b.keep};
+  dim3 grid((unsigned)(p0.blocks + p1.blocks), (unsigned)S);
+  QlProf prof(QLORA_K_LORA_COLACC, st);
+  // MK: the adapter input's keep bits come from the mask the forward stored
+  const bool mk = p1.dp.on && p1.dp.mask && !p1.dp.mask_write;
+  // chunk depth per rank bound: the LDS of two chunks stays within 64 KB
+#define QL_CM(RPV, KSV)                                                                   \
+  {                                                                                       \
+    const size_t lds = cm_lds_bytes<KSV>(rp);                                             \
+    if (mk)                                                                               \
+      colacc_kernel<true, RPV, KSV><<<grid, 256, lds, st>>>(p0, p1, M, rp, r, mps, (int)S, cnt); \
+    else                                                                                  \
+      colacc_kernel<false, RPV, KSV><<<grid, 256, lds, st>>>(p0, p1, M, rp, r, mps, (int)S, cnt); \
   }
-  ColaccOut o0{p0.part, a.C, a.out, a.transpose_out, a.C * r, a.dp.on ? s * a.dp.inv_keep : s};
-  ColaccOut o1{p1.part, b.C, b.out, b.transpose_out, b.C * r, b.dp.on ? s * b.dp.inv_keep : s};
-  QlProf prof(QLORA_K_LORA_COLACC_REDUCE, st);
-  colacc_reduce_kernel<<<(unsigned)ql_cdiv(o0.n + o1.n, 256), 256, 0, st>>>(o0, o1, (int)S, rp,
-                                                                           r);
+  if (rp <= 16) QL_CM(16, 4)
+  else if (rp <= 32) QL_CM(32, 2)
+  else if (rp <= 64) QL_CM(64, 2)
+  else QL_CM(128, 1)
+#undef QL_CM
   QL_LAUNCH_CHECK();
   return QLORA_OK;
 }
