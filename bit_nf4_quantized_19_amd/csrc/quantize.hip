@@ -27,11 +27,12 @@
 //    of one tensor span few octaves), so the LDS atomics are per wave, not
 //    per block; each workgroup then adds its histogram to one of NHC global
 //    copies (spreading the atomics over more addresses).
-//  * dq_mean_kernel (one workgroup) adds the histogram copies, places them
-//    into 384-bit limb sums with LDS atomics (one lane per exponent) and
-//    turns the sum into mu = round_f32(sum / nb) by exact long division.
-//  * dq_encode_kernel: one workgroup per group of 256 blocks: s2 and the
-//    int8 codes of its group.
+//  * dq_encode_kernel: every workgroup adds the histogram copies, places
+//    them into 384-bit limb sums with LDS atomics (one lane per exponent),
+//    turns the sum into mu = round_f32(sum / nb) by exact long division (the
+//    same value in every workgroup), then computes s2 and the int8 codes of
+//    its GPW groups of 256 blocks: the double quantisation is one launch
+//    after the quantiser (plus the histogram clear before it).
 #include <cstring>
 
 #include <algorithm>
@@ -43,7 +44,8 @@ namespace {
 
 constexpr int QT = 256;
 constexpr int QU = 2;      // chunks per lane (measured: 8 -> 19.0 us, 4 -> 16.4, 2 -> 15.6, 1 -> 17.5 at 4096x4096)
-constexpr int NHC = 64;    // global histogram copies (workgroup b adds to copy b % NHC)
+constexpr int NHC = 8;     // global histogram copies (workgroup b adds to copy b % NHC)
+constexpr int GPW = 8;     // double-quant groups per encode workgroup
 
 // Cell table entry: the candidate threshold T_j and the bits of H_j with j in
 // the low four mantissa bits (every H_j is a power of two, so those bits are
@@ -232,18 +234,33 @@ QL_DEV float mean_from_limbs(const unsigned long long *limb, uint32_t *sq, uint3
   return __uint_as_float(bits);
 }
 
-// One workgroup: lane t adds the NHC copies of bucket t (sum of 8-bit
-// significands of the absmax values with bf16 exponent field t, subnormals in
-// bucket 1) and adds h * 2^(t-1+64) into the limb sums with LDS atomics.
-__global__ __launch_bounds__(256) void dq_mean_kernel(const unsigned long long *__restrict__ hist,
-                                                     uint32_t nb, float *__restrict__ mu_out) {
+// Double quantisation in one launch. Every workgroup first derives the exact
+// mean itself: lane t adds the NHC histogram copies of bucket t (sum of
+// 8-bit significands of the absmax values with bf16 exponent field t,
+// subnormals in bucket 1) and adds h * 2^(t-1+64) into 384-bit limb sums with
+// LDS atomics; lane 0 rounds sum / nb once to float32. Then it encodes GPW
+// groups of 256 blocks (all their absmax loads issued first): per group
+// s2 = fl(max|a - mu| / 127) and q = clamp(rne(fl((a - mu) / s2)), -127, 127).
+__global__ __launch_bounds__(256) void dq_encode_kernel(
+    const unsigned long long *__restrict__ hist, const float *__restrict__ absmax, int64_t nb,
+    int64_t ng, int8_t *__restrict__ q, float *__restrict__ s2, float *__restrict__ mu_out) {
   __shared__ unsigned long long limb[12];
   __shared__ uint32_t sq[12];
+  __shared__ float s_mu;
+  __shared__ uint32_t wmax[GPW][4];
   const int tid = threadIdx.x;
-  if (tid < 12) limb[tid] = 0ull;
+  const int64_t g0 = (int64_t)blockIdx.x * GPW;
+  // the group loads do not depend on the mean: issue them with the histogram's
+  float av[GPW];
+#pragma unroll
+  for (int j = 0; j < GPW; ++j) {
+    const int64_t b = (g0 + j) * 256 + tid;
+    av[j] = b < nb ? absmax[b] : 0.0f;
+  }
   unsigned long long hc[NHC];
 #pragma unroll
   for (int c = 0; c < NHC; ++c) hc[c] = hist[c * 256 + tid];
+  if (tid < 12) limb[tid] = 0ull;
   unsigned long long h = 0;
 #pragma unroll
   for (int c = 0; c < NHC; ++c) h += hc[c];
@@ -257,33 +274,40 @@ __global__ __launch_bounds__(256) void dq_mean_kernel(const unsigned long long *
     if (bit) atomicAdd(&limb[li + 2], h >> (64 - bit));
   }
   __syncthreads();
-  if (tid == 0) mu_out[0] = mean_from_limbs(limb, sq, nb);
-}
-
-__global__ __launch_bounds__(256) void dq_encode_kernel(
-    const float *__restrict__ absmax, int64_t nb, const float *__restrict__ mu_p,
-    int8_t *__restrict__ q, float *__restrict__ s2) {
-  __shared__ uint32_t wmax[4];
-  const int tid = threadIdx.x;
-  const int64_t b = (int64_t)blockIdx.x * 256 + tid;
-  const float mu = mu_p[0];
-  float d = 0.0f;
-  if (b < nb) d = absmax[b] - mu;
-  uint32_t m = __float_as_uint(fabsf(d));
-  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  if (tid == 0) {
+    const float m = mean_from_limbs(limb, sq, (uint32_t)nb);
+    s_mu = m;
+    if (blockIdx.x == 0) mu_out[0] = m;
+  }
   __syncthreads();
-  const uint32_t gm = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-  const float sc = __uint_as_float(gm) / 127.0f;
-  if (tid == 0) s2[blockIdx.x] = sc;
-  if (b < nb) {
-    int qi = 0;
-    if (sc != 0.0f) {
-      float r = rintf(d / sc);
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      qi = (int)r;
+  const float mu = s_mu;
+  float dv[GPW];
+#pragma unroll
+  for (int j = 0; j < GPW; ++j) {
+    // blocks past nb (the last group's tail) take no part in the group max
+    dv[j] = (g0 + j) * 256 + tid < nb ? av[j] - mu : 0.0f;
+    uint32_t m = __float_as_uint(fabsf(dv[j]));
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if ((tid & 63) == 0) wmax[j][tid >> 6] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < GPW; ++j) {
+    const int64_t G = g0 + j;
+    if (G >= ng) break;
+    const uint32_t gm = max(max(wmax[j][0], wmax[j][1]), max(wmax[j][2], wmax[j][3]));
+    const float sc = __uint_as_float(gm) / 127.0f;
+    if (tid == 0) s2[G] = sc;
+    const int64_t b = G * 256 + tid;
+    if (b < nb) {
+      int qi = 0;
+      if (sc != 0.0f) {
+        float r = rintf(dv[j] / sc);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        qi = (int)r;
+      }
+      q[b] = (int8_t)qi;
     }
-    q[b] = (int8_t)qi;
   }
 }
 
@@ -317,8 +341,8 @@ qlora_status launch_quantize(const uint16_t *W0, int64_t n, uint8_t *codes,
   }
   {
     QlProf prof(QLORA_K_DOUBLE_QUANT, st);
-    dq_mean_kernel<<<1, 256, 0, st>>>(hist, (uint32_t)nb, mu);
-    dq_encode_kernel<<<(unsigned)ql_cdiv(nb, 256), 256, 0, st>>>(amax, nb, mu, q, s2);
+    const int64_t ng = ql_cdiv(nb, 256);
+    dq_encode_kernel<<<(unsigned)ql_cdiv(ng, GPW), 256, 0, st>>>(hist, amax, nb, ng, q, s2, mu);
   }
   QL_LAUNCH_CHECK();
   return QLORA_OK;
