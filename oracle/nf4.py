@@ -9,12 +9,13 @@ Pages followed
     at normal quantiles; every 64 weights form a block with one absmax scale.
   - double-quantisation bullet: the per-block scales are themselves quantised
     to 8 bits in blocks of 256 scales (0.5 -> about 0.127 bit per parameter).
-  - the runnable snippet: levels from the standard normal inverse CDF at
-    ``linspace(0.9677083, 0.5, 9)[:-1]`` (positive side) and
-    ``linspace(0.9677083, 0.5, 8)[:-1]`` (negated, negative side), an exact
-    zero, sorted and divided by the largest; per block
-    ``absmax = max |w|``, ``x = w / absmax``, code = index of the level with
-    the smallest ``|x - level|``; restore = ``levels[code] * absmax``.
+  - the worked example after the bullets: the levels are standard-normal
+    quantiles at probabilities spaced evenly between 1/2 and a top
+    probability the example gives (0.9677083), eight steps on the positive
+    side and seven, mirrored, on the negative side, plus an exact zero, all
+    divided by the positive end so they span [-1, 1]; a weight is coded as
+    the level nearest to it after division by its block's absmax, and
+    restored as that level times the absmax.
   - forward paragraph: frozen weights are dequantised to bfloat16 before the
     matrix product.
 * Day-25 LoRA/QLoRA notes (itingyu.github.io), section 3.3 "双重量化":
@@ -25,10 +26,11 @@ Pages followed
 
 Readings where the pages are silent
 ----------------------------------
-* Levels: the quantiles are evaluated in float64 at the literal decimal
-  probabilities and rounded once to float32 (the snippet's float32 evaluation
-  lands within 8 ulp; the tests check that).
-* Tie-break of the nearest-level search: lowest index (the snippet's argmin).
+* Levels: each probability 1/2 + (j/n)(p_top - 1/2) is formed exactly and
+  rounded once to float64 (p_top the float64 nearest the printed decimal),
+  the quantile is evaluated in float64, and the normalised level is rounded
+  once to float32.
+* Tie-break of the nearest-level search: lowest index.
 * All-zero block (absmax 0, ``0/0`` undefined): every code is the zero level.
 * Code packing: element ``2j`` in the high nibble of byte ``j``.
 * 8-bit absmax format: one global float32 mean ``mu`` (the exact mean of all
@@ -47,7 +49,8 @@ from statistics import NormalDist
 
 import numpy as np
 
-#: Top probability of the quantile grid, the literal printed in the snippet.
+#: Top probability of the quantile grid, as printed in the glossary's worked
+#: example (QLoRA glossary, "QLoRA 的工作原理").
 P_TOP = 0.9677083
 BLOCKSIZE = 64
 DQ_GROUP = 256
@@ -57,19 +60,27 @@ ZERO_CODE = 7  # index of the exact-zero level in the ascending table
 # --------------------------------------------------------------------------
 # Levels
 # --------------------------------------------------------------------------
+def _grid_probability(j: int, n: int) -> float:
+    """1/2 + (j/n)(P_TOP - 1/2), formed exactly and rounded once; j = n gives
+    P_TOP itself."""
+    return float(Fraction(1, 2) + Fraction(j, n) * (Fraction(P_TOP) - Fraction(1, 2)))
+
+
 def nf4_levels_f64() -> np.ndarray:
     """The 16 NF4 levels in float64, ascending.
 
-    QLoRA glossary (Ultralytics), "QLoRA 的工作原理", snippet: 8 positive
-    quantiles at linspace(P_TOP, 0.5, 9) without its last point, 7 negated
-    quantiles at linspace(P_TOP, 0.5, 8) without its last point, one exact
-    zero; sort; divide by the largest value.
+    QLoRA glossary (Ultralytics), "QLoRA 的工作原理" (NF4 bullet and the worked
+    example): with z the standard-normal quantile function, the positive
+    levels are z(p_j) for p_j = 1/2 + (j/8)(P_TOP - 1/2), j = 1..8; the
+    negative levels are -z(p) at p = 1/2 + (j/7)(P_TOP - 1/2), j = 1..7; level
+    zero is exact; every level is divided by the positive end z(P_TOP), so the
+    table runs from -1 to 1.
     """
-    icdf = NormalDist(0.0, 1.0).inv_cdf
-    positive = [icdf(p) for p in np.linspace(P_TOP, 0.5, 9)[:-1]]
-    negative = [-icdf(p) for p in np.linspace(P_TOP, 0.5, 8)[:-1]]
-    v = np.sort(np.array(negative + [0.0] + positive, dtype=np.float64))
-    return v / v.max()
+    z = NormalDist(0.0, 1.0).inv_cdf
+    top = z(P_TOP)
+    negative = [-z(_grid_probability(j, 7)) / top for j in range(7, 0, -1)]
+    positive = [z(_grid_probability(j, 8)) / top for j in range(1, 9)]
+    return np.array(negative + [0.0] + positive, dtype=np.float64)
 
 
 def nf4_levels() -> np.ndarray:
@@ -78,8 +89,9 @@ def nf4_levels() -> np.ndarray:
 
 
 def int4_levels() -> np.ndarray:
-    """Evenly spaced 4-bit levels ``linspace(-1, 1, 16)``, the snippet's
-    comparison baseline (QLoRA glossary, "QLoRA 的工作原理")."""
+    """16 evenly spaced levels from -1 to 1 (step 2/15), the grid the
+    glossary's worked example compares NF4 against (QLoRA glossary, "QLoRA
+    的工作原理")."""
     return np.linspace(-1.0, 1.0, 16).astype(np.float32)
 
 
@@ -89,9 +101,8 @@ def int4_levels() -> np.ndarray:
 def nearest_level(x: np.ndarray, levels: np.ndarray) -> np.ndarray:
     """Index of the level nearest to each float32 ``x``.
 
-    The snippet's ``(x[..., None] - levels).abs().argmin(-1)``: the distance
-    is one float32 subtraction, and argmin returns the first (lowest) index
-    among equal distances.
+    Nearest by absolute difference, the difference taken as one float32
+    subtraction; among equal distances the lowest index wins.
     """
     x = np.asarray(x, dtype=np.float32)
     lv = np.asarray(levels, dtype=np.float32)
@@ -117,7 +128,7 @@ def quantize_blocks(w: np.ndarray, levels: np.ndarray | None = None,
                     blocksize: int = BLOCKSIZE):
     """Blockwise absmax quantisation of a flat float32 array.
 
-    QLoRA glossary, "QLoRA 的工作原理" (NF4 bullet and snippet): per block of
+    QLoRA glossary, "QLoRA 的工作原理" (NF4 bullet and worked example): per block of
     ``blocksize`` consecutive weights, ``a = max |w|``, ``x = fl(w / a)``,
     code = nearest level. Returns ``(codes uint8 [n], absmax float32 [nb])``.
     An all-zero block gets the zero level's code.
@@ -224,7 +235,8 @@ def dequantize_absmax(q: np.ndarray, s2: np.ndarray, mu, group: int = DQ_GROUP):
 def restore_f32(codes: np.ndarray, absmax_deq: np.ndarray,
                 levels: np.ndarray | None = None,
                 blocksize: int = BLOCKSIZE) -> np.ndarray:
-    """``levels[code] * a'`` in float32 (the snippet's restore)."""
+    """``levels[code] * a'`` in float32: a weight is restored as its level
+    times its block's scale (QLoRA glossary, "QLoRA 的工作原理")."""
     lv = nf4_levels() if levels is None else np.asarray(levels, np.float32)
     c = np.asarray(codes, dtype=np.uint8).reshape(-1, blocksize)
     a = np.asarray(absmax_deq, dtype=np.float32).reshape(-1, 1)

@@ -1,12 +1,24 @@
 """Pins for the oracle's NF4 level table (QLoRA glossary, Ultralytics,
-"QLoRA 的工作原理": NF4 bullet and snippet)."""
+"QLoRA 的工作原理": NF4 bullet and the worked example after the bullets).
 
+The table is pinned by its closed-form properties, by mapping every level
+back through the normal CDF (a different routine from the quantile function
+that builds it), and by the mean squared errors the page prints for its
+worked example (tests/golden/p4_snippet_mse.json): the float32 table
+reproduces both printed figures, and plausible misreadings of the
+construction do not."""
+
+import json
 import math
+import os
+from statistics import NormalDist
 
 import numpy as np
 import pytest
 
 from oracle import nf4
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def test_sixteen_levels_exact_zero_and_unit_ends():
@@ -23,49 +35,83 @@ def _phi(x):
 
 
 def test_levels_are_the_stated_normal_quantiles():
-    # Map each normalised level back through the normal CDF (erfc: a different
-    # routine from the inverse CDF used to build them) and recover the grid.
+    # Map each normalised level back through the normal CDF (erfc) and recover
+    # the evenly spaced probabilities: 8 steps from 1/2 to the top on the
+    # positive side, 7 on the negative side.
     Lf = nf4.nf4_levels_f64()
-    zmax = abs(np.float64(0)) + 0.0
-    # the positive end is the quantile of the top probability
-    from statistics import NormalDist
     zmax = NormalDist().inv_cdf(nf4.P_TOP)
     assert abs(_phi(zmax) - nf4.P_TOP) < 1e-15
-    pos_p = np.linspace(nf4.P_TOP, 0.5, 9)[:-1]
-    neg_p = np.linspace(nf4.P_TOP, 0.5, 8)[:-1]
+    span = nf4.P_TOP - 0.5
+    want_pos = [0.5 + j * span / 8 for j in range(1, 9)]
+    want_neg = [0.5 + j * span / 7 for j in range(1, 8)]
     got_pos = sorted(_phi(z * zmax) for z in Lf[8:])
     got_neg = sorted(1.0 - _phi(z * zmax) for z in Lf[:7])
-    np.testing.assert_allclose(got_pos, sorted(pos_p), rtol=0, atol=2e-15)
-    np.testing.assert_allclose(got_neg, sorted(neg_p), rtol=0, atol=2e-15)
+    np.testing.assert_allclose(got_pos, want_pos, rtol=0, atol=2e-15)
+    np.testing.assert_allclose(got_neg, want_neg, rtol=0, atol=2e-15)
 
 
 def test_inverse_cdf_agrees_with_scipy():
     sp = pytest.importorskip("scipy.special")
-    from statistics import NormalDist
     icdf = NormalDist().inv_cdf
-    ps = np.concatenate([np.linspace(nf4.P_TOP, 0.5, 9), np.linspace(0.01, 0.99, 99)])
+    ps = np.concatenate([[0.5 + j * (nf4.P_TOP - 0.5) / 8 for j in range(9)],
+                         np.linspace(0.01, 0.99, 99)])
     for p in ps:
         a, b = icdf(p), float(sp.ndtri(p))
         assert abs(a - b) <= 1e-15 * max(1.0, abs(b)) + 1e-16
 
 
-def test_snippet_float32_construction_is_within_8_ulp():
-    # The page builds the table with torch in float32; the oracle's table is
-    # the float64 construction rounded once. They differ by a few ulp (the
-    # float32 probability grid and float32 inverse CDF), never by more than 8.
+def _page_example_mse(levels):
+    """Mean squared error of the page's worked example with `levels`: the
+    example's seeded weights (4096 blocks of 64 normal values times 0.02),
+    coded to the nearest level after dividing by each block's absmax and
+    restored as level times absmax."""
     torch = pytest.importorskip("torch")
-    normal = torch.distributions.Normal(0.0, 1.0)
-    positive = normal.icdf(torch.linspace(0.9677083, 0.5, 9)[:-1])
-    negative = -normal.icdf(torch.linspace(0.9677083, 0.5, 8)[:-1])
-    t = torch.cat([negative, torch.zeros(1), positive]).sort().values
-    t = (t / t.max()).numpy().astype(np.float32)
-    L = nf4.nf4_levels()
-    # ulp distance on the ordered integer line of float32
-    def key(a):
-        u = a.view(np.int32).astype(np.int64)
-        return np.where(u < 0, -(u & 0x7FFFFFFF), u)
-    assert np.max(np.abs(key(t) - key(L))) <= 8
-    np.testing.assert_allclose(t, L, rtol=1e-6, atol=0)
+    torch.manual_seed(0)
+    w = (torch.randn(4096, 64) * 0.02).numpy().astype(np.float32)
+    codes, absmax = nf4.quantize_blocks(w, levels)
+    restored = nf4.restore_f32(codes, absmax, levels)
+    diff = restored.astype(np.float64) - w.reshape(-1).astype(np.float64)
+    return f"{float(np.mean(diff * diff)):.3e}"
+
+
+def _golden():
+    with open(os.path.join(GOLDEN, "p4_snippet_mse.json")) as f:
+        return json.load(f)
+
+
+def test_float32_table_reproduces_the_printed_errors():
+    g = _golden()
+    assert _page_example_mse(nf4.nf4_levels()) == g["nf4_mse"]
+    assert _page_example_mse(nf4.int4_levels()) == g["int4_mse"]
+
+
+def _normalised(v):
+    v = np.sort(np.asarray(v, np.float64))
+    return (v / v.max()).astype(np.float32)
+
+
+@pytest.mark.parametrize("reading", ["midpoint_quantiles", "split_7_positive_8_negative",
+                                     "no_zero_level", "top_probability_one_step_lower"])
+def test_misreadings_miss_the_printed_error(reading):
+    # Each is a plausible wrong construction; the page's printed NF4 figure
+    # must reject it (so the golden value pins the table, not just its shape).
+    z = NormalDist().inv_cdf
+    span = nf4.P_TOP - 0.5
+    if reading == "midpoint_quantiles":       # q_i = z((i + 1/2) / 16)
+        L = _normalised([z((i + 0.5) / 16) for i in range(16)])
+    elif reading == "split_7_positive_8_negative":
+        L = _normalised([z(0.5 + j * span / 7) for j in range(1, 8)] + [0.0] +
+                        [-z(0.5 + j * span / 8) for j in range(1, 9)])
+    elif reading == "no_zero_level":          # 8 + 8 quantiles, no exact zero
+        L = _normalised([z(0.5 + j * span / 8) for j in range(1, 9)] +
+                        [-z(0.5 + j * span / 8) for j in range(1, 9)])
+    else:                                     # grid top at 1/2 + 7/8 of the span
+        top = 0.5 + 7 * span / 8
+        s2 = top - 0.5
+        L = _normalised([z(0.5 + j * s2 / 8) for j in range(1, 9)] + [0.0] +
+                        [-z(0.5 + j * s2 / 7) for j in range(1, 8)])
+    assert L.shape == (16,)
+    assert _page_example_mse(L) != _golden()["nf4_mse"], reading
 
 
 def test_int4_levels_evenly_spaced():

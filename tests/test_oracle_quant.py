@@ -20,7 +20,7 @@ def _mse(w, levels):
     return float(np.mean(diff * diff))
 
 
-def test_page_snippet_mse_values():
+def test_page_example_mse_values():
     torch = pytest.importorskip("torch")
     with open(os.path.join(GOLDEN, "p4_snippet_mse.json")) as f:
         gold = json.load(f)
