@@ -31,8 +31,10 @@
 //   * Work unit: 16 weight rows x one slice of 16 blocks (1024 columns).
 //     About one workgroup of 8 waves per compute unit; each workgroup serves
 //     one slice (table and X slice built once) and each wave takes up to two
-//     units, whose loads are all issued before the table is built and whose
-//     MFMA chains are interleaved. Partial sums per slice go to a float32
+//     units, whose MFMA chains are interleaved. Only their first code chunk
+//     is loaded before the table is built; the others go out after the
+//     workgroup barrier, one chunk ahead of the decode, so the decode runs
+//     while the codes stream in. Partial sums per slice go to a float32
 //     buffer; a second kernel adds the slices in a fixed order, the rank-r
 //     LoRA term in float32, and rounds to bf16.
 #include <algorithm>
@@ -48,6 +50,13 @@ constexpr int GT = 64 * GW;
 constexpr int GX = 2048 / GT;    // X chunks (16 tokens x 16 blocks x 8) per thread
 constexpr int GB = 16;           // blocks per slice (1024 columns)
 constexpr int GMAXW = 4;         // weights per grouped call
+// Code-load order (see the kernel): GPRE chunks go out before the table is
+// built, the rest GLA chunks ahead of the decode. Measured call times at
+// 11008x4096 (M = 1 / 16): all four chunks before the table 15.5 / 21.6 us;
+// GPRE = 1: 14.1 / 19.7 us (0 and 2 within 2%); GLA = 1: 14.0 / 19.0 us
+// (2..3 within 3%).
+constexpr int GPRE = 1;   // code chunks issued before the table is built (0..4)
+constexpr int GLA = 1;    // chunks of code loads ahead of the chunk being decoded (>= 1)
 // LDS: 256 rows of 256 bytes (table copies in bytes 0-127, X in 128-255),
 // then the zero region read by lanes outside their token group
 constexpr uint32_t ZBASE = 65536 + 64;
@@ -184,10 +193,10 @@ QL_DEV void unit_codes(GUnit &u, int c, int nblk, int q) {
 // MFMA steps of NU units of a wave (same slice, so they share the A
 // operand reads; their independent chains interleave). D[4q + t][n] = partial
 // sum of block 4c + q for token 4tp + t. Writes the units' partial sums.
-template <bool DQ, int TP, int NU>
+template <bool DQ, int TP, int NU, class Issue>
 QL_DEV void unit_compute(const GemvArgs &g, const GUnit *const (&us)[NU],
                          const unsigned char *smem, const uint32_t (&abase)[TP], uint32_t lcopy,
-                         int n, int q, int64_t slice) {
+                         int n, int q, int64_t slice, Issue issue) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[NU][TP];
 #pragma unroll
@@ -196,6 +205,8 @@ QL_DEV void unit_compute(const GemvArgs &g, const GUnit *const (&us)[NU],
     for (int tp = 0; tp < TP; ++tp) acc[v][tp] = zero;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
+    issue(c);   // the code loads of a later chunk go out before this chunk's decode
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 p[NU][TP];
 #pragma unroll
     for (int v = 0; v < NU; ++v)
@@ -271,28 +282,45 @@ QL_DEV void unit_compute(const GemvArgs &g, const GUnit *const (&us)[NU],
 // sums over the 128 columns of this slice that wave w covers, on 16x16x32
 // MFMA: A operand = X rows (tokens), B operand = A rows (ranks 16 cb ..
 // 16 cb + 15); D[4q + i][n] = partial H[token 4q + i][rank 16 cb + n]. One
-// X read serves every weight of the call.
-template <bool GRP>
-QL_DEV void lora_down_partial(const GemvArgs &g, int64_t slice, int nblk, int wave, int n,
-                              int q) {
+// X read serves every weight of the call. The X chunk and the first 16 ranks
+// of the first weight's A are loaded up front (HPre), before the code loads,
+// so the partial costs no memory round trip after the main compute.
+struct HPre {
+  uint4 xa[4];   // X[n][c0 + 32 i + 8 q .. + 7], raw (masked where used)
+  uint4 aa[4];   // A[n][...] of weight 0, ranks 0..15, raw
+};
+
+// Unconditional loads from clamped addresses (a branch around a load makes
+// the compiler wait for it on the spot); lanes outside M or the slice read
+// the first row of X or A and are zeroed where the values are used.
+QL_DEV void lora_down_load(const GemvArgs &g, int64_t slice, int nblk, int wave, int n, int q,
+                           HPre &h) {
   const int64_t c0 = slice * (64 * GB) + 128 * wave;  // first column of the wave
   const int ncol = 64 * nblk - 128 * wave;           // valid columns of the wave (may be <= 0)
-  uint4 xa[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const bool ok = 32 * i + 8 * q < ncol && n < g.M;
-    xa[i] = ok ? *(const uint4 *)(g.X + n * g.k + c0 + 32 * i + 8 * q) : ql::zero4();
+    const bool ok = 32 * i + 8 * q < ncol;
+    const int64_t col = c0 + 32 * i + 8 * q;
+    h.xa[i] = *(const uint4 *)(g.X + (ok && n < g.M ? n * g.k + col : 0));
+    h.aa[i] = *(const uint4 *)(g.w[0].Ap + (ok ? (int64_t)n * g.k + col : 0));
   }
+}
+
+template <bool GRP>
+QL_DEV void lora_down_partial(const GemvArgs &g, int64_t slice, int nblk, int wave, int n,
+                              int q, const HPre &h) {
+  const int64_t c0 = slice * (64 * GB) + 128 * wave;
+  const int ncol = 64 * nblk - 128 * wave;
   for (int wi = 0; wi < (GRP ? g.nw : 1); ++wi) {
     const GemvW W = GRP ? wsel(g, wi) : g.w[0];
     uint4 xm[4];   // X with this weight's adapter-input dropout applied
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xm[i] = xa[i];
+      xm[i] = (32 * i + 8 * q < ncol && n < g.M) ? h.xa[i] : ql::zero4();
       if (W.dp.on) {
         const uint64_t e = (uint64_t)(n < g.M ? n : 0) * (uint64_t)g.k +
                            (uint64_t)(c0 + 32 * i + 8 * q);
-        xm[i] = mask_bf16x8(xa[i], keep4(W.dp, e) | (keep4(W.dp, e + 4) << 4));
+        xm[i] = mask_bf16x8(xm[i], keep4(W.dp, e) | (keep4(W.dp, e + 4) << 4));
       }
     }
     for (int cb = 0; cb < g.rp / 16; ++cb) {
@@ -300,8 +328,10 @@ QL_DEV void lora_down_partial(const GemvArgs &g, int64_t slice, int nblk, int wa
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = 32 * i + 8 * q < ncol;
-        aa[i] = ok ? *(const uint4 *)(W.Ap + (int64_t)(16 * cb + n) * g.k + c0 + 32 * i + 8 * q)
-                   : ql::zero4();
+        aa[i] = !ok ? ql::zero4()
+                : (wi == 0 && cb == 0)
+                    ? h.aa[i]
+                    : *(const uint4 *)(W.Ap + (int64_t)(16 * cb + n) * g.k + c0 + 32 * i + 8 * q);
       }
       f32x4 hacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -351,6 +381,13 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
     const bool ok = m < g.M && b < nblk;  // else read X[0][0..7], stored as zeros
     xv[i] = *(const uint4 *)(g.X + (ok ? m * g.k + (b0 + b) * 64 + 8 * sc8 : 0));
   }
+  // the LoRA down-projection operands, in the workgroup that computes that
+  // partial (the last one of the slice, which has the fewest units); issued
+  // before the code loads so the waits for the codes count the same loads
+  // in every workgroup
+  const bool hwg = blockIdx.x == gridDim.x - 1;
+  HPre hp;
+  if (hwg) lora_down_load(g, slice, nblk, wave, n, q, hp);
   __builtin_amdgcn_sched_barrier(0);
   // 3. the wave's two units (row groups wave and wave + GW of this
   //    workgroup), loaded unconditionally (clamped) so every wait is exact
@@ -361,9 +398,14 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
   unit_load<DQ, FULL, GRP>(g, ua, min(rga, g.ngroups - 1), b0, nblk, n, q);
   unit_load<DQ, FULL, GRP>(g, ub, min(rgb, g.ngroups - 1), b0, nblk, n, q);
   // codes chunk by chunk, both units' chunk c before chunk c + 1: the
-  // compute of chunk c waits only for the loads up to it
+  // compute of chunk c waits only for the loads up to it. Only the first
+  // GPRE chunks go out before the table is built: once the memory queues are
+  // full a load instruction waits to issue, and a wave issues in order, so
+  // loads placed before the barrier below would hold every wave of the
+  // workgroup at it until nearly all of its data had streamed in, and no
+  // decode would overlap the stream.
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < GPRE; ++c) {
     unit_codes<FULL>(ua, c, nblk, q);
     unit_codes<FULL>(ub, c, nblk, q);
     __builtin_amdgcn_sched_barrier(0);
@@ -387,6 +429,22 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
   }
   if (tid < (int)(ZBYTES / 16)) *(uint4 *)(smem + ZBASE + 16 * tid) = ql::zero4();
   __syncthreads();
+  // the rest of the code loads: chunks up to GLA - 1 now, chunk c + GLA just
+  // before the decode of chunk c, so a wave held at a load issue has already
+  // decoded what arrived
+#pragma unroll
+  for (int c = GPRE; c < GLA && c < 4; ++c) {
+    unit_codes<FULL>(ua, c, nblk, q);
+    unit_codes<FULL>(ub, c, nblk, q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  auto issue = [&](int c) {
+    const int cn = c + GLA;
+    if (cn >= GPRE && cn < 4) {
+      unit_codes<FULL>(ua, cn, nblk, q);
+      unit_codes<FULL>(ub, cn, nblk, q);
+    }
+  };
 
   const uint32_t lcopy = 4u * (uint32_t)(lane & 31);
   const bool a_on = (n >> 2) == q;  // lane group q carries token rows 4q..4q+3
@@ -395,12 +453,25 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
   for (int tp = 0; tp < TP; ++tp) abase[tp] = a_on ? xa_base(tp, q, n & 3) : ZBASE;
   if (has_b) {  // has_b implies has_a
     const GUnit *const both[2] = {&ua, &ub};
-    unit_compute<DQ, TP, 2>(g, both, smem, abase, lcopy, n, q, slice);
+    unit_compute<DQ, TP, 2>(g, both, smem, abase, lcopy, n, q, slice, issue);
   } else if (has_a) {
     const GUnit *const one[1] = {&ua};
-    unit_compute<DQ, TP, 1>(g, one, smem, abase, lcopy, n, q, slice);
+    unit_compute<DQ, TP, 1>(g, one, smem, abase, lcopy, n, q, slice, issue);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) issue(c);   // every code register gets its (clamped) load
   }
-  if (blockIdx.x == gridDim.x - 1) lora_down_partial<GRP>(g, slice, nblk, wave, n, q);  // fewest units
+  // The second unit's loads were issued on every wave; keep their registers
+  // live to here so that no instruction above reuses one while its load is
+  // in flight (which would make the first wait of a one-unit wave cover
+  // every load).
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      asm volatile("" ::"v"(ub.cw[c][h].x), "v"(ub.cw[c][h].y), "v"(ub.cw[c][h].z),
+                   "v"(ub.cw[c][h].w));
+  if (hwg) lora_down_partial<GRP>(g, slice, nblk, wave, n, q, hp);
 }
 
 // Y[m][j] = bf16(sum_s part[s][m][j] + s_l * sum_t H[m][t] B[j][t]) with

@@ -15,13 +15,12 @@
 //     emits s*out as bf16 hi/lo parts for the fused GEMM epilogue. P is A
 //     (rows contiguous in c) or B read in place (columns contiguous in t),
 //     transposed per K-slice through LDS.
-//   * colacc: out[c][t] = s sum_m In[m][c] Q[m][t] on float32 FMA, one lane
-//     per four columns and 16 t, rows streamed 16 tokens per batch with the
-//     next batch in flight, the batch's Q block broadcast from LDS; eight
-//     waves per workgroup on disjoint token ranges, reduced in LDS in a fixed
-//     order; the token range is split S ways into partial sums that a second
-//     kernel adds in a fixed order. dB and dA run as two problems of one
-//     launch, and their reductions as one launch.
+//   * colacc: out[c][t] = s sum_m In[m][c] Q[m][t] on MFMA 16x16x32 with the
+//     tokens as the contraction (Q as bf16 hi + lo parts); a workgroup owns 64
+//     columns and one of S token ranges, streams token chunks through LDS with
+//     the next chunks' loads in flight, and writes its partial sums; the last
+//     workgroup of a column block to finish adds the S partials in split
+//     order and rounds them. dB and dA run as two problems of one launch.
 //   * layout: the zero-padded and transposed copies of A and B the other
 //     kernels read (A^T for the dX epilogue, B^T for G), in one launch.
 // r is padded to rp (a multiple of 16) with zero rows/columns.

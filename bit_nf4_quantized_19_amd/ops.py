@@ -90,7 +90,8 @@ TIMING_SIGNATURES = {
     "qlora_profile_release": (ctypes.c_int, []),
 }
 
-#: kernel ids of the timing hooks (QLORA_K_* in include/qlora_nf4_timing.h)
+#: kernel ids of the timing hooks (QLORA_K_* in include/qlora_nf4_timing.h);
+#: ids 8 and 10 are reserved and never recorded
 KERNELS = ["quantize", "double_quant", "dequantize", "gemm_fwd", "gemm_dx", "gemv",
            "gemv_epilogue", "lora_down", "lora_reduce", "lora_colacc", "lora_colacc_reduce",
            "merge", "layout", "adamw", "loftq_product", "loftq_small", "residual"]

@@ -27,6 +27,8 @@
 extern "C" {
 #endif
 
+/* Ids 8 and 10 name no kernel of this library (their reductions are folded
+ * into the producing kernels); they stay reserved so the other ids are stable. */
 enum {
   QLORA_K_QUANTIZE = 0, QLORA_K_DOUBLE_QUANT = 1, QLORA_K_DEQUANTIZE = 2,
   QLORA_K_GEMM_FWD = 3, QLORA_K_GEMM_DX = 4, QLORA_K_GEMV = 5, QLORA_K_GEMV_EPILOGUE = 6,
