@@ -10,7 +10,10 @@
 // Kernel design
 //  * quantize_kernel: one lane per 16-byte chunk (8 weights), 8 lanes per
 //    block, coalesced 16-byte loads and 4-byte code stores; each lane takes
-//    QU chunks 256 lanes apart and issues their loads together. The block absmax
+//    QU chunks 256 lanes apart per tile, and a workgroup (8 per CU) loops over
+//    tiles with the next tile's loads issued before the current tile is
+//    coded, so the table and the LDS histogram are set up once per
+//    workgroup and the loads stream without gaps. The block absmax
 //    is a DPP max over the 8 lanes on the bf16 magnitude bits. The code
 //    decision is division-free and bit-exact: the chunk's x is located in
 //    one of 65 cells (approximate reciprocal), the cell's single candidate
@@ -43,7 +46,13 @@
 namespace {
 
 constexpr int QT = 256;
-constexpr int QU = 2;      // chunks per lane (measured: 8 -> 19.0 us, 4 -> 16.4, 2 -> 15.6, 1 -> 17.5 at 4096x4096)
+// Tile = QU chunks per lane (QT QU chunks); QWPC workgroups per CU loop over
+// the tiles with the next tile's loads in flight. Measured quantise + DQ call
+// (4096x4096 / 22016x8192, us): one workgroup per tile, QU = 2: 24.1 / 131;
+// persistent QU = 2, 8 per CU: 23.2 / 121 (4 per CU 23.5 / 124, 2 per CU
+// 25.5 / 149; QU = 1 or 4 within 2% at 8 per CU).
+constexpr int QU = 2;
+constexpr int QWPC = 8;
 constexpr int NHC = 8;     // global histogram copies (workgroup b adds to copy b % NHC)
 constexpr int GPW = 8;     // double-quant groups per encode workgroup
 
@@ -98,17 +107,31 @@ QL_DEV uint32_t encode8(const uint32_t u[4], float a, const Cell *cell) {
   return (a == 0.0f) ? 0x77777777u : packed;
 }
 
+// Loads of tile t: chunk t * QT * QU + tid + u * QT for u < QU, at a clamped
+// index (a chunk past the end is never stored).
+QL_DEV void load_tile(const uint4 *__restrict__ W, int64_t nchunks, int64_t t, int tid,
+                      uint4 (&v)[QU]) {
+  const int64_t base = t * (QT * QU) + tid;
+#pragma unroll
+  for (int u = 0; u < QU; ++u) v[u] = W[min(base + u * QT, nchunks - 1)];
+}
+
 template <bool DQ>
 __global__ __launch_bounds__(QT) void quantize_kernel(
     const uint4 *__restrict__ W, uint32_t *__restrict__ codes,
     float *__restrict__ absmax_out, unsigned long long *__restrict__ hist,
-    int64_t nchunks) {
+    int64_t nchunks, int64_t ntiles) {
   __shared__ Cell cell[NF4_NCELL];
   // 8 private 32-bit copies of the histogram, one per block-leader slot of a
-  // wave (lanes 0, 8, .., 56), so the LDS atomics rarely collide; a copy
-  // receives at most 16 significands (< 2^12) per workgroup
+  // wave (lanes 0, 8, .., 56), so the LDS atomics rarely collide; an entry
+  // receives at most 4 QU significands (< 2^8 each) per tile, so it holds the
+  // sums of up to 2^20 tiles per workgroup
   __shared__ uint32_t lh8[8][256];
   const int tid = threadIdx.x;
+  // the first tile's loads go out before the table is set up
+  int64_t t = blockIdx.x;
+  uint4 v[QU];
+  load_tile(W, nchunks, t, tid, v);
   if (tid < NF4_NCELL) {
     const int j = c_cell[tid];
     cell[tid].T = __uint_as_float(c_thresh[j]);
@@ -117,39 +140,40 @@ __global__ __launch_bounds__(QT) void quantize_kernel(
   if (DQ)
 #pragma unroll
     for (int i = 0; i < 8; ++i) lh8[i][tid] = 0u;
-  const int64_t base = (int64_t)blockIdx.x * (QT * QU) + tid;
-  // the QU chunks of this lane, loads first; n % 64 == 0, so the 8 lanes of
-  // a block agree on validity
-  uint4 v[QU];
-#pragma unroll
-  for (int u = 0; u < QU; ++u) {
-    const int64_t ch = base + u * QT;
-    v[u] = ch < nchunks ? W[ch] : make_uint4(0u, 0u, 0u, 0u);
-  }
   __syncthreads();
+  // tiles t, t + G, ...: the next tile's loads are in flight while this one
+  // is coded (in the last round they re-read this tile, from cache)
+  for (; t < ntiles; t += gridDim.x) {
+    uint4 vn[QU];
+    load_tile(W, nchunks, t + gridDim.x < ntiles ? t + gridDim.x : t, tid, vn);
+    const int64_t base = t * (QT * QU) + tid;
 #pragma unroll
-  for (int u = 0; u < QU; ++u) {
-    const int64_t ch = base + u * QT;
-    const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-    uint32_t m = 0;
+    for (int u = 0; u < QU; ++u) {
+      const int64_t ch = base + u * QT;
+      const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) m = max(m, max(w4[i] & 0x7fffu, (w4[i] >> 16) & 0x7fffu));
-    const uint32_t mb = max8_dpp(m);
-    const float a = __uint_as_float(mb << 16);
-    uint32_t packed;
-    if (__builtin_expect(__any(a < 0x1p-90f && a > 0.0f), 0))
-      packed = encode8<true>(w4, a, cell);
-    else
-      packed = encode8<false>(w4, a, cell);
-    const bool ok = ch < nchunks;
-    if (ok) codes[ch] = packed;
-    const bool leader = ok && (ch & 7) == 0;
-    if (leader) absmax_out[ch >> 3] = a;
-    if (DQ) {
-      const uint32_t t = mb >> 7, man = mb & 0x7fu;
-      const uint32_t sig = t ? (man | 0x80u) : man;
-      if (leader && sig) atomicAdd(&lh8[(tid >> 3) & 7][t ? t : 1u], sig);
+      for (int i = 0; i < 4; ++i) m = max(m, max(w4[i] & 0x7fffu, (w4[i] >> 16) & 0x7fffu));
+      const uint32_t mb = max8_dpp(m);
+      const float a = __uint_as_float(mb << 16);
+      uint32_t packed;
+      if (__builtin_expect(__any(a < 0x1p-90f && a > 0.0f), 0))
+        packed = encode8<true>(w4, a, cell);
+      else
+        packed = encode8<false>(w4, a, cell);
+      // n % 64 == 0, so the 8 lanes of a block agree on validity
+      const bool ok = ch < nchunks;
+      if (ok) codes[ch] = packed;
+      const bool leader = ok && (ch & 7) == 0;
+      if (leader) absmax_out[ch >> 3] = a;
+      if (DQ) {
+        const uint32_t e = mb >> 7, man = mb & 0x7fu;
+        const uint32_t sig = e ? (man | 0x80u) : man;
+        if (leader && sig) atomicAdd(&lh8[(tid >> 3) & 7][e ? e : 1u], sig);
+      }
     }
+#pragma unroll
+    for (int u = 0; u < QU; ++u) v[u] = vn[u];
   }
   if (DQ) {
     __syncthreads();
@@ -168,11 +192,31 @@ __global__ void zero_u64_kernel(unsigned long long *p, int n) {
 
 // mu = nearest float32 (ties to even) of N / nb, N the numerator in units of
 // 2^-197 scaled by 2^64, held as 12 32-bit limbs whose sums `limb` still lack
-// their carries. Executed by one lane. The long division goes 16 bits at a
-// time in fp64: each partial dividend r * 2^16 + d (r < nb < 2^32) is below
-// 2^48 and exact, the quotient is below 2^16, and an integer quotient k - e
-// (e >= 1/nb) sits more than 2^-48 relatively below k, so the correctly
-// rounded fp64 quotient never reaches k: its floor is the integer quotient.
+// their carries. Executed by one lane; sq is LDS scratch for the quotient
+// limbs (read at run-time positions).
+// Long division, 16 quotient bits per step, in fp64: each partial dividend
+// c = r * 2^16 + d (r < nb < 2^32) is an integer below 2^48, held exactly.
+// The digit is floor(c * (1/nb)) corrected once: the product's relative error
+// is below 2^-52 and c / nb < 2^16, so it is within 2^-36 of c / nb and its
+// floor is the digit or one off; r' = c - q nb (exact: an integer below
+// 2^49) outside [0, nb) moves q by one.
+// Only the quotient limbs down to the one holding the guard bit are formed:
+// below it the rest of the quotient is nonzero exactly when the running
+// remainder or a lower limb of N is, which is all the sticky bit needs.
+QL_DEV uint32_t div_digit16(double c, double dn, double inv, double &r) {
+  double q = floor(c * inv);
+  double rr = fma(-q, dn, c);
+  if (rr < 0.0) {
+    q -= 1.0;
+    rr += dn;
+  } else if (rr >= dn) {
+    q += 1.0;
+    rr -= dn;
+  }
+  r = rr;
+  return (uint32_t)q;
+}
+
 QL_DEV float mean_from_limbs(const unsigned long long *limb, uint32_t *sq, uint32_t nb) {
   uint32_t N[12];
   unsigned long long carry = 0;
@@ -185,40 +229,47 @@ QL_DEV float mean_from_limbs(const unsigned long long *limb, uint32_t *sq, uint3
     nonzero |= N[i] != 0u;
   }
   if (!nonzero || nb == 0) return 0.0f;
-  const double dn = (double)nb;
-  uint32_t Q[12];
-  unsigned long long rem = 0;
+  const double dn = (double)nb, inv = 1.0 / dn;
+  double rem = 0.0;
+  bool started = false, done = false, lower = false;
+  int E = 0, e_eff = 0, sh = 0, gl = 0;
 #pragma unroll
   for (int i = 11; i >= 0; --i) {
     uint32_t qw = 0;
-    if (rem != 0 || N[i] != 0u) {
-      const double c1 = (double)((rem << 16) | (N[i] >> 16));
-      const double q1 = floor(c1 / dn);
-      const double c2 = (c1 - q1 * dn) * 65536.0 + (double)(N[i] & 0xFFFFu);
-      const double q2 = floor(c2 / dn);
-      rem = (unsigned long long)(c2 - q2 * dn);
-      qw = ((uint32_t)q1 << 16) | (uint32_t)q2;
+    if (done) {
+      lower |= N[i] != 0u;   // a limb below the stop
+    } else if (rem != 0.0 || N[i] != 0u) {
+      double r1;
+      const uint32_t q1 = div_digit16(rem * 65536.0 + (double)(N[i] >> 16), dn, inv, r1);
+      const uint32_t q2 = div_digit16(r1 * 65536.0 + (double)(N[i] & 0xFFFFu), dn, inv, rem);
+      qw = (q1 << 16) | q2;
     }
-    Q[i] = qw;
     sq[i] = qw;
+    if (!done) {
+      if (!started && qw != 0u) {
+        started = true;
+        const int p = 32 * i + 31 - __builtin_clz(qw);
+        E = p - 197;
+        e_eff = E < -126 ? -126 : E;
+        sh = e_eff - 23 + 197;  // bit of the quotient holding the float32 ulp (>= 48)
+        gl = (sh - 1) >> 5;     // limb of the guard bit
+      }
+      if (started && i <= gl) done = true;
+    }
   }
-  int top = 0;
-#pragma unroll
-  for (int i = 1; i < 12; ++i) if (Q[i]) top = i;
-  const int p = 32 * top + 31 - __builtin_clz(sq[top]);
-  const int E = p - 197;
-  int e_eff = E < -126 ? -126 : E;
-  const int sh = e_eff - 23 + 197;  // bit of Q holding the float32 ulp (>= 48)
+  if (!started) return 0.0f;  // N < nb: below 2^-197 (not reachable from bf16 inputs)
+  // the stop was at limb gl, or at limb 0 below it (a quotient whose top limb
+  // lies under the guard's): formed limbs below the guard's count as they are
+  lower |= rem != 0.0;
+  for (int j = 0; j < gl; ++j) lower |= sq[j] != 0u;
   const int li = sh >> 5, lb = sh & 31;
   const unsigned long long win = (unsigned long long)sq[li] |
                                  ((unsigned long long)sq[li + 1] << 32);  // li <= 10
   uint32_t mant = (uint32_t)((win >> lb) & 0xFFFFFFull);
-  const int g = sh - 1, gl = g >> 5, gb = g & 31;
+  const int gb = (sh - 1) & 31;
   const uint32_t gw = sq[gl];
   const uint32_t guard = (gw >> gb) & 1u;
-  bool sticky = rem != 0 || (gw & ((1u << gb) - 1u)) != 0u;
-#pragma unroll
-  for (int i = 0; i < 12; ++i) sticky |= (i < gl) && Q[i] != 0u;
+  const bool sticky = lower || (gw & ((1u << gb) - 1u)) != 0u;
   if (guard && (sticky || (mant & 1u))) ++mant;
   uint32_t bits;
   if (E >= -126) {
@@ -232,6 +283,20 @@ QL_DEV float mean_from_limbs(const unsigned long long *limb, uint32_t *sq, uint3
     bits = mant;  // subnormal (or the smallest normal after rounding up)
   }
   return __uint_as_float(bits);
+}
+
+// max over the 64 lanes of a wave (every lane gets it): rows of 16 by DPP,
+// then the four row maxima by readlane
+QL_DEV uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half-row mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
 }
 
 // Double quantisation in one launch. Every workgroup first derives the exact
@@ -286,28 +351,31 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(
   for (int j = 0; j < GPW; ++j) {
     // blocks past nb (the last group's tail) take no part in the group max
     dv[j] = (g0 + j) * 256 + tid < nb ? av[j] - mu : 0.0f;
-    uint32_t m = __float_as_uint(fabsf(dv[j]));
-    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    const uint32_t m = wave_max_u32(__float_as_uint(fabsf(dv[j])));
     if ((tid & 63) == 0) wmax[j][tid >> 6] = m;
   }
   __syncthreads();
+  // group scales, then the codes of all groups (no early exit, so the
+  // groups' divisions interleave); blocks past nb are not stored
+  float sc[GPW];
+#pragma unroll
+  for (int j = 0; j < GPW; ++j)
+    sc[j] = __uint_as_float(max(max(wmax[j][0], wmax[j][1]), max(wmax[j][2], wmax[j][3]))) / 127.0f;
+  if (tid == 0) {
+#pragma unroll
+    for (int j = 0; j < GPW; ++j)
+      if (g0 + j < ng) s2[g0 + j] = sc[j];
+  }
 #pragma unroll
   for (int j = 0; j < GPW; ++j) {
-    const int64_t G = g0 + j;
-    if (G >= ng) break;
-    const uint32_t gm = max(max(wmax[j][0], wmax[j][1]), max(wmax[j][2], wmax[j][3]));
-    const float sc = __uint_as_float(gm) / 127.0f;
-    if (tid == 0) s2[G] = sc;
-    const int64_t b = G * 256 + tid;
-    if (b < nb) {
-      int qi = 0;
-      if (sc != 0.0f) {
-        float r = rintf(dv[j] / sc);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        qi = (int)r;
-      }
-      q[b] = (int8_t)qi;
+    int qi = 0;
+    if (sc[j] != 0.0f) {
+      float r = rintf(dv[j] / sc[j]);
+      r = fminf(fmaxf(r, -127.0f), 127.0f);
+      qi = (int)r;
     }
+    const int64_t b = (g0 + j) * 256 + tid;
+    if (b < nb) q[b] = (int8_t)qi;
   }
 }
 
@@ -323,11 +391,12 @@ qlora_status launch_quantize(const uint16_t *W0, int64_t n, uint8_t *codes,
                              float *absmax_out, int dq, int8_t *q, float *s2,
                              float *mu, void *ws, hipStream_t st) {
   const int64_t nchunks = n / 8, nb = n / 64;
-  const int64_t grid = ql_cdiv(nchunks, QT * QU);
+  const int64_t ntiles = ql_cdiv(nchunks, QT * QU);
+  const int64_t grid = std::min<int64_t>(ntiles, (int64_t)QWPC * ql_num_cus());
   if (!dq) {
     QlProf prof(QLORA_K_QUANTIZE, st);
     quantize_kernel<false><<<(unsigned)grid, QT, 0, st>>>((const uint4 *)W0, (uint32_t *)codes,
-                                                 absmax_out, nullptr, nchunks);
+                                                 absmax_out, nullptr, nchunks, ntiles);
     QL_LAUNCH_CHECK();
     return QLORA_OK;
   }
@@ -337,7 +406,7 @@ qlora_status launch_quantize(const uint16_t *W0, int64_t n, uint8_t *codes,
   {
     QlProf prof(QLORA_K_QUANTIZE, st);
     quantize_kernel<true><<<(unsigned)grid, QT, 0, st>>>((const uint4 *)W0, (uint32_t *)codes, amax,
-                                                hist, nchunks);
+                                                hist, nchunks, ntiles);
   }
   {
     QlProf prof(QLORA_K_DOUBLE_QUANT, st);
