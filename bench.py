@@ -337,6 +337,7 @@ def measure_rows(ops, synth, torch, dev):
     """Per-row measurements (quantise, dequantise, GEMV, merge): call time of
     back-to-back calls on inputs rotated through more than the last-level
     cache, and the main kernel's event-bracketed time from a separate pass."""
+    import numpy as np
     out = {}
     # quantise / dequantise: 12 distinct 4096x4096 weights (403 MB bf16)
     nset = 12
@@ -421,7 +422,12 @@ def measure_rows(ops, synth, torch, dev):
     fq3 = lambda i: ops.linear_fwd_multi(wq, Xq, Aq, Bq, ALPHA, save_h=False, Ys=Yq, ws=wsq3)
     f3 = lambda i: [ops.linear_fwd(wq[j], Xq, Aq[j], Bq[j], ALPHA, save_h=False, Y=Yq[j])
                     for j in range(3)]
-    ms_multi, ms_three = _call_ms(fq3, 1, 20), _call_ms(f3, 1, 20)
+    # alternate the two forms so neither gets a clock or cache state of its own
+    tm, t3 = [], []
+    for _ in range(5):
+        t3.append(_call_ms(f3, 1, 20))
+        tm.append(_call_ms(fq3, 1, 20))
+    ms_multi, ms_three = float(np.median(tm)), float(np.median(t3))
     qflops = 3 * (2 * M * D * K + 4 * M * R * D)
     out["qkv_fwd_multi"] = {"shape": [3, D, K], "tokens": M, "r": R,
                             "multi_call_us": round(1e3 * ms_multi, 2),
