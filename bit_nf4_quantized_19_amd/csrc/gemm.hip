@@ -148,6 +148,9 @@ struct Tile {
   int chalf, crow_off, ccol, srow, sblk, dcol;
 
   f32x16 acc[2][2];
+  // the rank-r epilogue's operands of rank chunk 0 (L rows of the forward's
+  // whole-piece path, and the S hi/lo parts), loaded before the last K-steps
+  uint4 pre_a[2], pre_b[2][2];
 
   // tile (tm, tn): token rows tm*BM.., output columns tn*BN..
   QL_DEV void init(const GemmArgs &ga, int64_t tm, int64_t tn) {
@@ -422,6 +425,7 @@ struct Tile {
       step<1, false>(s + 1);
       step<2, false>(s + 2);
     }
+    lora_prefetch();
     for (; s < nk; s += 3) {
       step<0, true>(s);
       if (s + 1 < nk) step<1, true>(s + 1);
@@ -466,6 +470,30 @@ struct Tile {
     store();
   }
 
+  // Unconditional loads from clamped addresses (their latency then runs
+  // under the last K-steps); out-of-range lanes are zeroed where used.
+  QL_DEV void lora_prefetch() {
+    if (MODE == 0 && g.r % 8 == 0) {
+      const int tq = 8 * h < g.r ? 8 * h : g.r - 8;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t n = n0 + wn * 64 + 32 * i + r32;
+        const int64_t nc = n < g.Ntot ? n : g.Ntot - 1;
+        pre_a[i] = *(const uint4 *)(g.L + nc * g.r + tq);
+      }
+    }
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      const uint16_t *S = part ? g.Slo : g.Shi;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t m = m0 + wm * 64 + 32 * j + r32;
+        const int64_t mc = m < g.M ? m : g.M - 1;
+        pre_b[part][j] = *(const uint4 *)(S + mc * g.rp + 8 * h);
+      }
+    }
+  }
+
   QL_DEV void lora_term(f32x16 (&dst)[2][2]) {
     for (int t0 = 0; t0 < g.rp; t0 += 16) {
       // L[n][t0 + 8h .. +7] read in place (ranks past r and n past Ntot: 0);
@@ -478,7 +506,8 @@ struct Tile {
         for (int i = 0; i < 2; ++i) {
           const int64_t n = n0 + wn * 64 + 32 * i + r32;
           const int64_t nc = n < g.Ntot ? n : g.Ntot - 1;
-          const uint4 v = *(const uint4 *)(g.L + nc * g.r + (tq < g.r ? tq : g.r - 8));
+          const uint4 v = t0 == 0 ? pre_a[i]
+                                  : *(const uint4 *)(g.L + nc * g.r + (tq < g.r ? tq : g.r - 8));
           a[i] = (n < g.Ntot && tq < g.r) ? v : ql::zero4();
         }
       } else {
@@ -515,7 +544,10 @@ struct Tile {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int64_t m = m0 + wm * 64 + 32 * j + r32;
-          b[j] = (m < g.M) ? *(const uint4 *)(S + m * g.rp + t0 + 8 * h) : ql::zero4();
+          if (t0 == 0)
+            b[j] = m < g.M ? pre_b[part][j] : ql::zero4();
+          else
+            b[j] = (m < g.M) ? *(const uint4 *)(S + m * g.rp + t0 + 8 * h) : ql::zero4();
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
