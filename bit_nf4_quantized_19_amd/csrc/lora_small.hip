@@ -411,10 +411,14 @@ __global__ __launch_bounds__(256) void colacc_kernel(ColaccProb p0, ColaccProb p
 #pragma unroll
     for (int b = 0; b < RPM / 16; ++b) {
       if (b >= tbs) break;
-      float *dst = P.part + ((int64_t)split * P.C + c) * rp + 16 * b + 4 * g;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __hip_atomic_store(dst + i, acc[b][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // four consecutive ranks: two 8-byte stores (the offset is a multiple of 16 bytes)
+      uint64_t *dst = (uint64_t *)(P.part + ((int64_t)split * P.C + c) * rp + 16 * b + 4 * g);
+      const uint64_t w0 = (uint64_t)__float_as_uint(acc[b][0]) |
+                          ((uint64_t)__float_as_uint(acc[b][1]) << 32);
+      const uint64_t w1 = (uint64_t)__float_as_uint(acc[b][2]) |
+                          ((uint64_t)__float_as_uint(acc[b][3]) << 32);
+      __hip_atomic_store(dst, w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst + 1, w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   // the last workgroup of this column block adds the S partials in order
@@ -425,37 +429,56 @@ __global__ __launch_bounds__(256) void colacc_kernel(ColaccProb p0, ColaccProb p
     s_last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
   __syncthreads();
   if (!s_last) return;
-  // four outputs per pass, all their S partial loads issued before any sum
-  for (int o0 = 0; o0 < CM_COLS * r; o0 += 4 * 256) {
-    float p[4][CM_MAXSPLIT];
-    int64_t oi[4];
+  // thread (col = tid / 4, q = tid % 4) adds ranks 16 b + 4 q .. +3 of column
+  // c0 + col over the S splits in split order; each split's four values are
+  // two 8-byte agent-scope loads from a clamped (always valid) split, four
+  // splits' loads in flight before their sums
+  {
+    const int col = tid >> 2, q4 = tid & 3;
+    const int64_t cc = c0 + col;
+    const bool cok = cc < P.C;
+    const int64_t ccl = cok ? cc : c0;
+    for (int b = 0; b < tbs; ++b) {
+      float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int s0 = 0; s0 < S; s0 += 4) {
+        // addresses first (all live at once), then the eight loads back to back
+        const uint64_t *src[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int o = o0 + 256 * j + tid;
-      int col, t;
-      if (P.transpose_out) {
-        t = o / CM_COLS;
-        col = o % CM_COLS;
-      } else {
-        col = o / r;
-        t = o % r;
+        for (int u = 0; u < 4; ++u) {
+          const int sp = s0 + u < S ? s0 + u : s0;
+          src[u] = (const uint64_t *)(P.part + ((int64_t)sp * P.C + ccl) * rp + 16 * b + 4 * q4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        uint64_t w[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          w[u][0] = __hip_atomic_load(src[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          w[u][1] = __hip_atomic_load(src[u] + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (s0 + u >= S) break;
+          v[0] += __uint_as_float((uint32_t)w[u][0]);
+          v[1] += __uint_as_float((uint32_t)(w[u][0] >> 32));
+          v[2] += __uint_as_float((uint32_t)w[u][1]);
+          v[3] += __uint_as_float((uint32_t)(w[u][1] >> 32));
+        }
       }
-      const int64_t cc = c0 + col;
-      const bool ok = o < CM_COLS * r && cc < P.C;
-      oi[j] = ok ? (P.transpose_out ? (int64_t)t * P.C + cc : cc * r + t) : -1;
+      // all four results first, then the stores (one 8-byte store when the
+      // four ranks are consecutive and aligned in out)
+      uint32_t ob[4];
 #pragma unroll
-      for (int sp = 0; sp < CM_MAXSPLIT; ++sp)
-        p[j][sp] = (ok && sp < S) ? __hip_atomic_load(P.part + ((int64_t)sp * P.C + cc) * rp + t,
-                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                  : 0.0f;
-    }
+      for (int i = 0; i < 4; ++i) ob[i] = ql::f_to_bf16(P.scale * v[i]);
+      const int t4 = 16 * b + 4 * q4;
+      if (cok && !P.transpose_out && (r & 3) == 0 && t4 < r) {
+        *(uint2 *)(P.out + cc * r + t4) = make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
+      } else if (cok) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float v = 0.0f;
-#pragma unroll
-      for (int sp = 0; sp < CM_MAXSPLIT; ++sp)
-        if (sp < S) v += p[j][sp];
-      if (oi[j] >= 0) P.out[oi[j]] = ql::f_to_bf16(P.scale * v);
+        for (int i = 0; i < 4; ++i)
+          if (t4 + i < r)
+            P.out[P.transpose_out ? (int64_t)(t4 + i) * P.C + cc : cc * r + t4 + i] = (uint16_t)ob[i];
+      }
     }
   }
   if (tid == 0)   // left clear for the next call on this workspace
