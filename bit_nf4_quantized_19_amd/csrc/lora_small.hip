@@ -186,13 +186,16 @@ __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
   red[wave][lane] = acc;
   __syncthreads();
   if (wave != 0) return;
-  f32x4 v = red[0][lane];
+  // all the waves' partials read first (one LDS latency), then added in wave order
+  f32x4 x[SK_W];
 #pragma unroll
-  for (int w = 1; w < SK_W; ++w) {
-    const f32x4 x = red[w][lane];
+  for (int w = 0; w < SK_W; ++w) x[w] = red[w][lane];
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 v = x[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] += x[i];
-  }
+  for (int w = 1; w < SK_W; ++w)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += x[w][i];
   const int t = t0 + r16;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
