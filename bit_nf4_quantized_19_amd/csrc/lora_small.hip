@@ -338,11 +338,15 @@ QL_DEV void cm_compute(f32x4 (&acc)[RPM / 16], const uint32_t *sin, const uint16
   }
 }
 
+// Chunks in flight per thread, and the target workgroup count from which
+// the token split S is derived. Measured at 4096x4096, 2048 tokens, r = 16
+// (dA + dB launch, us): target 256 / 512 / 640 / 768 / 896 / 1024 ->
+// 18.8 / 16.4 / 15.9 / 15.7 / 15.6 / 17.5; three chunks in flight no better.
 #ifndef QL_CM_PF
 #define QL_CM_PF 2
 #endif
 #ifndef QL_CM_WGS
-#define QL_CM_WGS 512
+#define QL_CM_WGS 768
 #endif
 constexpr int CM_PF = QL_CM_PF;   // chunks whose loads are in flight per thread
 
@@ -489,7 +493,7 @@ __global__ __launch_bounds__(256) void colacc_kernel(ColaccProb p0, ColaccProb p
 }
 
 int64_t colacc_split(int64_t M, int64_t C0, int64_t C1) {
-  // about four workgroups per compute unit, each split at least one chunk
+  // about three workgroups per compute unit, each split at least one chunk
   const int64_t blocks = ql_cdiv(C0, CM_COLS) + ql_cdiv(C1, CM_COLS);
   int64_t S = ql_cdiv(QL_CM_WGS, blocks);
   S = std::min<int64_t>(S, ql_cdiv(M, 128));
