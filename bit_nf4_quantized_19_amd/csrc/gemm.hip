@@ -146,6 +146,10 @@ struct Tile {
   // dX block column.
   int64_t crow64, srow64, drow64;
   int chalf, crow_off, ccol, srow, sblk, dcol;
+  // dX decode: bit offset of row i's int8 scale code in its dword. Row j of
+  // step kk is kk + 4 jg + i with kk a multiple of 64, so j % 4 == i and the
+  // block index j (k / 64) + dcol / 64 has the same value mod 4 in every step.
+  int qsh[4];
 
   f32x16 acc[2][2];
   // the rank-r epilogue's operands of rank chunk 0 (L rows of the forward's
@@ -196,6 +200,9 @@ struct Tile {
       sblk = (int)(c0 < g.k ? c0 : g.k - 64);
       const int64_t dc = n0 + 64 * (((tid >> 1) & 31) >> 4);
       dcol = (int)(dc < g.k ? dc : g.k - 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        qsh[i] = 8 * (int)(((uint32_t)i * (uint32_t)(g.k >> 6) + (uint32_t)(dcol >> 6)) & 3u);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -294,19 +301,39 @@ struct Tile {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         di.c[i] = raw[(4 * jg + i) * 32 + kg];
-        const int64_t j = kk + 4 * jg + i;
-        const int64_t jc = j < g.d ? j : g.d - 1;
-        // only blk % 4 is used (the int8 code's byte in its dword): 32-bit math
-        const int64_t blk = (int64_t)((uint32_t)jc * (uint32_t)(g.k >> 6) + (uint32_t)(dcol >> 6));
-        const float v = scale_of<DQ>(sQ<CS>()[8 * jg + 2 * i + bsel],
-                                     sS<CS>()[8 * jg + 2 * i + bsel], blk, mu);
-        di.a[i] = j < g.d ? v : 0.0f;  // rows past d: zero
+        const uint32_t qd = sQ<CS>()[8 * jg + 2 * i + bsel];
+        const float s2 = sS<CS>()[8 * jg + 2 * i + bsel];
+        if (DQ) {
+          const int qv = (int)(int8_t)(qd >> qsh[i]);
+          const float prod = (float)qv * s2;
+          di.a[i] = prod + mu;
+        } else {
+          di.a[i] = __uint_as_float(qd);
+        }
       }
+      if (kk + BK > g.d) {   // the last step of a ragged K: rows past d are zero
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int sh = i == 0 ? 4 : i == 1 ? 0 : i == 2 ? 12 : 8;
+        for (int i = 0; i < 4; ++i)
+          if (kk + 4 * jg + i >= g.d) di.a[i] = 0.0f;
+      }
+      // level addresses as in the forward decode: two rows' code pairs in one
+      // word, each nibble times 4 in a byte lane (ev: high nibbles = columns
+      // 4kg and 4kg+2, od: low nibbles = columns 4kg+1 and 4kg+3), then one
+      // bit-field extract per level
+      const char *lvb = (const char *)s_lv;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) di.f[4 * i + q] = s_lv[(di.c[q] >> sh) & 15];
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const uint32_t w = di.c[2 * h2] | (di.c[2 * h2 + 1] << 16);
+        const uint32_t ev = (w >> 2) & 0x3C3C3C3Cu, od = (w << 2) & 0x3C3C3C3Cu;
+        // row 2 h2 in bytes 0-1, row 2 h2 + 1 in bytes 2-3
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int q = 2 * h2 + rr, sb = 16 * rr;
+          di.f[0 * 4 + q] = *(const float *)(lvb + __builtin_amdgcn_ubfe(ev, sb, 8));
+          di.f[1 * 4 + q] = *(const float *)(lvb + __builtin_amdgcn_ubfe(od, sb, 8));
+          di.f[2 * 4 + q] = *(const float *)(lvb + __builtin_amdgcn_ubfe(ev, sb + 8, 8));
+          di.f[3 * 4 + q] = *(const float *)(lvb + __builtin_amdgcn_ubfe(od, sb + 8, 8));
+        }
       }
     }
     return di;
