@@ -124,7 +124,10 @@ __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
   dp.mask = QL_SKPICK(dp.mask);
   constexpr int PQ = 272;   // bytes per lane group in the transposition slot (256 + pad)
   __shared__ f32x4 red[SK_W][64];
-  __shared__ __align__(16) unsigned char pst[PCOL ? SK_W : 1][4 * PQ];
+  // per-wave slot for re-laying out the P pieces of one K-slice: B's raw
+  // pieces (PCOL) or A's 16 rows of 64 bytes at a stride of 80 (!PCOL)
+  constexpr int AST = 80;
+  __shared__ __align__(16) unsigned char pst[SK_W][PCOL ? 4 * PQ : 16 * AST];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
   const int64_t mb = blockIdx.x;
@@ -133,10 +136,14 @@ __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
   const bool m_ok = r16 < SK_TOK && m < M;   // MFMA rows past SK_TOK stay zero
   const uint16_t *inr = In + (m_ok ? m : 0) * C + 8 * kq;
   const int64_t c_lo = wave * cpw, c_hi = min(C, c_lo + cpw);
-  const bool t_ok = t0 + r16 < r;
-  const uint16_t *prow = Pm + (t_ok ? t0 + r16 : 0) * C + 8 * kq;          // !PCOL
+  // !PCOL: A rows are loaded whole (lane -> row ra = lane / 4, 16-byte piece
+  // pa = lane % 4 of the slice's 64 bytes, so a quarter-wave reads 4 rows of
+  // 64 contiguous bytes) and re-laid out through the slot; rows past r read 0
+  const int ra = lane >> 2, pa = lane & 3;
+  const bool ta_ok = t0 + ra < r;
+  const uint16_t *prow = Pm + (ta_ok ? t0 + ra : 0) * C + 8 * pa;           // !PCOL
   const int rho = (lane >> 1) & 7, hf = lane & 1;                           // PCOL raw piece
-  unsigned char *slot = pst[PCOL ? wave : 0];
+  unsigned char *slot = pst[wave];
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int64_t c = c_lo; c < c_hi; c += 32 * SK_UNROLL) {
     uint4 a[SK_UNROLL], b[SK_UNROLL];
@@ -147,8 +154,8 @@ __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
       b[u] = ql::zero4();
       if (cc + 8 * kq < c_hi) {   // c_hi % 8 == 0: a chunk is all in or all out
         if (m_ok) a[u] = *(const uint4 *)(inr + cc);
-        if (!PCOL && t_ok) b[u] = *(const uint4 *)(prow + cc);
       }
+      if (!PCOL && ta_ok && cc + 8 * pa < c_hi) b[u] = *(const uint4 *)(prow + cc);
       if (dp.on) {   // dropped elements of X (token m, columns cc + 8kq ..) read as 0
         const uint64_t e = (uint64_t)(m_ok ? m : 0) * (uint64_t)C + (uint64_t)(cc + 8 * kq);
         const uint32_t k8 = keep4(dp, e) | (keep4(dp, e + 4) << 4);
@@ -161,6 +168,15 @@ __global__ __launch_bounds__(64 * SK_W) void skinny_kernel(SkinnyArgs a) {
       if (PCOL) {
         const int64_t row = cc + 8 * kq + rho;   // B row, t = t0 + 8 hf .. +7
         if (row < c_hi) b[u] = *(const uint4 *)(Pm + row * r + t0 + 8 * hf);
+      }
+    }
+    if (!PCOL) {
+      // lane (t = r16, kq) needs A[t][cc + 8kq .. +7]: row ra's piece pa in,
+      // row r16's piece kq out
+#pragma unroll
+      for (int u = 0; u < SK_UNROLL; ++u) {
+        *(uint4 *)(slot + ra * AST + pa * 16) = b[u];
+        b[u] = *(const uint4 *)(slot + r16 * AST + kq * 16);
       }
     }
     if (PCOL) {
