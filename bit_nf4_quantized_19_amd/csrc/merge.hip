@@ -7,11 +7,15 @@
 // with w' the bf16 dequantised weight and the rank-r product summed in
 // float32 (exact bf16 products, MFMA accumulation order).
 //
-// Workgroup tile: 4 waves x 32 rows, MC = 256 columns.
+// Workgroup tile: 4 waves x 32 rows, MC = 128 columns (256- and 64-column
+// tiles measured 10% and 15% slower per call at 4096x4096).
 //  * A^T of the tile's columns (all ranks, zero-padded to a multiple of 16)
-//    is staged once in LDS; the column pitch (2 rp + 16 bytes, an odd number
-//    of 16-byte slots) keeps the operand reads conflict-free.
-//  * Each wave keeps the B entries of its 32 rows in registers and walks the
+//    is staged once in LDS, each thread writing rank pairs as 4-byte words;
+//    the column pitch (2 rp + 16 bytes, an odd number of 16-byte slots) keeps
+//    the operand reads conflict-free.
+//  * Each wave keeps the B entries of its 32 rows in registers (one 16-byte
+//    load per rank chunk when r % 8 == 0, as the whole-piece loads cut the
+//    call by 8%) and walks the
 //    tile in 32-column blocks: 32x32x16 bf16 MFMAs give D[c][j] = (B A)[j][c]
 //    with lane (j, h) holding columns 8g + 4h .. 8g + 4h + 3 (g = 0..3) of
 //    row j, exactly the columns whose code nibbles it reads, so the update is
@@ -27,7 +31,7 @@
 
 namespace {
 
-constexpr int MC = 256, MT = 256, MNB = MC / 32;  // tile columns, threads, column blocks
+constexpr int MC = 128, MT = 256, MNB = MC / 32;  // tile columns, threads, column blocks
 constexpr int MAXRP = 128;
 __constant__ uint32_t c_levels_m[16] = NF4_LEVEL_BITS;
 
@@ -55,19 +59,21 @@ __global__ __launch_bounds__(MT) void merge_kernel(MergeArgs g) {
   const int64_t jc = min(j, g.d - 1);
   if (tid < 16) s_lv[tid] = __uint_as_float(c_levels_m[tid]);
 
-  // 1. A^T chunk loads: thread (t = tid % 16, 16-column segment tid / 16),
-  //    one 16-rank chunk per pass
+  // 1. A^T chunk loads, one 16-rank chunk per pass: thread (rank pair
+  //    tp = tid % 8, 8-column segment tid / 8) loads ranks 16 ch + 2tp, +1 of
+  //    columns 8 seg .. +7 (threads past MC repeat a segment; they write
+  //    nothing)
   uint4 av[NCH][2];
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) {
-    const int t = 16 * ch + (tid & 15);
-    const int64_t col = c0 + 16 * (tid >> 4);
+    const int t = 16 * ch + 2 * (tid & 7);
+    const int64_t col = c0 + 8 * ((tid >> 3) & (MC / 8 - 1));
     av[ch][0] = ql::zero4();
     av[ch][1] = ql::zero4();
-    if (t < g.r && col < g.k) {  // k % 64 == 0: the 16 columns are all in range
+    if (col < g.k) {  // k % 64 == 0: the 8 columns are all in range
       const uint16_t *src = g.A + (int64_t)t * g.k + col;
-      av[ch][0] = *(const uint4 *)src;
-      av[ch][1] = *(const uint4 *)(src + 8);
+      if (t < g.r) av[ch][0] = *(const uint4 *)src;
+      if (t + 1 < g.r) av[ch][1] = *(const uint4 *)(src + g.k);
     }
   }
   // 2. this lane's code words: row j, 32-column block b = 16 bytes (clamped
@@ -93,25 +99,41 @@ __global__ __launch_bounds__(MT) void merge_kernel(MergeArgs g) {
   const float mu = DQ ? g.sc.mu[0] : 0.0f;
   // B entries of row j, ranks 16 ch + 8h .. +7 (ranks past r are zero)
   uint32_t bw[NCH][4];
+  if (g.r % 8 == 0) {
+    // whole 16-byte pieces: ranks 16 ch + 8h .. +7 of row j, one load each
 #pragma unroll
-  for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * ch + 8 * h + 2 * i;
-      uint32_t lo = 0, hi = 0;
-      if (t < g.r) lo = g.B[jc * g.r + t];
-      if (t + 1 < g.r) hi = g.B[jc * g.r + t + 1];
-      bw[ch][i] = lo | (hi << 16);
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int t = 16 * ch + 8 * h;
+      const uint4 v = *(const uint4 *)(g.B + jc * g.r + (t < g.r ? t : g.r - 8));
+      const bool ok = t < g.r;
+      bw[ch][0] = ok ? v.x : 0u; bw[ch][1] = ok ? v.y : 0u;
+      bw[ch][2] = ok ? v.z : 0u; bw[ch][3] = ok ? v.w : 0u;
     }
+  } else {
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * ch + 8 * h + 2 * i;
+        uint32_t lo = 0, hi = 0;
+        if (t < g.r) lo = g.B[jc * g.r + t];
+        if (t + 1 < g.r) hi = g.B[jc * g.r + t + 1];
+        bw[ch][i] = lo | (hi << 16);
+      }
+  }
   // 3. A^T to LDS: column c at c * PITCH, rank t at byte 2t
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) {
-    const int t = 16 * ch + (tid & 15), seg = tid >> 4;
-    const uint32_t v[8] = {av[ch][0].x, av[ch][0].y, av[ch][0].z, av[ch][0].w,
-                           av[ch][1].x, av[ch][1].y, av[ch][1].z, av[ch][1].w};
+    if (tid >= MC) break;   // MC / 8 segments of 8 columns, 8 rank pairs each
+    const int t = 16 * ch + 2 * (tid & 7), seg = tid >> 3;
+    const uint32_t v0[4] = {av[ch][0].x, av[ch][0].y, av[ch][0].z, av[ch][0].w};
+    const uint32_t v1[4] = {av[ch][1].x, av[ch][1].y, av[ch][1].z, av[ch][1].w};
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      *(uint16_t *)(s_at + (16 * seg + i) * PITCH + 2 * t) = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t lo = (v0[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      const uint32_t hi = (v1[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      *(uint32_t *)(s_at + (8 * seg + i) * PITCH + 2 * t) = lo | (hi << 16);
+    }
   }
   __syncthreads();
 
