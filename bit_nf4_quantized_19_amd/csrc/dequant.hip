@@ -8,8 +8,10 @@
 // 2 out). A lane owns 4-byte code words (8 weights, one 16-byte output store);
 // a wave's load and store instructions each cover one contiguous run (256
 // bytes of codes, 1 KB of output), and every lane issues all its loads (DU
-// code words and their block-scale inputs) before the first use. Levels come
-// from a 16-entry LDS table (any lookup pattern is conflict-free).
+// code words and one block's scale inputs) before the first use: the 64
+// blocks of a wave's words get their a' from one lane each and reach the
+// lanes that need them by lane shuffles. Levels come from a 16-entry LDS
+// table (any lookup pattern is conflict-free).
 #include <algorithm>
 
 #include "kernels.h"
@@ -38,22 +40,25 @@ __global__ __launch_bounds__(DT) void dequant_kernel(const uint32_t *__restrict_
     idx[i] = w0 + 64 * i + lane;
     cw[i] = codes[min(idx[i], nchunks - 1)];
   }
-  float sa[DU], sb[DU];
-#pragma unroll
-  for (int i = 0; i < DU; ++i) {
-    const int64_t blk = min(idx[i], nchunks - 1) >> 3;
-    if (DQ) {
-      sa[i] = (float)sc.q[blk];
-      sb[i] = sc.s2[blk >> 8];
-    } else {
-      sa[i] = sc.absmax[blk];
-    }
+  // block scales: the wave's code words cover the 64 consecutive blocks
+  // w0 / 8 ..; lane l derives a' of block w0 / 8 + l (one load of each scale
+  // input), and the lane holding word i of block 8 i + lane / 8 takes it
+  // from lane 8 i + lane / 8
+  const int64_t nb = nchunks >> 3;
+  const int64_t blk = min((w0 >> 3) + lane, nb - 1);
+  float a_l;
+  if (DQ) {
+    const float qv = (float)sc.q[blk];
+    const float s2 = sc.s2[blk >> 8];
+    const float prod = qv * s2;
+    a_l = prod + sc.mu[0];
+  } else {
+    a_l = sc.absmax[blk];
   }
-  const float mu = DQ ? sc.mu[0] : 0.0f;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < DU; ++i) {
-    const float ap = DQ ? sa[i] * sb[i] + mu : sa[i];
+    const float ap = __shfl(a_l, 8 * i + (lane >> 3));
     const uint32_t c = cw[i];
     float f[8];
 #pragma unroll
