@@ -13,8 +13,9 @@
 //     the c range and issue the loads of eight 32-wide K-slices before their
 //     MFMAs, and the waves' sums are added in LDS in a fixed order; it also
 //     emits s*out as bf16 hi/lo parts for the fused GEMM epilogue. P is A
-//     (rows contiguous in c) or B read in place (columns contiguous in t),
-//     transposed per K-slice through LDS.
+//     (rows contiguous in c, loaded as 64-byte row segments) or B read in
+//     place (columns contiguous in t); either is re-laid out into the MFMA
+//     operand order per K-slice through the wave's LDS slot.
 //   * colacc: out[c][t] = s sum_m In[m][c] Q[m][t] on MFMA 16x16x32 with the
 //     tokens as the contraction (Q as bf16 hi + lo parts); a workgroup owns 64
 //     columns and one of S token ranges, streams token chunks through LDS with
