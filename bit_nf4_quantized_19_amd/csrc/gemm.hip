@@ -462,39 +462,51 @@ struct Tile {
 
   // LoRA rank-r term: two extra K-chunks per 16 of rp (hi and lo of S), then
   // the bf16 stores. Lane holds D[8(e/4) + 4(l/32) + e%4][l%32] = Out[m][n].
-  // With adapter-input dropout (dX only) the rank-r term goes to its own
-  // accumulators and is added where the input element was kept, times
-  // 1/(1-p): dX = dY W' + s (G A) * keep / (1 - p).
+  // With adapter-input dropout (dX only) the rank-r term of each 32 x 32
+  // block goes to an accumulator of its own and is added where the input
+  // element was kept, times 1/(1-p): dX = dY W' + s (G A) * keep / (1 - p).
   QL_DEV void epilogue() {
     if (MODE == 1 && g.keep) {
-      f32x16 lacc[2][2];
+      // keep bits of the lane's two token rows: byte (n - bc) / 4 of the
+      // wave's 64-column block bc (bit n % 4), one 16-byte load per row,
+      // issued before the rank-r products (Ntot % 64 == 0, so a block is
+      // either inside the row or wholly past it)
+      int64_t bc = n0 + wn * 64;
+      bc = bc + 64 <= g.Ntot ? bc : g.Ntot - 64;   // blocks past Ntot: not stored
+      uint4 kw[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int q = 0; q < 16; ++q) lacc[i][j][q] = 0.0f;
-      lora_term(lacc);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          int64_t m = m0 + wm * 64 + 32 * j + r32;
-          m = m < g.M ? m : g.M - 1;   // rows past M: not stored
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            int64_t n = n0 + wn * 64 + 32 * i + 8 * q4 + 4 * h;
-            n = n < g.Ntot ? n : g.Ntot - 4;   // columns past Ntot: not stored
-            const uint32_t kb = g.keep[m * (g.Ntot >> 2) + (n >> 2)];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if ((kb >> e) & 1u) acc[i][j][4 * q4 + e] += lacc[i][j][4 * q4 + e] * g.inv_keep;
-          }
-        }
+      for (int j = 0; j < 2; ++j) {
+        int64_t m = m0 + wm * 64 + 32 * j + r32;
+        m = m < g.M ? m : g.M - 1;   // rows past M: not stored
+        kw[j] = *(const uint4 *)(g.keep + m * (g.Ntot >> 2) + (bc >> 2));
+      }
+      keep_block<0, 0>(kw);
+      keep_block<0, 1>(kw);
+      keep_block<1, 0>(kw);
+      keep_block<1, 1>(kw);
     } else {
-      lora_term(acc);
+      lora_term<0, 2, 0, 2>(acc);
     }
     store();
+  }
+
+  // One 32 x 32 block of the dropout epilogue (one block at a time keeps the
+  // extra accumulator at 16 registers).
+  template <int I, int J>
+  QL_DEV void keep_block(const uint4 (&kw)[2]) {
+    f32x16 lacc[1][1];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) lacc[0][0][q] = 0.0f;
+    lora_term<I, 1, J, 1>(lacc);
+    const uint32_t w4[4] = {kw[J].x, kw[J].y, kw[J].z, kw[J].w};
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      // columns 32 I + 8 q4 + 4 h of the block: byte 8 I + 2 q4 + h
+      const uint32_t kb = w4[2 * I + (q4 >> 1)] >> (8 * (2 * (q4 & 1) + h));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((kb >> e) & 1u) acc[I][J][4 * q4 + e] += lacc[0][0][4 * q4 + e] * g.inv_keep;
+    }
   }
 
   // Unconditional loads from clamped addresses (their latency then runs
@@ -521,65 +533,67 @@ struct Tile {
     }
   }
 
-  QL_DEV void lora_term(f32x16 (&dst)[2][2]) {
+  // the rank-r term of the 32 x 32 blocks (I0 .., J0 ..), NI x NJ of them
+  template <int I0, int NI, int J0, int NJ>
+  QL_DEV void lora_term(f32x16 (&dst)[NI][NJ]) {
     for (int t0 = 0; t0 < g.rp; t0 += 16) {
       // L[n][t0 + 8h .. +7] read in place (ranks past r and n past Ntot: 0);
       // loads from clamped addresses, the zeroing applied afterwards
-      uint4 a[2];
+      uint4 a[NI];
       if (MODE == 0 && g.r % 8 == 0) {
         // forward, B rows of whole 16-byte pieces: one load per operand
         const int tq = t0 + 8 * h;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int64_t n = n0 + wn * 64 + 32 * i + r32;
+        for (int ii = 0; ii < NI; ++ii) {
+          const int64_t n = n0 + wn * 64 + 32 * (I0 + ii) + r32;
           const int64_t nc = n < g.Ntot ? n : g.Ntot - 1;
-          const uint4 v = t0 == 0 ? pre_a[i]
+          const uint4 v = t0 == 0 ? pre_a[I0 + ii]
                                   : *(const uint4 *)(g.L + nc * g.r + (tq < g.r ? tq : g.r - 8));
-          a[i] = (n < g.Ntot && tq < g.r) ? v : ql::zero4();
+          a[ii] = (n < g.Ntot && tq < g.r) ? v : ql::zero4();
         }
       } else {
-        // gather: all 16 loads issued before any use
-        uint32_t e[2][8];
+        // gather: all loads issued before any use
+        uint32_t e[NI][8];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int64_t n = n0 + wn * 64 + 32 * i + r32;
+        for (int ii = 0; ii < NI; ++ii) {
+          const int64_t n = n0 + wn * 64 + 32 * (I0 + ii) + r32;
           const int64_t nc = n < g.Ntot ? n : g.Ntot - 1;
 #pragma unroll
           for (int x = 0; x < 8; ++x) {
             const int t = t0 + 8 * h + x, tc = t < g.r ? t : g.r - 1;
-            e[i][x] = g.L[MODE == 0 ? nc * g.r + tc : (int64_t)tc * g.Ntot + nc];
+            e[ii][x] = g.L[MODE == 0 ? nc * g.r + tc : (int64_t)tc * g.Ntot + nc];
           }
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const bool n_ok = n0 + wn * 64 + 32 * i + r32 < g.Ntot;
+        for (int ii = 0; ii < NI; ++ii) {
+          const bool n_ok = n0 + wn * 64 + 32 * (I0 + ii) + r32 < g.Ntot;
           uint32_t w[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int t = t0 + 8 * h + 2 * q;
-            const uint32_t lo = (n_ok && t < g.r) ? e[i][2 * q] : 0u;
-            const uint32_t hi = (n_ok && t + 1 < g.r) ? e[i][2 * q + 1] : 0u;
+            const uint32_t lo = (n_ok && t < g.r) ? e[ii][2 * q] : 0u;
+            const uint32_t hi = (n_ok && t + 1 < g.r) ? e[ii][2 * q + 1] : 0u;
             w[q] = lo | (hi << 16);
           }
-          a[i] = make_uint4(w[0], w[1], w[2], w[3]);
+          a[ii] = make_uint4(w[0], w[1], w[2], w[3]);
         }
       }
 #pragma unroll
       for (int part = 0; part < 2; ++part) {
         const uint16_t *S = part ? g.Slo : g.Shi;
-        uint4 b[2];
+        uint4 b[NJ];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int64_t m = m0 + wm * 64 + 32 * j + r32;
+        for (int jj = 0; jj < NJ; ++jj) {
+          const int64_t m = m0 + wm * 64 + 32 * (J0 + jj) + r32;
           if (t0 == 0)
-            b[j] = m < g.M ? pre_b[part][j] : ql::zero4();
+            b[jj] = m < g.M ? pre_b[part][J0 + jj] : ql::zero4();
           else
-            b[j] = (m < g.M) ? *(const uint4 *)(S + m * g.rp + t0 + 8 * h) : ql::zero4();
+            b[jj] = (m < g.M) ? *(const uint4 *)(S + m * g.rp + t0 + 8 * h) : ql::zero4();
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) dst[i][j] = ql::mfma32(a[i], b[j], dst[i][j]);
+          for (int jj = 0; jj < NJ; ++jj) dst[ii][jj] = ql::mfma32(a[ii], b[jj], dst[ii][jj]);
       }
     }
   }
