@@ -27,7 +27,11 @@
 //   * fetching codes (waves 0-3) or block-scale words (waves 4-7) three
 //     steps ahead, also by LDS DMA;
 //   * decoding its share of the next step's W' tile (16 weights per lane)
-//     into LDS, three stages;
+//     into LDS, three stages (forward: levels from a 16-entry LDS table
+//     times the row's a'; dX: each lane first writes four entries of a
+//     per-row table of the 16 products bf16(level * a') over its wave's
+//     codes in the code stage, then reads each weight's product with one
+//     2-byte load, which needs no multiply or rounding per weight);
 //   * 16 v_mfma_f32_32x32x16_bf16 per step on its 64 (n) x 64 (m) eighth of
 //     the tile (2 x 4 waves), operands read from LDS.
 // Timeline probes of the four-wave form (one wave per SIMD, 64 x 128 per
@@ -71,7 +75,9 @@ struct GemmArgs {
 // LDS, one object per stage.
 __shared__ uint4 s_X0[BM * 8], s_X1[BM * 8], s_X2[BM * 8];  // In tiles, 256 rows x 128 B
 __shared__ uint4 s_W0[BN * 8], s_W1[BN * 8], s_W2[BN * 8];  // W' tiles, 128 rows x 128 B
-__shared__ uint4 s_C0[256], s_C1[256], s_C2[256];           // codes, 16 B per lane
+// codes, 16 B per lane (256-byte aligned: the dX decode's product tables
+// overwrite them in place, addressed by byte permutes within 256-byte windows)
+__shared__ __align__(256) uint4 s_C0[256], s_C1[256], s_C2[256];
 __shared__ uint32_t s_Q0[128], s_Q1[128], s_Q2[128];        // scale dword per entry
 __shared__ float s_S0[128], s_S1[128], s_S2[128];           // s2 per entry
 __shared__ float s_lv[16];
@@ -146,10 +152,16 @@ struct Tile {
   // dX block column.
   int64_t crow64, srow64, drow64;
   int chalf, crow_off, ccol, srow, sblk, dcol;
-  // dX decode: bit offset of row i's int8 scale code in its dword. Row j of
-  // step kk is kk + 4 jg + i with kk a multiple of 64, so j % 4 == i and the
-  // block index j (k / 64) + dcol / 64 has the same value mod 4 in every step.
-  int qsh[4];
+  // dX decode (patch rows 4jg..4jg+3, columns 4kg..4kg+3 of the step): the
+  // product-table entries this thread builds, levels 4 tm .. 4 tm + 3 of
+  // table row tr (and the bit offset of that row's int8 scale code in its
+  // dword: row j of step kk is kk + 4 jg + tr with kk a multiple of 64, so
+  // j % 4 == tr and the block index j (k / 64) + dcol / 64 has the same value
+  // mod 4 in every step); the byte offset of that entry pair in the stage;
+  // the tables' 256-byte window (jg) and the rows' offsets in it.
+  int tr, tqsh, toff, twin;
+  float tlv[4];
+  uint32_t roff[2];
 
   f32x16 acc[2][2];
   // the rank-r epilogue's operands of rank chunk 0 (L rows of the forward's
@@ -200,9 +212,22 @@ struct Tile {
       sblk = (int)(c0 < g.k ? c0 : g.k - 64);
       const int64_t dc = n0 + 64 * (((tid >> 1) & 31) >> 4);
       dcol = (int)(dc < g.k ? dc : g.k - 64);
+      const int jg = 2 * (tid >> 6) + (tid & 1), kg = (tid >> 1) & 31, bsel = kg >> 4;
+      tr = (kg & 15) >> 2;
+      const int tm = kg & 3;
+      tqsh = 8 * (int)(((uint32_t)tr * (uint32_t)(g.k >> 6) + (uint32_t)(dcol >> 6)) & 3u);
+      // table (row j, block b) holds bf16(level[c] * a'(j, b)) at byte 2c of
+      // the 32 bytes at 64 j + 32 b: the bytes of row j's codes of block b,
+      // read by the same wave before it overwrites them
+      toff = (4 * jg + tr) * 64 + bsel * 32 + 8 * tm;
+      twin = 256 * jg;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        qsh[i] = 8 * (int)(((uint32_t)i * (uint32_t)(g.k >> 6) + (uint32_t)(dcol >> 6)) & 3u);
+      for (int x = 0; x < 4; ++x) tlv[x] = __uint_as_float(c_levels_g[4 * tm + x]);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const uint32_t ra = (uint32_t)(4 * h2 + bsel) * 32u, rb = (uint32_t)(4 * h2 + 2 + bsel) * 32u;
+        roff[h2] = ra | (ra << 8) | (rb << 16) | (rb << 24);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -281,10 +306,8 @@ struct Tile {
   // slots (the row permutation alone gives 8).
   static constexpr int kParts = MODE == 0 ? 2 : 4;
   struct DecIn {
-    uint32_t c[4];   // forward: 2 code words; dX: 4 rows' 2-byte code pairs
-    float a[4];      // forward: a[0] = the row's a'; dX: a' of each row
-    float f[16];     // dX: the 16 levels, read as soon as the codes are in (their
-                     // LDS latency then overlaps the step's first matrix ops)
+    uint32_t c[4];   // forward: 2 code words; dX: the table-address bytes ev[0..1], od[0..1]
+    float a[4];      // forward: a[0] = the row's a'
   };
 
   template <int CS>
@@ -296,44 +319,40 @@ struct Tile {
       const int64_t blk = (drow64 * g.k + kk) >> 6;
       di.a[0] = scale_of<DQ>(sQ<CS>()[tid >> 2], sS<CS>()[tid >> 2], blk, mu);
     } else {
+      // dX: the patch's four rows' code pairs, and the a' of the table row
+      // this thread fills
       const int jg = 2 * (tid >> 6) + (tid & 1), kg = (tid >> 1) & 31, bsel = kg >> 4;
       const uint16_t *raw = (const uint16_t *)sC<CS>();
+      uint32_t c[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        di.c[i] = raw[(4 * jg + i) * 32 + kg];
-        const uint32_t qd = sQ<CS>()[8 * jg + 2 * i + bsel];
-        const float s2 = sS<CS>()[8 * jg + 2 * i + bsel];
-        if (DQ) {
-          const int qv = (int)(int8_t)(qd >> qsh[i]);
-          const float prod = (float)qv * s2;
-          di.a[i] = prod + mu;
-        } else {
-          di.a[i] = __uint_as_float(qd);
-        }
+      for (int i = 0; i < 4; ++i) c[i] = raw[(4 * jg + i) * 32 + kg];
+      const uint32_t qd = sQ<CS>()[8 * jg + 2 * tr + bsel];
+      const float s2 = sS<CS>()[8 * jg + 2 * tr + bsel];
+      float a;
+      if (DQ) {
+        const int qv = (int)(int8_t)(qd >> tqsh);
+        const float prod = (float)qv * s2;
+        a = prod + mu;
+      } else {
+        a = __uint_as_float(qd);
       }
-      if (kk + BK > g.d) {   // the last step of a ragged K: rows past d are zero
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (kk + 4 * jg + i >= g.d) di.a[i] = 0.0f;
-      }
-      // level addresses as in the forward decode: two rows' code pairs in one
-      // word, each nibble times 4 in a byte lane (ev: high nibbles = columns
-      // 4kg and 4kg+2, od: low nibbles = columns 4kg+1 and 4kg+3), then one
-      // bit-field extract per level
-      const char *lvb = (const char *)s_lv;
+      if (kk + 4 * jg + tr >= g.d) a = 0.0f;   // the last step of a ragged K: rows past d are zero
+      // the code reads above and the table write below touch the same bytes;
+      // LDS accesses of a wave execute in order, and the asm statements keep
+      // the compiler from reordering them
+      asm volatile("" ::: "memory");
+      *(uint2 *)((char *)sC<CS>() + toff) =
+          make_uint2(ql::pack_bf16x2(tlv[0] * a, tlv[1] * a), ql::pack_bf16x2(tlv[2] * a, tlv[3] * a));
+      asm volatile("" ::: "memory");
+      // table-address bytes, two rows per word: each nibble times 2 plus the
+      // row's table offset in the window (ev: high nibbles = columns 4kg and
+      // 4kg+2, od: low nibbles = columns 4kg+1 and 4kg+3; row 2 h2 in bytes
+      // 0-1, row 2 h2 + 1 in bytes 2-3)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const uint32_t w = di.c[2 * h2] | (di.c[2 * h2 + 1] << 16);
-        const uint32_t ev = (w >> 2) & 0x3C3C3C3Cu, od = (w << 2) & 0x3C3C3C3Cu;
-        // row 2 h2 in bytes 0-1, row 2 h2 + 1 in bytes 2-3
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          const int q = 2 * h2 + rr, sb = 16 * rr;
-          di.f[0 * 4 + q] = *(const float *)(lvb + __builtin_amdgcn_ubfe(ev, sb, 8));
-          di.f[1 * 4 + q] = *(const float *)(lvb + __builtin_amdgcn_ubfe(od, sb, 8));
-          di.f[2 * 4 + q] = *(const float *)(lvb + __builtin_amdgcn_ubfe(ev, sb + 8, 8));
-          di.f[3 * 4 + q] = *(const float *)(lvb + __builtin_amdgcn_ubfe(od, sb + 8, 8));
-        }
+        const uint32_t w = c[2 * h2] | (c[2 * h2 + 1] << 16);
+        di.c[h2] = ((w >> 3) & 0x1E1E1E1Eu) | roff[h2];
+        di.c[2 + h2] = ((w << 1) & 0x1E1E1E1Eu) | roff[h2];
       }
     }
     return di;
@@ -361,12 +380,23 @@ struct Tile {
       o.w = ql::pack_bf16x2(f[6] * a, f[7] * a);
       sW<WS>()[swz(tid >> 2, 4 * ((tid >> 1) & 1) + 2 * (tid & 1) + i)] = o;
     } else {
-      // column 4kg+i: nibble at bit 4, 0, 12, 8 of the 2-byte pair
+      // column 4kg+i of the patch: row r's bf16 W' from its table by a
+      // 2-byte read, the address = the window's upper bytes with the row's
+      // address byte (ev for even columns, od for odd; byte 2 (r%2) + i/2 of
+      // word r/2)
       const int jg = 2 * (tid >> 6) + (tid & 1), kg = (tid >> 1) & 31;
-      const float *f = &di.f[4 * i];
+      const uint32_t hb = lds_addr(sC<WS>()) + (uint32_t)twin;
+      uint32_t v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t x = di.c[(i & 1) * 2 + (r >> 1)];
+        const uint32_t sel = 0x07060500u | (uint32_t)(2 * (r & 1) + (i >> 1));
+        const uint32_t addr = __builtin_amdgcn_perm(hb, x, sel);
+        v[r] = *(const __attribute__((address_space(3))) uint16_t *)(uintptr_t)addr;
+      }
       uint2 o;
-      o.x = ql::pack_bf16x2(f[0] * di.a[0], f[1] * di.a[1]);
-      o.y = ql::pack_bf16x2(f[2] * di.a[2], f[3] * di.a[3]);
+      o.x = v[0] | (v[1] << 16);
+      o.y = v[2] | (v[3] << 16);
       ((uint2 *)sW<WS>())[2 * swz(4 * kg + i, jg >> 1) + (jg & 1)] = o;
     }
   }
