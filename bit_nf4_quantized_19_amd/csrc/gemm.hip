@@ -72,7 +72,10 @@ struct GemmArgs {
   float inv_keep;        // 1/(1-p)
 };
 
-// LDS, one object per stage.
+// LDS, one object per stage. The level table is the most aligned object, so
+// it is placed at LDS address 0 and the forward decode's table addresses need
+// no base added (an instruction offset cannot reach the top of 160 KB).
+__shared__ __align__(1024) float s_lv[16];
 __shared__ uint4 s_X0[BM * 8], s_X1[BM * 8], s_X2[BM * 8];  // In tiles, 256 rows x 128 B
 __shared__ uint4 s_W0[BN * 8], s_W1[BN * 8], s_W2[BN * 8];  // W' tiles, 128 rows x 128 B
 // codes, 16 B per lane (256-byte aligned: the dX decode's product tables
@@ -80,7 +83,6 @@ __shared__ uint4 s_W0[BN * 8], s_W1[BN * 8], s_W2[BN * 8];  // W' tiles, 128 row
 __shared__ __align__(256) uint4 s_C0[256], s_C1[256], s_C2[256];
 __shared__ uint32_t s_Q0[128], s_Q1[128], s_Q2[128];        // scale dword per entry
 __shared__ float s_S0[128], s_S1[128], s_S2[128];           // s2 per entry
-__shared__ float s_lv[16];
 
 template <int S> QL_DEV uint4 *sX() { return S == 0 ? s_X0 : S == 1 ? s_X1 : s_X2; }
 template <int S> QL_DEV uint4 *sW() { return S == 0 ? s_W0 : S == 1 ? s_W1 : s_W2; }
@@ -369,8 +371,10 @@ struct Tile {
       float f[8];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        f[2 * b] = *(const float *)(lvb + __builtin_amdgcn_ubfe(ev4, 8 * b, 8));
-        f[2 * b + 1] = *(const float *)(lvb + __builtin_amdgcn_ubfe(od4, 8 * b, 8));
+        // byte b of ev4 / od4 zero-extended by one byte permute (the level
+        // table is at LDS address 0, so this is the whole address)
+        f[2 * b] = *(const float *)(lvb + __builtin_amdgcn_perm(0u, ev4, 0x0C0C0C00u | (uint32_t)b));
+        f[2 * b + 1] = *(const float *)(lvb + __builtin_amdgcn_perm(0u, od4, 0x0C0C0C00u | (uint32_t)b));
       }
       const float a = di.a[0];
       uint4 o;
