@@ -218,16 +218,21 @@ struct Tile {
       tr = (kg & 15) >> 2;
       const int tm = kg & 3;
       tqsh = 8 * (int)(((uint32_t)tr * (uint32_t)(g.k >> 6) + (uint32_t)(dcol >> 6)) & 3u);
-      // table (row j, block b) holds bf16(level[c] * a'(j, b)) at byte 2c of
-      // the 32 bytes at 64 j + 32 b: the bytes of row j's codes of block b,
-      // read by the same wave before it overwrites them
-      toff = (4 * jg + tr) * 64 + bsel * 32 + 8 * tm;
+      // table (patch row i, block b) holds bf16(level[c] * a') at byte 2c of
+      // 32-byte slot (2i + b + 2 (jg % 2)) % 8 of the 256-byte window of rows
+      // 4jg..4jg+3, i.e. over codes of those rows, which the same wave reads
+      // before it overwrites them; the rotation by jg puts the four tables
+      // one lookup instruction of a wave reads (two windows, two blocks) on
+      // four different groups of 8 LDS banks
+      const int rot = 2 * (jg & 1);
+      toff = 256 * jg + ((2 * tr + bsel + rot) & 7) * 32 + 8 * tm;
       twin = 256 * jg;
 #pragma unroll
       for (int x = 0; x < 4; ++x) tlv[x] = __uint_as_float(c_levels_g[4 * tm + x]);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const uint32_t ra = (uint32_t)(4 * h2 + bsel) * 32u, rb = (uint32_t)(4 * h2 + 2 + bsel) * 32u;
+        const uint32_t ra = (uint32_t)((4 * h2 + bsel + rot) & 7) * 32u;
+        const uint32_t rb = (uint32_t)((4 * h2 + 2 + bsel + rot) & 7) * 32u;
         roff[h2] = ra | (ra << 8) | (rb << 16) | (rb << 24);
       }
     }
