@@ -519,6 +519,54 @@ qlora_status qlora_adamw_step(float *param, float *exp_avg, float *exp_avg_sq,
                       (uint16_t *)dv[4], n, s, (hipStream_t)stream);
 }
 
+// Memory kind of p: device memory, page-locked host memory, or neither.
+enum class MemKind { Other, Device, PinnedHost };
+static MemKind mem_kind(const void *p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return MemKind::Other;
+  }
+  if (a.type == hipMemoryTypeDevice) return MemKind::Device;
+  if (a.type == hipMemoryTypeHost) return MemKind::PinnedHost;
+  return MemKind::Other;
+}
+
+// nbuf copies of n float32 between device memory and page-locked host
+// memory, enqueued on the stream after every pointer has been checked.
+static qlora_status adamw_page(float *const *dst, const float *const *src, int32_t nbuf,
+                               int64_t n, bool to_host, void *stream) {
+  if (!dst || !src || nbuf < 1 || nbuf > 3 || n < 1 || n > (INT64_MAX >> 2))
+    return QLORA_ERR_INVALID_ARG;
+  const MemKind want_dst = to_host ? MemKind::PinnedHost : MemKind::Device;
+  const MemKind want_src = to_host ? MemKind::Device : MemKind::PinnedHost;
+  for (int i = 0; i < nbuf; ++i) {
+    if (!dst[i] || !src[i] || !aligned16(dst[i]) || !aligned16(src[i]))
+      return QLORA_ERR_INVALID_ARG;
+    if (mem_kind(dst[i]) != want_dst || mem_kind(src[i]) != want_src)
+      return QLORA_ERR_INVALID_ARG;
+  }
+  const hipMemcpyKind kind = to_host ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
+  for (int i = 0; i < nbuf; ++i) {
+    if (hipMemcpyAsync(dst[i], src[i], (size_t)n * sizeof(float), kind,
+                       (hipStream_t)stream) != hipSuccess) {
+      (void)hipGetLastError();
+      return QLORA_ERR_HIP;
+    }
+  }
+  return QLORA_OK;
+}
+
+qlora_status qlora_adamw_page_out(float *const *host, const float *const *dev, int32_t nbuf,
+                                  int64_t n, void *stream) {
+  return adamw_page(host, dev, nbuf, n, true, stream);
+}
+
+qlora_status qlora_adamw_page_in(float *const *dev, const float *const *host, int32_t nbuf,
+                                 int64_t n, void *stream) {
+  return adamw_page(dev, host, nbuf, n, false, stream);
+}
+
 }  // extern "C"
 
 int ql_num_cus() {

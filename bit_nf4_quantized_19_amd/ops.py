@@ -79,6 +79,8 @@ SIGNATURES = {
                                           ctypes.POINTER(ctypes.c_float)]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qlora_adamw_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
+    "qlora_adamw_page_out": (ctypes.c_int, [_vp, _vp, _i32, _i64, _vp]),
+    "qlora_adamw_page_in": (ctypes.c_int, [_vp, _vp, _i32, _i64, _vp]),
 }
 
 #: the timing build's extra symbols; mirrors include/qlora_nf4_timing.h
@@ -477,6 +479,32 @@ def adamw_step(param: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Ten
     _check(lib().qlora_adamw_step(_ptr(param), _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(grad),
                                   _ptr(param_bf16), n, ctypes.addressof(hp), int(step),
                                   _stream(stream)), "qlora_adamw_step")
+
+
+def _page(fn: str, dst, src, stream):
+    if len(dst) != len(src) or not 1 <= len(dst) <= 3:
+        raise ValueError("dst and src must list the same 1 to 3 buffers")
+    n = dst[0].numel()
+    for t in list(dst) + list(src):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+            raise ValueError(f"every buffer must be a contiguous float32 tensor of {n} elements")
+    arr = ctypes.c_void_p * len(dst)
+    d = arr(*[t.data_ptr() for t in dst])
+    s = arr(*[t.data_ptr() for t in src])
+    _check(getattr(lib(), fn)(d, s, len(dst), n, _stream(stream)), fn)
+
+
+def adamw_page_out(host, dev, stream=None):
+    """Enqueue copies of the optimiser state ``dev`` (CUDA float32 tensors:
+    param, exp_avg, exp_avg_sq or a subset) into the page-locked host
+    tensors ``host`` on the stream."""
+    _page("qlora_adamw_page_out", host, dev, stream)
+
+
+def adamw_page_in(dev, host, stream=None):
+    """Enqueue copies of the paged-out state ``host`` (page-locked float32
+    tensors) back into the CUDA tensors ``dev`` on the stream."""
+    _page("qlora_adamw_page_in", dev, host, stream)
 
 
 def profile_begin(cap: int = 4096, kernels=None):

@@ -294,6 +294,34 @@ QLORA_API qlora_status qlora_adamw_step(float *param, float *exp_avg, float *exp
                               const qlora_adamw_hparams *hp, int64_t step, void *stream);
 
 /*
+ * Paging of the AdamW state (Day-25 notes 3.4: the optimiser state moves to
+ * CPU RAM when device memory runs short and back when it is needed; QLoRA
+ * glossary, "QLoRA 的工作原理", paged-optimiser bullet).
+ *
+ * qlora_adamw_page_out: for i = 0..nbuf-1, copy n float32 elements from the
+ * device buffer dev[i] to the page-locked host buffer host[i].
+ * qlora_adamw_page_in: the same copies from host[i] back to dev[i].
+ * The buffers are typically param, exp_avg and exp_avg_sq of one LoRA
+ * matrix (1 <= nbuf <= 3). The copies are enqueued on `stream` without
+ * synchronising; a qlora_adamw_step enqueued later on the same stream sees
+ * the moved state, and after page_out the caller may reuse or free dev[i]
+ * once the stream has passed the copy. Between page_out and page_in the
+ * step can also run on the host buffers directly (qlora_adamw_step accepts
+ * page-locked state). Values are copied bit for bit.
+ * dev[i]: device memory; host[i]: page-locked host memory (hipHostMalloc,
+ * torch pin_memory); every pointer 16-byte aligned and holding n floats;
+ * n >= 1. A pointer of the wrong kind (pageable host memory, a device
+ * pointer where a host one is expected), a NULL or a misaligned pointer
+ * returns QLORA_ERR_INVALID_ARG with nothing enqueued; a failed copy
+ * enqueue returns QLORA_ERR_HIP (copies of earlier buffers may already be
+ * enqueued).
+ */
+QLORA_API qlora_status qlora_adamw_page_out(float *const *host, const float *const *dev,
+                                            int32_t nbuf, int64_t n, void *stream);
+QLORA_API qlora_status qlora_adamw_page_in(float *const *dev, const float *const *host,
+                                           int32_t nbuf, int64_t n, void *stream);
+
+/*
  * LoftQ initialisation (LLM-train tutorial ch. 3, jwzheng96.github.io,
  * section 3.10: factor the gap between the 16-bit weight and its 4-bit base
  * into the LoRA branch, alternating an SVD with the quantisation).

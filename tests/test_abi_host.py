@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
     ops = _ops()
     L = ops.lib()
     names = _declared_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for name in names:
         assert hasattr(L, name), name
         assert name in ops.SIGNATURES, name
@@ -234,6 +234,19 @@ adam("adam_beta1_one", hp=HP(2e-4, 1.0, 0.999, 1e-8, 0.0))
 adam("adam_neg_lr", hp=HP(-1e-3, 0.9, 0.999, 1e-8, 0.0))
 adam("adam_nan_eps", hp=HP(2e-4, 0.9, 0.999, float("nan"), 0.0))
 adam("adam_unknown_pointer")   # not memory the device can reach: refused
+PA = ctypes.c_void_p * 3
+def page(name, fn, nbuf=3, n=64, dst=(P, P, P), src=(P, P, P), null_list=False):
+    d = None if null_list else PA(*dst)
+    out[name] = getattr(L, fn)(d, PA(*src), nbuf, n, None)
+for fn in ("qlora_adamw_page_out", "qlora_adamw_page_in"):
+    tag = fn.rsplit("_", 1)[-1]
+    page(f"page_{tag}_null_list", fn, null_list=True)
+    page(f"page_{tag}_nbuf0", fn, nbuf=0)
+    page(f"page_{tag}_nbuf4", fn, nbuf=4)
+    page(f"page_{tag}_n0", fn, n=0)
+    page(f"page_{tag}_null_buf", fn, dst=(P, None, P))
+    page(f"page_{tag}_misaligned", fn, src=(P, P, P + 4))
+    page(f"page_{tag}_unknown_pointer", fn)   # neither device nor page-locked memory
 print(repr(out))
 """
 
@@ -251,6 +264,8 @@ EXPECTED = {
     "codebook_null": -1, "adam_null_param": -1, "adam_null_grad": -1, "adam_n0": -1,
     "adam_step0": -1, "adam_misaligned_m": -1, "adam_misaligned_out": -1,
     "adam_beta1_one": -1, "adam_neg_lr": -1, "adam_nan_eps": -1, "adam_unknown_pointer": -1,
+    **{f"page_{t}_{c}": -1 for t in ("out", "in")
+       for c in ("null_list", "nbuf0", "nbuf4", "n0", "null_buf", "misaligned", "unknown_pointer")},
 }
 
 

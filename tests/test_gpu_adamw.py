@@ -117,3 +117,47 @@ def test_step_after_backward_on_the_lora_matrices(ops):
         moved = np.abs(tp.cpu().numpy() - p32)
         nz = g != 0
         assert np.all(moved[nz] > 0.5 * HP["lr"]) and np.all(moved[nz] < 1.5 * HP["lr"] + 1e-3 * np.abs(p32[nz]))
+
+
+def test_library_paging_out_and_back_is_bit_exact(ops):
+    # steps 1-2 on the device; the library pages the state out to page-locked
+    # host memory, the device copies are overwritten, step 3 runs on the
+    # host copies, the library pages them back in, step 4 runs on the
+    # device: every bit equals four steps of the oracle
+    n = 4096 * 5 + 12
+    print(f"[adamw] library paging n={n}", flush=True)
+    p, m, v = _state(n, 21)
+    dev = [_f32(x, "device") for x in (p, m, v)]
+    host = [torch.empty(n, dtype=torch.float32).pin_memory() for _ in range(3)]
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    grads = [_grad(n, 70 + s) for s in range(4)]
+    want = (p, m, v)
+    for s in range(4):
+        if s == 2:
+            ops.adamw_page_out(host, dev)
+            for t in dev:
+                t.fill_(float("nan"))   # stream-ordered after the copies
+            ops.adamw_step(*host, to_dev(grads[s]), out, s + 1, **HP)
+            ops.adamw_page_in(dev, host)
+        else:
+            ops.adamw_step(*dev, to_dev(grads[s]), out, s + 1, **HP)
+        *want, ob = oadam.adamw_step(*want, grads[s], step=s + 1, **HP)
+    torch.cuda.synchronize()
+    for got, w in zip(dev, want):
+        assert _bits_equal(got.cpu().numpy(), w)
+    assert np.array_equal(to_host_bits(out), ob)
+
+
+def test_library_paging_refuses_the_wrong_memory_kind(ops):
+    n = 1024
+    dev = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(2)]
+    pinned = [torch.zeros(n, dtype=torch.float32).pin_memory() for _ in range(2)]
+    pageable = [torch.zeros(n, dtype=torch.float32) for _ in range(2)]
+    with pytest.raises(ops.QLoRAError):
+        ops.adamw_page_out(pageable, dev)        # pageable host destination
+    with pytest.raises(ops.QLoRAError):
+        ops.adamw_page_out(dev, dev)             # device memory as the host side
+    with pytest.raises(ops.QLoRAError):
+        ops.adamw_page_in(pinned, pinned)        # host memory as the device side
+    ops.adamw_page_out(pinned, dev)
+    torch.cuda.synchronize()
