@@ -98,7 +98,8 @@ QL_DEV T pick4(int i, T a0, T a1, T a2, T a3) {
   return i == 0 ? a0 : i == 1 ? a1 : i == 2 ? a2 : a3;
 }
 #define QL_PICK(arr, i, f) pick4(i, arr[0].f, arr[1].f, arr[2].f, arr[3].f)
-QL_DEV GemvW wsel(const GemvArgs &g, int i) {
+template <class Args>
+QL_DEV GemvW wsel(const Args &g, int i) {
   GemvW W;
   W.codes = QL_PICK(g.w, i, codes);
   W.sc.absmax = QL_PICK(g.w, i, sc.absmax);
@@ -121,7 +122,8 @@ QL_DEV GemvW wsel(const GemvArgs &g, int i) {
   W.dp.mask = nullptr;
   return W;
 }
-QL_DEV int weight_of(const GemvArgs &g, int64_t rg) {
+template <class Args>
+QL_DEV int weight_of(const Args &g, int64_t rg) {
   int i = 0;
 #pragma unroll
   for (int j = 1; j < GMAXW; ++j) i += (j < g.nw && rg >= g.w[j].gbase) ? 1 : 0;
@@ -474,6 +476,263 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
   if (hwg) lora_down_partial<GRP>(g, slice, nblk, wave, n, q, hp);
 }
 
+// ---- few-token forward on VALU (M <= VMAXM, no adapter-input dropout) ----
+// Same partial sums as above, organised for one or two tokens, where the
+// 16x16x32 MFMA would run with 15 of 16 rows zero and every X operand would
+// be an LDS read. A slice is 2048 columns: lane l owns columns 32 l .. 32 l
+// + 31 (16 code bytes, half of block l / 2), keeps those X values in
+// registers for every row it visits, and per code byte reads the pair of
+// bf16 levels from the byte table (32 copies, as above) and adds both
+// products with one v_dot2_f32_bf16 per token. The 32-weight partial is
+// scaled by the block's a' once. A workgroup serves one slice: its threads
+// load the slice of X once and pass it through LDS; each wave takes VR
+// rows, and the per-row sums of its lanes are added by a butterfly that
+// hands each lane group one (row, token) sum in a fixed order. The byte
+// table is built first (it waits on nothing), then every load of a wave (X,
+// block scales, the VR rows' code words) is issued before the barrier, so
+// the whole record is requested at the start and each row is decoded as it
+// arrives. H = X A^T partials come from one more workgroup per slice and
+// weight (ranks 2w, 2w + 1 of each 16 for wave w). Both go to the epilogue
+// kernel below (one H partial per slice).
+// Measured call times (graph replay, 16 rotated weights, us) against the
+// MFMA kernel above at M = 1: 13.9 / 14.3 (11008x4096) and 14.8 / 15.9
+// (4096x11008). With a decode-free copy of this kernel the call takes
+// ~12.6: the read of the record in this shape (plus the epilogue launch,
+// ~3.5) sets the time, not the decode. Sixteen rows per wave (half the
+// waves) measured 19.8 / 20.0; each wave reading its own X slice from L2
+// instead of through LDS, 14.4 / 14.8.
+constexpr int VW = 8;          // waves per workgroup
+constexpr int VCOL = 2048;     // columns per slice (64 lanes x 32)
+constexpr int VR = 8;          // weight rows per wave
+constexpr int VMAXM = 2;       // tokens served by this path
+
+struct VArgs {
+  GemvW w[GMAXW];   // gbase counts groups of VR rows
+  int nw;
+  int64_t k;
+  const uint16_t *X;
+  int64_t M;
+  int64_t nunits;   // row groups of all weights x slices
+  int S;            // slices
+  int nrow_wg;      // workgroups of row units; the H workgroups follow
+  float *part;      // [S][M][dtot]
+  int64_t dtot;
+  int rp;
+};
+
+// Sum v[i] over the 64 lanes of a wave for every i, in a fixed order: each
+// butterfly step hands half of the entries to the lane partner that keeps
+// them, so after the steps lane l holds the sum of entry l >> (6 - log2 N)
+// in its return value (all lanes of a group of 64 / N hold the same bits).
+template <int N>
+QL_DEV float wave_transpose_sum(float (&v)[N], int lane) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N: power of two up to 64");
+#pragma unroll
+  for (int st = 0; st < 6; ++st) {
+    const int mask = 32 >> st;
+    const int half = N >> (st + 1);
+    const bool up = (lane & mask) != 0;
+    if (half >= 1) {
+#pragma unroll
+      for (int i = 0; i < half; ++i) {
+        const float send = up ? v[i] : v[i + half];
+        const float keep = up ? v[i + half] : v[i];
+        v[i] = keep + __shfl_xor(send, mask);
+      }
+    } else {
+      v[0] += __shfl_xor(v[0], mask);
+    }
+  }
+  return v[0];
+}
+
+// X[m][col0 .. col0 + 31] of tokens m < MV as 16 bf16 pairs (token rows past
+// M and lanes past k read clamped addresses; their sums are never stored or
+// are zeroed)
+template <int MV>
+QL_DEV void valu_load_x(const VArgs &g, int64_t colc, uint32_t (&xw)[MV][16]) {
+#pragma unroll
+  for (int m = 0; m < MV; ++m) {
+    const int64_t mr = m < g.M ? m : 0;
+    const uint4 *src = (const uint4 *)(g.X + mr * g.k + colc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = src[i];
+      xw[m][4 * i] = v.x;
+      xw[m][4 * i + 1] = v.y;
+      xw[m][4 * i + 2] = v.z;
+      xw[m][4 * i + 3] = v.w;
+    }
+  }
+}
+
+QL_DEV float dot2bf(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// H partials of one slice of one weight: wave w takes ranks 16 c + 2 w, +1
+// for every chunk c of 16 ranks.
+template <int MV, bool GRP>
+QL_DEV void valu_lora_down(const VArgs &g, int hidx, int wave, int lane) {
+  const int wi = hidx / g.S, slice = hidx % g.S;
+  const GemvW W = GRP ? wsel(g, wi) : g.w[0];
+  const int64_t col0 = (int64_t)slice * VCOL + 32 * lane;
+  const bool lok = col0 < g.k;
+  const int64_t colc = lok ? col0 : 0;
+  uint32_t xw[MV][16];
+  valu_load_x<MV>(g, colc, xw);
+  for (int cb = 0; cb < g.rp / 16; ++cb) {
+    float v[2 * MV];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = 16 * cb + 2 * wave + tt;
+      const uint4 *src = (const uint4 *)(W.Ap + (int64_t)t * g.k + colc);
+      uint32_t aw[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 a = src[i];
+        aw[4 * i] = a.x;
+        aw[4 * i + 1] = a.y;
+        aw[4 * i + 2] = a.z;
+        aw[4 * i + 3] = a.w;
+      }
+#pragma unroll
+      for (int m = 0; m < MV; ++m) {
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+          p0 = dot2bf(aw[j], xw[m][j], p0);
+          p1 = dot2bf(aw[j + 1], xw[m][j + 1], p1);
+        }
+        v[tt * MV + m] = lok ? p0 + p1 : 0.f;
+      }
+    }
+    const float sum = wave_transpose_sum<2 * MV>(v, lane);
+    const int idx = lane >> (6 - (MV == 1 ? 1 : 2));
+    const int tt = idx / MV, m = idx % MV;
+    if ((lane & (64 / (2 * MV) - 1)) == 0 && m < g.M)
+      W.hpart[((int64_t)slice * g.M + m) * g.rp + 16 * cb + 2 * wave + tt] = sum;
+  }
+}
+
+template <bool DQ, int MV, bool GRP>
+__global__ __launch_bounds__(64 * VW) void nf4_gemv_valu_kernel(VArgs g) {
+  __shared__ __align__(16) unsigned char lut[256 * 256];
+  __shared__ __align__(16) uint4 xs[MV][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if ((int)blockIdx.x >= g.nrow_wg) {   // uniform per workgroup
+    valu_lora_down<MV, GRP>(g, (int)blockIdx.x - g.nrow_wg, wave, lane);
+    return;
+  }
+  // workgroup b: slice b % S, row groups (b / S) VW + wave (clamped; the
+  // waves past the last row group write nothing)
+  const int slice = (int)(blockIdx.x % g.S);
+  const int64_t ngroups = g.nunits / g.S;
+  const int64_t rg = ((int64_t)blockIdx.x / g.S) * VW + wave;
+  const int64_t rgc = rg < ngroups ? rg : ngroups - 1;
+  const GemvW W = GRP ? wsel(g, weight_of(g, rgc)) : g.w[0];
+  const int64_t row0 = (rgc - W.gbase) * VR;
+  const int64_t nbr = g.k >> 6;
+  const int64_t col0 = (int64_t)slice * VCOL + 32 * lane;
+  const bool lok = col0 < g.k;
+  const int64_t colc = lok ? col0 : 0;
+  // 1. byte table: entry e = (level[e >> 4], level[e & 15]) as a bf16 pair
+  //    (even element low), 32 copies in bytes 0-127 of row e; built first,
+  //    as it waits on no memory
+  {
+    const int te = tid & 255;
+    uint32_t lv_hi = c_levels_v[0], lv_lo = c_levels_v[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      const uint32_t v = c_levels_v[i];
+      lv_hi = (te >> 4) == i ? v : lv_hi;
+      lv_lo = (te & 15) == i ? v : lv_lo;
+    }
+    const uint32_t v = ql::pack_bf16x2(__uint_as_float(lv_hi), __uint_as_float(lv_lo));
+    const uint4 v4 = make_uint4(v, v, v, v);
+    unsigned char *t = lut + te * 256 + 64 * (tid >> 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(uint4 *)(t + 16 * i) = v4;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // 2. loads, in the order they are needed: the slice of X (8 columns per
+  //    thread, clamped past k), then per row the block-scale inputs and the
+  //    lane's code word
+  uint4 xv[MV];
+  {
+    const int64_t xc = (int64_t)slice * VCOL + 8 * (tid & 255);
+#pragma unroll
+    for (int m = 0; m < MV; ++m)
+      xv[m] = *(const uint4 *)(g.X + (m < g.M ? m : 0) * g.k + (xc < g.k ? xc : 0));
+  }
+  const float mu = DQ ? W.sc.mu[0] : 0.0f;
+  uint4 cw[VR];
+  float sa[VR], sb[VR];
+#pragma unroll
+  for (int r = 0; r < VR; ++r) {
+    const int64_t row = min(row0 + r, W.d - 1);
+    const int64_t blk = row * nbr + (colc >> 6);
+    if (DQ) {
+      sa[r] = (float)W.sc.q[blk];
+      sb[r] = W.sc.s2[blk >> 8];
+    } else {
+      sa[r] = W.sc.absmax[blk];
+      sb[r] = 0.0f;
+    }
+    cw[r] = *(const uint4 *)(W.codes + row * (g.k >> 1) + (colc >> 1));
+  }
+  // 3. X through LDS: waits for the X loads only (issued first), then each
+  //    lane takes its 32 columns into registers
+  if (tid < 256) {
+#pragma unroll
+    for (int m = 0; m < MV; ++m) xs[m][tid] = xv[m];
+  }
+  __syncthreads();
+  uint32_t xw[MV][16];
+#pragma unroll
+  for (int m = 0; m < MV; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = xs[m][4 * lane + i];
+      xw[m][4 * i] = v.x;
+      xw[m][4 * i + 1] = v.y;
+      xw[m][4 * i + 2] = v.z;
+      xw[m][4 * i + 3] = v.w;
+    }
+  // 4. rows in load order: 16 table reads and 16 MV dot products per lane
+  const uint32_t lcopy = 4u * (uint32_t)(lane & 31);
+  float acc[VR * MV];
+#pragma unroll
+  for (int r = 0; r < VR; ++r) {
+    const uint32_t cws[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
+    float p0[MV], p1[MV];
+#pragma unroll
+    for (int m = 0; m < MV; ++m) p0[m] = p1[m] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t lv = *(const uint32_t *)(lut + __builtin_amdgcn_perm(
+                                                       cws[j >> 2], lcopy, 0x0C0C0400u + ((j & 3) << 8)));
+#pragma unroll
+      for (int m = 0; m < MV; ++m) {
+        if (j & 1) p1[m] = dot2bf(lv, xw[m][j], p1[m]);
+        else p0[m] = dot2bf(lv, xw[m][j], p0[m]);
+      }
+    }
+    const float ap = DQ ? sa[r] * sb[r] + mu : sa[r];
+#pragma unroll
+    for (int m = 0; m < MV; ++m) acc[r * MV + m] = lok ? ap * (p0[m] + p1[m]) : 0.f;
+  }
+  // 5. per (row, token) sums over the lanes; lane group idx writes entry idx
+  constexpr int N = VR * MV;
+  const float sum = wave_transpose_sum<N>(acc, lane);
+  constexpr int LG = N == 8 ? 3 : N == 16 ? 2 : N == 32 ? 1 : 0;   // log2(64 / N)
+  const int idx = lane >> LG;
+  const int r = idx / MV, m = idx % MV;
+  if (rg < ngroups && (lane & ((1 << LG) - 1)) == 0 && m < g.M && row0 + r < W.d)
+    g.part[((int64_t)slice * g.M + m) * g.dtot + W.rbase + row0 + r] = sum;
+}
+
 // Y[m][j] = bf16(sum_s part[s][m][j] + s_l * sum_t H[m][t] B[j][t]) with
 // H[m][t] = sum_p hpart[p][m][t] (fixed orders), per weight of the call;
 // workgroup (x, m) serves 256 columns of one weight and builds its H[m] in
@@ -567,12 +826,90 @@ size_t gemv_part_bytes(int64_t dtot, int64_t k, int64_t M, int rp, int nw) {
   return (size_t)(gemv_splits(k) * M * dtot * 4 + nw * gemv_splits(k) * GW * M * rp * 4);
 }
 
+// The VALU path for M <= VMAXM without adapter-input dropout: S = k / 2048
+// slices (the last may be ragged), one H partial per slice and weight; its
+// partial sums fit in the workspace sized for the MFMA path (fewer slices,
+// fewer H partials).
+static qlora_status launch_gemv_valu(int nw, const GemvIn *in, int64_t k, const uint16_t *X,
+                                     int64_t M, int r, int rp, float s, float *part,
+                                     hipStream_t st) {
+  const int64_t S = ql_cdiv(k, VCOL);
+  int64_t dtot = 0, ngroups = 0, eblocks = 0;
+  VArgs g{};
+  EpiArgs e{};
+  for (int i = 0; i < nw; ++i) {
+    const int64_t d = in[i].d;
+    g.w[i] = GemvW{in[i].codes, in[i].sc, d, d * (k >> 6), ngroups, dtot, in[i].Ap, nullptr,
+                   in[i].dp};
+    e.w[i] = EpiW{in[i].Bp, nullptr, in[i].Y, in[i].H_save, d, dtot, eblocks, 1.0f};
+    ngroups += ql_cdiv(d, VR);
+    eblocks += ql_cdiv(d, 256);
+    dtot += d;
+  }
+  for (int i = 0; i < nw; ++i) {
+    float *hpart = part + S * M * dtot + (int64_t)i * S * M * rp;
+    g.w[i].hpart = hpart;
+    e.w[i].hpart = hpart;
+  }
+  for (int i = nw; i < GMAXW; ++i) {  // unused slots: never selected
+    g.w[i] = g.w[0];
+    e.w[i] = e.w[0];
+  }
+  const int64_t nunits = ngroups * S;
+  const int64_t nrow_wg = ql_cdiv(ngroups, VW) * S;
+  if (nrow_wg + nw * S > 0x7fffffff || eblocks > 0x7fffffff) return QLORA_ERR_UNSUPPORTED;
+  g.nw = nw;
+  g.k = k;
+  g.X = X;
+  g.M = M;
+  g.nunits = nunits;
+  g.S = (int)S;
+  g.nrow_wg = (int)nrow_wg;
+  g.part = part;
+  g.dtot = dtot;
+  g.rp = rp;
+  {
+    QlProf prof(QLORA_K_GEMV, st);
+    const unsigned grid = (unsigned)(nrow_wg + nw * S);
+#define QL_VGEMV(DQV, MVV)                                                  \
+  if (nw > 1)                                                               \
+    nf4_gemv_valu_kernel<DQV, MVV, true><<<grid, 64 * VW, 0, st>>>(g);      \
+  else                                                                      \
+    nf4_gemv_valu_kernel<DQV, MVV, false><<<grid, 64 * VW, 0, st>>>(g);
+    if (in[0].sc.dq) {
+      if (M == 1) { QL_VGEMV(true, 1) } else { QL_VGEMV(true, 2) }
+    } else {
+      if (M == 1) { QL_VGEMV(false, 1) } else { QL_VGEMV(false, 2) }
+    }
+#undef QL_VGEMV
+  }
+  {
+    e.nw = nw;
+    e.part = part;
+    e.S = (int)S;
+    e.M = M;
+    e.dtot = dtot;
+    e.nhp = (int)S;
+    e.rp = rp;
+    e.r = r;
+    e.s = s;
+    QlProf prof(QLORA_K_GEMV_EPILOGUE, st);
+    dim3 eg((unsigned)eblocks, (unsigned)M);
+    gemv_epilogue_kernel<<<eg, 256, 0, st>>>(e);
+  }
+  QL_LAUNCH_CHECK();
+  return QLORA_OK;
+}
+
 qlora_status launch_gemv_fwd(int nw, const GemvIn *in, int64_t k, const uint16_t *X, int64_t M,
                              int r, int rp, float s, float *part, hipStream_t st) {
   if (M < 1 || M > 16 || rp < 16 || rp > 128 || rp % 16) return QLORA_ERR_INVALID_ARG;
   if (nw < 1 || nw > GMAXW) return QLORA_ERR_INVALID_ARG;
   for (int i = 1; i < nw; ++i)
     if (in[i].sc.dq != in[0].sc.dq) return QLORA_ERR_INVALID_ARG;
+  bool drop = false;
+  for (int i = 0; i < nw; ++i) drop = drop || in[i].dp.on;
+  if (M <= VMAXM && !drop) return launch_gemv_valu(nw, in, k, X, M, r, rp, s, part, st);
   const int ncu = ql_num_cus();
   const int64_t S = gemv_splits(k);
   int64_t dtot = 0, ngroups = 0, eblocks = 0;

@@ -129,6 +129,23 @@ def test_gemv_slices(ops, d, k, M, dq):
     _assert_close(g, o, ["Y"])
 
 
+# ---- one or two tokens: the VALU decode path --------------------------------
+# 2048-column slices (lane l owns 32 columns), 8 rows per wave, H partials
+# per slice in workgroups of their own, a butterfly per (row, token) sum
+@pytest.mark.parametrize("d,k,M,r,dq", [
+    (64, 64, 1, 16, True),        # one block per row: two active lanes of one slice
+    (104, 2112, 2, 16, False),    # a full slice + one block, 13 row groups
+    (8, 4096, 1, 5, True),        # padded ranks, a single row group, two slices
+    (48, 11008, 2, 64, True),     # five full slices + 768 columns, four rank chunks
+    (16, 2048, 1, 128, False),    # r = 128, exactly one slice
+    (200, 960, 2, 3, True),       # one ragged slice, odd r
+])
+def test_gemv_valu_path(ops, d, k, M, r, dq):
+    g, o = _case(ops, d, k, M, r, 2.0 * r, dq, seed=d + k + M + r, bwd=False)
+    _assert_close(g, o, ["Y"])
+    assert rel_frob(g["H"], o["H"]) < 1e-5
+
+
 # ---- config 3: decode-shaped GEMV, fwd only ---------------------------------
 _GEMV_CACHE = {}
 
