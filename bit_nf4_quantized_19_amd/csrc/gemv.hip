@@ -495,12 +495,14 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
 // weight (ranks 2w, 2w + 1 of each 16 for wave w). Both go to the epilogue
 // kernel below (one H partial per slice).
 // Measured call times (graph replay, 16 rotated weights, us) against the
-// MFMA kernel above at M = 1: 13.9 / 14.3 (11008x4096) and 14.8 / 15.9
-// (4096x11008). With a decode-free copy of this kernel the call takes
-// ~12.6: the read of the record in this shape (plus the epilogue launch,
-// ~3.5) sets the time, not the decode. Sixteen rows per wave (half the
-// waves) measured 19.8 / 20.0; each wave reading its own X slice from L2
-// instead of through LDS, 14.4 / 14.8.
+// MFMA kernel above at M = 1: 13.3 / 14.5 (11008x4096) and 14.1 / 16.0
+// (4096x11008). A decode-free copy of an earlier form of this kernel took
+// ~12.6 per call: the read of the record in this shape (plus the epilogue
+// launch, ~3.5) sets the time more than the decode does. Measured and not
+// kept: sixteen rows per wave (half the waves) 19.8 / 20.0; each wave
+// reading its own X slice from L2 instead of through LDS, 14.4 / 14.8 (with
+// the butterfly still spilling); this path for four tokens 21.0 / 21.8
+// against 14.9 / 16.3 on MFMA (one workgroup per CU at 134 registers).
 constexpr int VW = 8;          // waves per workgroup
 constexpr int VCOL = 2048;     // columns per slice (64 lanes x 32)
 constexpr int VR = 8;          // weight rows per wave
@@ -535,8 +537,12 @@ QL_DEV float wave_transpose_sum(float (&v)[N], int lane) {
     if (half >= 1) {
 #pragma unroll
       for (int i = 0; i < half; ++i) {
-        const float send = up ? v[i] : v[i + half];
-        const float keep = up ? v[i + half] : v[i];
+        // the pair as opaque register values: otherwise the lane-dependent
+        // selects become an indexed access to a scratch copy of v
+        float lo = v[i], hi = v[i + half];
+        asm("" : "+v"(lo), "+v"(hi));
+        const float send = up ? lo : hi;
+        const float keep = up ? hi : lo;
         v[i] = keep + __shfl_xor(send, mask);
       }
     } else {
@@ -609,9 +615,10 @@ QL_DEV void valu_lora_down(const VArgs &g, int hidx, int wave, int lane) {
       }
     }
     const float sum = wave_transpose_sum<2 * MV>(v, lane);
-    const int idx = lane >> (6 - (MV == 1 ? 1 : 2));
+    constexpr int LGH = MV == 1 ? 5 : MV == 2 ? 4 : 3;   // log2(64 / (2 MV))
+    const int idx = lane >> LGH;
     const int tt = idx / MV, m = idx % MV;
-    if ((lane & (64 / (2 * MV) - 1)) == 0 && m < g.M)
+    if ((lane & ((1 << LGH) - 1)) == 0 && m < g.M)
       W.hpart[((int64_t)slice * g.M + m) * g.rp + 16 * cb + 2 * wave + tt] = sum;
   }
 }
