@@ -61,6 +61,7 @@ def _snapshot(b):
 @pytest.mark.parametrize("d,k,M,r,dropout,mask", [
     (512, 768, 96, 16, 0.0, False),    # GEMM path
     (1024, 1088, 4, 16, 0.0, False),   # GEMV path
+    (1024, 2112, 1, 16, 0.0, False),   # GEMV path for one token (VALU)
     (512, 768, 96, 16, 0.1, False),    # with dropout (bits redrawn in the backward)
     (512, 768, 96, 16, 0.1, True)])    # with dropout, bits stored by the forward
 def test_graph_replays_match_eager(ops, d, k, M, r, dropout, mask):
