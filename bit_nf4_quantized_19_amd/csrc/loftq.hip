@@ -16,8 +16,9 @@
 //   mul_left   Z_part = R[chunk, :]^T Y[chunk, :] (fp32 MFMA 16x16x4, split over d)
 //   reduce_gram  sum of the split partials in a fixed order, with the
 //              float64 partial Gram matrices Y^T Y of 256-row chunks
-//   orth_apply CholeskyQR: every workgroup factors the summed Gram matrix in
-//              one wave (float64, registers) and applies L^{-T} to its rows,
+//   orth_apply CholeskyQR: every workgroup sums the partial Gram matrices
+//              (all threads, one entry each), factors the sum in one wave
+//              (float64, registers) and applies L^{-T} to its rows,
 //              optionally with the partial Gram matrices of its output (run
 //              twice per orthonormalisation: CholeskyQR2)
 //   eig        one wave: Jacobi (round-robin, float64) on (Q^T R)(Q^T R)^T
@@ -25,6 +26,8 @@
 //   apply      row-wise product with a p x p matrix (bf16 A^T / B)
 //   residual_f32, residual_bf16, pad: elementwise.
 // Every kernel is deterministic (fixed summation orders, no atomics).
+
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -249,8 +252,11 @@ __global__ __launch_bounds__(256) void mul_left_kernel(const float *__restrict__
 // Partial Gram matrix of the rows staged in ys (rows x P, zero past n):
 // g[a][c] = sum_i ys[i][a] ys[i][c] in float64, written to gout.
 // rows is a multiple of 4; four partial sums over rows i % 4, added in order.
-template <int P>
-QL_DEV void gram_rows(const float (*ys)[P], int rows, double *gout) {
+// T is the staging type: float, or the same values already widened to
+// double (one conversion per element instead of two per product; the
+// products and sums are the same).
+template <int P, class T>
+QL_DEV void gram_rows(const T (*ys)[P], int rows, double *gout) {
   for (int e = threadIdx.x; e < P * P; e += 256) {
     const int a = e / P, c = e % P;
     double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
@@ -265,12 +271,14 @@ QL_DEV void gram_rows(const float (*ys)[P], int rows, double *gout) {
 }
 
 // Y (n x P) = sum over s < ns of part[s] (in order), and the partial Gram
-// matrix of each 256-row chunk (gout[block], float64).
+// matrix of each 256-row chunk (gout[block], float64). The chunk is staged in
+// LDS as double for P = 16 (32 KB), as float for wider P.
 template <int P>
 __global__ __launch_bounds__(256) void reduce_gram_kernel(const float *__restrict__ part, int ns,
                                                           int64_t n, float *__restrict__ Y,
                                                           double *__restrict__ gout) {
-  __shared__ float ys[kGramRows][P];
+  using T = typename std::conditional<P == 16, double, float>::type;
+  __shared__ T ys[kGramRows][P];
   const int64_t r0 = (int64_t)blockIdx.x * kGramRows;
   const int64_t n4 = n * P / 4;
   for (int e = threadIdx.x; e < kGramRows * P / 4; e += 256) {
@@ -279,14 +287,15 @@ __global__ __launch_bounds__(256) void reduce_gram_kernel(const float *__restric
     f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
     if (r0 + row < n) {
       v = ((const f32x4 *)part)[g];
-#pragma unroll 8
+#pragma unroll 16
       for (int s = 1; s < ns; ++s) v += ((const f32x4 *)part)[(int64_t)s * n4 + g];
       ((f32x4 *)Y)[g] = v;
     }
-    *(f32x4 *)&ys[row][4 * c4] = v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ys[row][4 * c4 + i] = (T)v[i];
   }
   __syncthreads();
-  gram_rows<P>(ys, kGramRows, gout + (int64_t)blockIdx.x * P * P);
+  gram_rows<P, T>(ys, kGramRows, gout + (int64_t)blockIdx.x * P * P);
 }
 
 // 1/sqrt(x) for x > 0: the hardware estimate refined by two Newton steps
@@ -305,26 +314,29 @@ QL_DEV double bcast(double x, int l) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// One wave (all 64 lanes active): G = sum of nch partial Gram matrices
-// (float64), G = L L^T by columns with lane i holding row i of L in
-// registers (other rows by readlane); a pivot not above 1e-12 of its diagonal
-// entry marks a dependent column, whose L column is zero (its Q column comes
-// out zero). Lane j then computes column j of L^{-1}; Ms = L^{-T} (fp32), so
-// that Q = Y Ms has orthonormal columns.
+// Every thread of the workgroup: G = sum of the nch partial Gram matrices
+// (float64, in partial order), entry e summed by thread e % 256, into Gs.
 template <int P>
-QL_DEV void chol_wave(const double *__restrict__ gin, int nch, float (*Ms)[P]) {
+QL_DEV void gram_sum(const double *__restrict__ gin, int nch, double (*Gs)[P]) {
+  for (int e = threadIdx.x; e < P * P; e += 256) {
+    double sum = 0.0;
+#pragma unroll 16
+    for (int b = 0; b < nch; ++b) sum += gin[(int64_t)b * P * P + e];
+    Gs[e / P][e % P] = sum;
+  }
+}
+
+// One wave (all 64 lanes active), after gram_sum: G = L L^T by columns with
+// lane i holding row i of L in registers (other rows by readlane); a pivot
+// not above 1e-12 of its diagonal entry marks a dependent column, whose L
+// column is zero (its Q column comes out zero). Lane j then computes column
+// j of L^{-1}; Ms = L^{-T} (fp32), so that Q = Y Ms has orthonormal columns.
+template <int P>
+QL_DEV void chol_wave(const double (*Gs)[P], float (*Ms)[P]) {
   const int lane = threadIdx.x & 63;
   double L[P];
 #pragma unroll
-  for (int c = 0; c < P; ++c) L[c] = 0.0;
-  constexpr int kUB = P <= 16 ? 4 : (P <= 32 ? 2 : 1);   // partial matrices per load batch
-  if (lane < P)
-#pragma unroll kUB
-    for (int b = 0; b < nch; ++b) {
-      const double *g = gin + (int64_t)b * P * P + lane * P;
-#pragma unroll
-      for (int c = 0; c < P; ++c) L[c] += g[c];
-    }
+  for (int c = 0; c < P; ++c) L[c] = lane < P ? Gs[lane][c] : 0.0;
   // L[c] holds G[lane][c] until column c is computed; ri[j] = 1 / L[j][j]
   // (0 for a dependent column)
   double ri[P];
@@ -354,7 +366,8 @@ QL_DEV void chol_wave(const double *__restrict__ gin, int nch, float (*Ms)[P]) {
 }
 
 // Q = Y L^{-T} with L from the partial Gram matrices gin (each workgroup
-// recomputes the P x P factor in its first wave); with GRAM the partial Gram
+// sums them with all its threads and factors the P x P result in its first
+// wave); with GRAM the partial Gram
 // matrix of the workgroup's output rows goes to gout[block]. A thread owns
 // one row and one 16-column block; a workgroup orth_rows(NB) rows (a multiple
 // of 4 with rows x NB <= 256; the other threads only take part in the
@@ -368,8 +381,11 @@ __global__ __launch_bounds__(256) void orth_apply_kernel(const float *__restrict
   constexpr int NB = P / 16, RPB = orth_rows(NB);
   static_assert(RPB % 4 == 0 && RPB * NB <= 256, "rows per workgroup");
   __shared__ float Ms[P][P];
-  __shared__ float ys[GRAM ? RPB : 1][P];
-  if (threadIdx.x < 64) chol_wave<P>(gin, nch, Ms);
+  __shared__ double Gs[P][P];
+  __shared__ double ys[GRAM ? RPB : 1][P];
+  gram_sum<P>(gin, nch, Gs);
+  __syncthreads();
+  if (threadIdx.x < 64) chol_wave<P>(Gs, Ms);
   __syncthreads();
   const int lr = threadIdx.x / NB, cb = threadIdx.x % NB;
   const bool own = lr < RPB;
@@ -399,9 +415,9 @@ __global__ __launch_bounds__(256) void orth_apply_kernel(const float *__restrict
   if (GRAM) {
     if (own)
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) ys[lr][cb * 16 + jj] = o[jj];
+      for (int jj = 0; jj < 16; ++jj) ys[lr][cb * 16 + jj] = (double)o[jj];
     __syncthreads();
-    gram_rows<P>(ys, RPB, gout + (int64_t)blockIdx.x * P * P);
+    gram_rows<P, double>(ys, RPB, gout + (int64_t)blockIdx.x * P * P);
   }
 }
 
