@@ -1,4 +1,8 @@
-// Memory-bound NF4 forward for few tokens (M <= 16), gfx950.
+// Memory-bound NF4 forward for few tokens (M <= 16), gfx950. Two kernels
+// produce the same float32 partial sums: the MFMA kernel below (3 to 16
+// tokens, or any count with adapter-input dropout) and a VALU kernel for one
+// or two tokens (section "few-token forward on VALU" further down); one
+// epilogue kernel finishes both.
 //
 // Same layer as the fused GEMM (QLoRA glossary, Ultralytics, "QLoRA 的工作原理",
 // forward paragraph): Y = X W'^T + s H B^T. With M <= 16 the time is the HBM
