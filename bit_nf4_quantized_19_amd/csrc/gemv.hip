@@ -495,9 +495,9 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
 // table is built first (it waits on nothing), then every load of a wave (X,
 // block scales, the VR rows' code words) is issued before the barrier, so
 // the whole record is requested at the start and each row is decoded as it
-// arrives. H = X A^T partials come from one more workgroup per slice and
-// weight (ranks 2w, 2w + 1 of each 16 for wave w). Both go to the epilogue
-// kernel below (one H partial per slice).
+// arrives. H = X A^T partials come from one more workgroup per slice, weight
+// and 16 ranks (ranks 2w, 2w + 1 of the 16 for wave w). Both go to the
+// epilogue kernel below (one H partial per slice).
 // Measured call times (graph replay, 16 rotated weights, us) against the
 // MFMA kernel above at M = 1: 13.3 / 14.5 (11008x4096) and 14.1 / 16.0
 // (4096x11008). A decode-free copy of an earlier form of this kernel took
@@ -581,50 +581,50 @@ QL_DEV float dot2bf(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// H partials of one slice of one weight: wave w takes ranks 16 c + 2 w, +1
-// for every chunk c of 16 ranks.
+// H partials of one slice of one weight for one chunk of 16 ranks (one
+// workgroup per weight, slice and chunk): wave w takes ranks 16 cb + 2 w, +1.
 template <int MV, bool GRP>
 QL_DEV void valu_lora_down(const VArgs &g, int hidx, int wave, int lane) {
-  const int wi = hidx / g.S, slice = hidx % g.S;
+  const int nrc = g.rp / 16;
+  const int cb = hidx % nrc, ws = hidx / nrc;
+  const int wi = ws / g.S, slice = ws % g.S;
   const GemvW W = GRP ? wsel(g, wi) : g.w[0];
   const int64_t col0 = (int64_t)slice * VCOL + 32 * lane;
   const bool lok = col0 < g.k;
   const int64_t colc = lok ? col0 : 0;
   uint32_t xw[MV][16];
   valu_load_x<MV>(g, colc, xw);
-  for (int cb = 0; cb < g.rp / 16; ++cb) {
-    float v[2 * MV];
+  float v[2 * MV];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int t = 16 * cb + 2 * wave + tt;
-      const uint4 *src = (const uint4 *)(W.Ap + (int64_t)t * g.k + colc);
-      uint32_t aw[16];
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = 16 * cb + 2 * wave + tt;
+    const uint4 *src = (const uint4 *)(W.Ap + (int64_t)t * g.k + colc);
+    uint32_t aw[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 a = src[i];
-        aw[4 * i] = a.x;
-        aw[4 * i + 1] = a.y;
-        aw[4 * i + 2] = a.z;
-        aw[4 * i + 3] = a.w;
-      }
-#pragma unroll
-      for (int m = 0; m < MV; ++m) {
-        float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-          p0 = dot2bf(aw[j], xw[m][j], p0);
-          p1 = dot2bf(aw[j + 1], xw[m][j + 1], p1);
-        }
-        v[tt * MV + m] = lok ? p0 + p1 : 0.f;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const uint4 a = src[i];
+      aw[4 * i] = a.x;
+      aw[4 * i + 1] = a.y;
+      aw[4 * i + 2] = a.z;
+      aw[4 * i + 3] = a.w;
     }
-    const float sum = wave_transpose_sum<2 * MV>(v, lane);
-    constexpr int LGH = MV == 1 ? 5 : MV == 2 ? 4 : 3;   // log2(64 / (2 MV))
-    const int idx = lane >> LGH;
-    const int tt = idx / MV, m = idx % MV;
-    if ((lane & ((1 << LGH) - 1)) == 0 && m < g.M)
-      W.hpart[((int64_t)slice * g.M + m) * g.rp + 16 * cb + 2 * wave + tt] = sum;
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        p0 = dot2bf(aw[j], xw[m][j], p0);
+        p1 = dot2bf(aw[j + 1], xw[m][j + 1], p1);
+      }
+      v[tt * MV + m] = lok ? p0 + p1 : 0.f;
+    }
   }
+  const float sum = wave_transpose_sum<2 * MV>(v, lane);
+  constexpr int LGH = MV == 1 ? 5 : MV == 2 ? 4 : 3;   // log2(64 / (2 MV))
+  const int idx = lane >> LGH;
+  const int tt = idx / MV, m = idx % MV;
+  if ((lane & ((1 << LGH) - 1)) == 0 && m < g.M)
+    W.hpart[((int64_t)slice * g.M + m) * g.rp + 16 * cb + 2 * wave + tt] = sum;
 }
 
 template <bool DQ, int MV, bool GRP>
@@ -868,7 +868,8 @@ static qlora_status launch_gemv_valu(int nw, const GemvIn *in, int64_t k, const 
   }
   const int64_t nunits = ngroups * S;
   const int64_t nrow_wg = ql_cdiv(ngroups, VW) * S;
-  if (nrow_wg + nw * S > 0x7fffffff || eblocks > 0x7fffffff) return QLORA_ERR_UNSUPPORTED;
+  const int64_t nh_wg = nw * S * (rp / 16);   // H: one workgroup per weight, slice, 16 ranks
+  if (nrow_wg + nh_wg > 0x7fffffff || eblocks > 0x7fffffff) return QLORA_ERR_UNSUPPORTED;
   g.nw = nw;
   g.k = k;
   g.X = X;
@@ -881,7 +882,7 @@ static qlora_status launch_gemv_valu(int nw, const GemvIn *in, int64_t k, const 
   g.rp = rp;
   {
     QlProf prof(QLORA_K_GEMV, st);
-    const unsigned grid = (unsigned)(nrow_wg + nw * S);
+    const unsigned grid = (unsigned)(nrow_wg + nh_wg);
 #define QL_VGEMV(DQV, MVV)                                                  \
   if (nw > 1)                                                               \
     nf4_gemv_valu_kernel<DQV, MVV, true><<<grid, 64 * VW, 0, st>>>(g);      \
