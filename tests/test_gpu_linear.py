@@ -203,3 +203,16 @@ def test_linear_is_deterministic(ops):
     b = _run(ops, inp, True, 32.0)
     for key in ("Y", "dX", "dA", "dB", "H"):
         assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 16])
+def test_decode_forward_is_deterministic(ops, M):
+    # both decode kernels (VALU for one or two tokens, MFMA above) and the
+    # epilogue sum their partials in fixed orders: repeated calls give the
+    # same bits, at the down-projection shape (six slices, one ragged)
+    print(f"[gemv determinism] M={M}", flush=True)
+    inp = synth.linear_inputs(4096, 11008, M, 16, idx=12, with_dy=False)
+    a = _run(ops, inp, True, 32.0, bwd=False)
+    b = _run(ops, inp, True, 32.0, bwd=False, w_dev=a["w"])
+    for key in ("Y", "H"):
+        assert np.array_equal(a[key], b[key]), key
