@@ -499,10 +499,12 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
 // and 16 ranks (ranks 2w, 2w + 1 of the 16 for wave w). Both go to the
 // epilogue kernel below (one H partial per slice).
 // Measured call times (graph replay, 16 rotated weights, us) against the
-// MFMA kernel above at M = 1: 13.3 / 14.5 (11008x4096) and 14.1 / 16.0
-// (4096x11008). A decode-free copy of an earlier form of this kernel took
-// ~12.6 per call: the read of the record in this shape (plus the epilogue
-// launch, ~3.5) sets the time more than the decode does. Measured and not
+// MFMA kernel above at M = 1: 12.9 / 14.3 (11008x4096) and 14.0 / 16.4
+// (4096x11008). The int8 block codes as one dword per lane (below) instead
+// of a byte load per row took 0.5 us off each; with no block-scale loads at
+// all (a timing copy) the call took 12.5 / 13.2 before that change, so the
+// read of the record in this shape (plus the epilogue launch, ~3.5) sets
+// the time more than the decode or the scales do. Measured and not
 // kept: sixteen rows per wave (half the waves) 19.8 / 20.0; each wave
 // reading its own X slice from L2 instead of through LDS, 14.4 / 14.8 (with
 // the butterfly still spilling); this path for four tokens 21.0 / 21.8
@@ -627,7 +629,12 @@ QL_DEV void valu_lora_down(const VArgs &g, int hidx, int wave, int lane) {
     W.hpart[((int64_t)slice * g.M + m) * g.rp + 16 * cb + 2 * wave + tt] = sum;
 }
 
-template <bool DQ, int MV, bool GRP>
+// QA (double quantisation with k % 256 == 0, so every row's int8 codes start
+// 4-byte aligned): one dword load per lane brings the codes of all VR rows'
+// slice blocks (lane l: row l / 8, blocks 4 (l % 8) .. + 3), handed to the
+// lanes that need them by one shuffle per row; otherwise one byte load per
+// row and lane.
+template <bool DQ, int MV, bool GRP, bool QA>
 __global__ __launch_bounds__(64 * VW) void nf4_gemv_valu_kernel(VArgs g) {
   __shared__ __align__(16) unsigned char lut[256 * 256];
   __shared__ __align__(16) uint4 xs[MV][256];
@@ -678,6 +685,13 @@ __global__ __launch_bounds__(64 * VW) void nf4_gemv_valu_kernel(VArgs g) {
       xv[m] = *(const uint4 *)(g.X + (m < g.M ? m : 0) * g.k + (xc < g.k ? xc : 0));
   }
   const float mu = DQ ? W.sc.mu[0] : 0.0f;
+  static_assert(!QA || VR == 8, "one dword load per lane covers 8 rows");
+  uint32_t qd = 0;
+  if (DQ && QA) {   // clamped to the last row and the row's last 4 blocks
+    const int64_t rq = min(row0 + (lane >> 3), W.d - 1);
+    const int64_t off = min((int64_t)slice * (VCOL / 64) + 4 * (lane & 7), nbr - 4);
+    qd = *(const uint32_t *)(W.sc.q + rq * nbr + off);
+  }
   uint4 cw[VR];
   float sa[VR], sb[VR];
 #pragma unroll
@@ -685,7 +699,7 @@ __global__ __launch_bounds__(64 * VW) void nf4_gemv_valu_kernel(VArgs g) {
     const int64_t row = min(row0 + r, W.d - 1);
     const int64_t blk = row * nbr + (colc >> 6);
     if (DQ) {
-      sa[r] = (float)W.sc.q[blk];
+      sa[r] = QA ? 0.0f : (float)W.sc.q[blk];
       sb[r] = W.sc.s2[blk >> 8];
     } else {
       sa[r] = W.sc.absmax[blk];
@@ -729,6 +743,10 @@ __global__ __launch_bounds__(64 * VW) void nf4_gemv_valu_kernel(VArgs g) {
         if (j & 1) p1[m] = dot2bf(lv, xw[m][j], p1[m]);
         else p0[m] = dot2bf(lv, xw[m][j], p0[m]);
       }
+    }
+    if (DQ && QA) {   // this lane's block code of row r, from lane 8 r + l / 8
+      const uint32_t w = (uint32_t)__shfl((int)qd, 8 * r + (lane >> 3));
+      sa[r] = (float)(int8_t)(w >> (8 * ((lane >> 1) & 3)));
     }
     const float ap = DQ ? sa[r] * sb[r] + mu : sa[r];
 #pragma unroll
@@ -883,15 +901,18 @@ static qlora_status launch_gemv_valu(int nw, const GemvIn *in, int64_t k, const 
   {
     QlProf prof(QLORA_K_GEMV, st);
     const unsigned grid = (unsigned)(nrow_wg + nh_wg);
-#define QL_VGEMV(DQV, MVV)                                                  \
-  if (nw > 1)                                                               \
-    nf4_gemv_valu_kernel<DQV, MVV, true><<<grid, 64 * VW, 0, st>>>(g);      \
-  else                                                                      \
-    nf4_gemv_valu_kernel<DQV, MVV, false><<<grid, 64 * VW, 0, st>>>(g);
-    if (in[0].sc.dq) {
-      if (M == 1) { QL_VGEMV(true, 1) } else { QL_VGEMV(true, 2) }
+#define QL_VGEMV(DQV, MVV, QAV)                                                  \
+  if (nw > 1)                                                                    \
+    nf4_gemv_valu_kernel<DQV, MVV, true, QAV><<<grid, 64 * VW, 0, st>>>(g);      \
+  else                                                                           \
+    nf4_gemv_valu_kernel<DQV, MVV, false, QAV><<<grid, 64 * VW, 0, st>>>(g);
+    const bool qa = (k % 256) == 0;
+    if (in[0].sc.dq && qa) {
+      if (M == 1) { QL_VGEMV(true, 1, true) } else { QL_VGEMV(true, 2, true) }
+    } else if (in[0].sc.dq) {
+      if (M == 1) { QL_VGEMV(true, 1, false) } else { QL_VGEMV(true, 2, false) }
     } else {
-      if (M == 1) { QL_VGEMV(false, 1) } else { QL_VGEMV(false, 2) }
+      if (M == 1) { QL_VGEMV(false, 1, false) } else { QL_VGEMV(false, 2, false) }
     }
 #undef QL_VGEMV
   }

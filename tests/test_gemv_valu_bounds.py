@@ -7,7 +7,9 @@ This model restates the kernel's work split (row workgroups: slice b % S, row
 groups (b / S) * 8 + wave, 8 rows per wave, lane l on columns 32 l .. 32 l + 31
 of a 2048-column slice; H workgroups: one per weight, slice and 16 ranks) and
 its butterfly's writer lanes, and checks for grouped and ragged shapes that
-  - every X, code, int8-scale, s2 and A read lies inside its buffer,
+  - every X, code, int8-scale, s2 and A read lies inside its buffer (the
+    int8 codes as one aligned dword per lane when k % 256 == 0, and each
+    lane's block inside the dword its shuffle reads),
   - every slice partial (slice, token, output column) and every H partial
     (weight, slice, token, rank) is written exactly once,
   - the partials fit in the workspace the forward sizes for the GEMV path.
@@ -89,6 +91,17 @@ def _check(ds, k, M, rp):
             lok = col0 < k
             colc = np.where(lok, col0, 0)
             nb = d * k // 64
+            if k % 256 == 0:   # aligned int8 codes: one dword per lane for the 8 rows
+                rq = np.minimum(row0 + (lane >> 3), d - 1)
+                off = np.minimum(slice_ * (VCOL // 64) + 4 * (lane & 7), nbr - 4)
+                qa = rq * nbr + off
+                assert qa.min() >= 0 and (qa + 4).max() <= nb and (qa % 4 == 0).all(), "int8 dword read"
+                # each valid lane's block lies in the dword of lane 8 r + l / 8
+                src_off = slice_ * (VCOL // 64) + 4 * (lane >> 3)
+                blk_in_slice = slice_ * (VCOL // 64) + (lane >> 1)
+                ok = lok
+                assert (src_off[ok] <= blk_in_slice[ok]).all() and (blk_in_slice[ok] < src_off[ok] + 4).all()
+                assert (src_off[ok] + 4 <= nbr).all(), "a valid lane's dword was clamped"
             for r in range(VR):
                 row = min(row0 + r, d - 1)
                 blk = row * nbr + (colc >> 6)

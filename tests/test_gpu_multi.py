@@ -27,6 +27,7 @@ CASES = [
     # (d list, k, M, r, dq)
     ([704, 704], 1088, 1, 16, True),          # gate/up shaped, ragged slice
     ([192, 320, 64], 2112, 2, 16, False),     # two tokens (VALU path), three sizes
+    ([256, 512], 4096, 1, 16, True),           # one token, aligned int8 codes (dword loads)
     ([512, 256, 768], 2112, 4, 16, True),      # q/k/v-like, three sizes
     ([1024, 1024, 1024, 1024], 1024, 16, 16, False),  # four weights, absmax path
     ([200, 320], 576, 7, 5, True),             # padded ranks, ragged row groups
