@@ -146,7 +146,7 @@ QL_DEV constexpr uint32_t xa_imm(int c, int s) {
 // Registers of one work unit (16 rows x one slice) of a wave.
 struct GUnit {
   uint4 cw[4][2];   // lane (n, q): blocks 4c + q of row n, 32 bytes each
-  uint32_t qw[5];   // int8 scale codes of the row's slice (aligned dwords)
+  uint32_t qw[5];   // int8 scale codes of the row's slice (aligned dwords; QA: qw[0] only)
   float araw[4];    // absmax of blocks 4c + q (no double quantisation)
   float s2lo, s2hi;
   float mu;         // the weight's DQ mean
@@ -157,7 +157,10 @@ struct GUnit {
   const uint8_t *crow;   // the lane's row codes of this slice
 };
 
-template <bool DQ, bool FULL, bool GRP>
+// QA: k % 256 == 0, so a row's slice codes start 4-byte aligned and lane
+// (n, q) loads just the dword of blocks 4q .. 4q + 3 of its row; the lane
+// that needs block 4c + q takes it from lane (n, c) by a shuffle.
+template <bool DQ, bool FULL, bool GRP, bool QA>
 QL_DEV void unit_load(const GemvArgs &g, GUnit &u, int64_t rg, int64_t b0, int nblk, int n,
                       int q) {
   const int64_t nbr = g.k >> 6;
@@ -176,8 +179,12 @@ QL_DEV void unit_load(const GemvArgs &g, GUnit &u, int64_t rg, int64_t b0, int n
     // array has a multiple of 8 bytes, so a clamped dword index stays in it)
     const uint32_t *qp = (const uint32_t *)W.sc.q;
     const int64_t w0 = u.blk0 >> 2, wlast = (W.nb >> 2) - 1;
+    if (QA) {
+      u.qw[0] = qp[min(w0 + q, wlast)];
+    } else {
 #pragma unroll
-    for (int j = 0; j < 5; ++j) u.qw[j] = qp[min(w0 + j, wlast)];
+      for (int j = 0; j < 5; ++j) u.qw[j] = qp[min(w0 + j, wlast)];
+    }
   } else {
     u.mu = 0.0f;
 #pragma unroll
@@ -199,7 +206,7 @@ QL_DEV void unit_codes(GUnit &u, int c, int nblk, int q) {
 // MFMA steps of NU units of a wave (same slice, so they share the A
 // operand reads; their independent chains interleave). D[4q + t][n] = partial
 // sum of block 4c + q for token 4tp + t. Writes the units' partial sums.
-template <bool DQ, int TP, int NU, class Issue>
+template <bool DQ, int TP, int NU, bool QA, class Issue>
 QL_DEV void unit_compute(const GemvArgs &g, const GUnit *const (&us)[NU],
                          const unsigned char *smem, const uint32_t (&abase)[TP], uint32_t lcopy,
                          int n, int q, int64_t slice, Issue issue) {
@@ -245,7 +252,8 @@ QL_DEV void unit_compute(const GemvArgs &g, const GUnit *const (&us)[NU],
       if (DQ) {
         const float s2 = ((u.blk0 + 4 * c + q) >> 8) == (u.blk0 >> 8) ? u.s2lo : u.s2hi;
         const uint32_t win =
-            __builtin_amdgcn_alignbyte(u.qw[c + 1], u.qw[c], (uint32_t)(u.blk0 & 3));
+            QA ? (uint32_t)__shfl((int)u.qw[0], n + 16 * c)
+               : __builtin_amdgcn_alignbyte(u.qw[c + 1], u.qw[c], (uint32_t)(u.blk0 & 3));
         const int qv = (int)(int8_t)(win >> (8 * q));
         ap = (float)qv * s2 + u.mu;
       } else {
@@ -355,7 +363,7 @@ QL_DEV void lora_down_partial(const GemvArgs &g, int64_t slice, int nblk, int wa
 // of them) of one slice; wave w takes the workgroup's row groups w and
 // w + GW, both loaded before the table is built, then computed together. The
 // table and the X slice are built once per workgroup.
-template <bool DQ, int TP, bool FULL, bool GRP>
+template <bool DQ, int TP, bool FULL, bool GRP, bool QA>
 __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
   __shared__ __align__(16) unsigned char smem[LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -401,8 +409,8 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
   const bool has_a = wave < g.rpw && rga < g.ngroups;
   const bool has_b = wave + GW < g.rpw && rgb < g.ngroups;
   GUnit ua, ub;
-  unit_load<DQ, FULL, GRP>(g, ua, min(rga, g.ngroups - 1), b0, nblk, n, q);
-  unit_load<DQ, FULL, GRP>(g, ub, min(rgb, g.ngroups - 1), b0, nblk, n, q);
+  unit_load<DQ, FULL, GRP, QA>(g, ua, min(rga, g.ngroups - 1), b0, nblk, n, q);
+  unit_load<DQ, FULL, GRP, QA>(g, ub, min(rgb, g.ngroups - 1), b0, nblk, n, q);
   // codes chunk by chunk, both units' chunk c before chunk c + 1: the
   // compute of chunk c waits only for the loads up to it. Only the first
   // GPRE chunks go out before the table is built: once the memory queues are
@@ -459,10 +467,10 @@ __global__ __launch_bounds__(GT) void nf4_gemv_kernel(GemvArgs g) {
   for (int tp = 0; tp < TP; ++tp) abase[tp] = a_on ? xa_base(tp, q, n & 3) : ZBASE;
   if (has_b) {  // has_b implies has_a
     const GUnit *const both[2] = {&ua, &ub};
-    unit_compute<DQ, TP, 2>(g, both, smem, abase, lcopy, n, q, slice, issue);
+    unit_compute<DQ, TP, 2, QA>(g, both, smem, abase, lcopy, n, q, slice, issue);
   } else if (has_a) {
     const GUnit *const one[1] = {&ua};
-    unit_compute<DQ, TP, 1>(g, one, smem, abase, lcopy, n, q, slice, issue);
+    unit_compute<DQ, TP, 1, QA>(g, one, smem, abase, lcopy, n, q, slice, issue);
   } else {
 #pragma unroll
     for (int c = 0; c < 4; ++c) issue(c);   // every code register gets its (clamped) load
@@ -989,11 +997,17 @@ qlora_status launch_gemv_fwd(int nw, const GemvIn *in, int64_t k, const uint16_t
     const int tp = (int)ql_cdiv(M, 4);
     // every slice is full when k is a multiple of 1024
     const bool full = (k % (64 * GB)) == 0;
-#define QL_GEMV4(DQV, TPV, FV)                                          \
+#define QL_GEMV5(DQV, TPV, FV, QAV)                                     \
   if (nw > 1)                                                           \
-    nf4_gemv_kernel<DQV, TPV, FV, true><<<grid, GT, 0, st>>>(g);        \
+    nf4_gemv_kernel<DQV, TPV, FV, true, QAV><<<grid, GT, 0, st>>>(g);   \
   else                                                                  \
-    nf4_gemv_kernel<DQV, TPV, FV, false><<<grid, GT, 0, st>>>(g);
+    nf4_gemv_kernel<DQV, TPV, FV, false, QAV><<<grid, GT, 0, st>>>(g);
+#define QL_GEMV4(DQV, TPV, FV)                                          \
+  if (DQV && (k % 256) == 0) {                                          \
+    QL_GEMV5(DQV, TPV, FV, DQV)                                         \
+  } else {                                                              \
+    QL_GEMV5(DQV, TPV, FV, false)                                       \
+  }
 #define QL_GEMV3(DQV, TPV)                                              \
   if (full) {                                                           \
     QL_GEMV4(DQV, TPV, true)                                            \
@@ -1010,6 +1024,7 @@ qlora_status launch_gemv_fwd(int nw, const GemvIn *in, int64_t k, const uint16_t
 #undef QL_GEMV
 #undef QL_GEMV3
 #undef QL_GEMV4
+#undef QL_GEMV5
   }
   {
     e.nw = nw;
