@@ -45,7 +45,11 @@ struct MergeArgs {
   uint16_t *Wm;
 };
 
-template <bool DQ, int NCH>
+// MQ (double quantisation with k % 128 == 0): the tile's two 64-column
+// blocks of a row have adjacent int8 codes at an even index (c0 / 64 is
+// even), read as one 2-byte load, and share one s2 (an even block index is
+// never the last of its 256-block group).
+template <bool DQ, int NCH, bool MQ>
 __global__ __launch_bounds__(MT) void merge_kernel(MergeArgs g) {
   constexpr int RP = 16 * NCH;            // padded rank
   constexpr int PITCH = 2 * RP + 16;      // bytes per A^T column
@@ -86,14 +90,23 @@ __global__ __launch_bounds__(MT) void merge_kernel(MergeArgs g) {
   // block scales: 32-column block b lies in 64-column block (c0 + 32 b) / 64
   float sa[MNB / 2], sb[MNB / 2];
   const int64_t nbr = g.k >> 6;
+  if (DQ && MQ) {
+    static_assert(MNB / 2 == 2, "two 64-column blocks per tile");
+    const int64_t blk = jc * nbr + min(c0 / 64, nbr - 2);
+    const uint32_t q2 = *(const uint16_t *)(g.sc.q + blk);
+    sa[0] = (float)(int8_t)(q2 & 0xFFu);
+    sa[1] = (float)(int8_t)(q2 >> 8);
+    sb[0] = sb[1] = g.sc.s2[blk >> 8];
+  } else {
 #pragma unroll
-  for (int b2 = 0; b2 < MNB / 2; ++b2) {
-    const int64_t blk = jc * nbr + min(c0 / 64 + b2, nbr - 1);
-    if (DQ) {
-      sa[b2] = (float)g.sc.q[blk];
-      sb[b2] = g.sc.s2[blk >> 8];
-    } else {
-      sa[b2] = g.sc.absmax[blk];
+    for (int b2 = 0; b2 < MNB / 2; ++b2) {
+      const int64_t blk = jc * nbr + min(c0 / 64 + b2, nbr - 1);
+      if (DQ) {
+        sa[b2] = (float)g.sc.q[blk];
+        sb[b2] = g.sc.s2[blk >> 8];
+      } else {
+        sa[b2] = g.sc.absmax[blk];
+      }
     }
   }
   const float mu = DQ ? g.sc.mu[0] : 0.0f;
@@ -201,10 +214,13 @@ qlora_status launch_merge(const uint8_t *codes, ql::ScaleSrc sc, int64_t d, int6
   dim3 grid((unsigned)gx, (unsigned)gy);
   QlProf prof(QLORA_K_MERGE, st);
 #define QL_MERGE(NCHV)                                                 \
-  if (sc.dq)                                                           \
-    merge_kernel<true, NCHV><<<grid, MT, 0, st>>>(g);                  \
+  if (sc.dq && mq)                                                     \
+    merge_kernel<true, NCHV, true><<<grid, MT, 0, st>>>(g);            \
+  else if (sc.dq)                                                      \
+    merge_kernel<true, NCHV, false><<<grid, MT, 0, st>>>(g);           \
   else                                                                 \
-    merge_kernel<false, NCHV><<<grid, MT, 0, st>>>(g);
+    merge_kernel<false, NCHV, false><<<grid, MT, 0, st>>>(g);
+  const bool mq = (k % 128) == 0;
   switch (nch) {
     case 1: QL_MERGE(1) break;
     case 2: QL_MERGE(2) break;

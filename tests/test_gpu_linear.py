@@ -176,6 +176,7 @@ def test_config3_gemv(ops, d, k, M):
                                             (256, 256, 8, 16.0, False),
                                             (200, 320, 3, 6.0, True),
                                             (40, 704, 40, 16.0, True),   # 3 rank chunks, ragged tiles
+                                            (136, 640, 24, 48.0, True),  # paired int8 loads (k % 128 == 0), ragged rows
                                             (8, 64, 128, 64.0, False)])  # r = 128, one block
 def test_merge(ops, d, k, r, alpha, dq):
     inp = synth.linear_inputs(d, k, 1, r, idx=3, with_dy=False)
