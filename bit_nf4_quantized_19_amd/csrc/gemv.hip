@@ -822,17 +822,34 @@ __global__ __launch_bounds__(256) void gemv_epilogue_kernel(EpiArgs e) {
   const int64_t j = xb * 256 + tid;
   const int64_t jc = j < W.d ? j : W.d - 1;
   const uint4 b0 = *(const uint4 *)(W.Bp + jc * rp), b1 = *(const uint4 *)(W.Bp + jc * rp + 8);
+  // eight slices' loads in flight (clamped slice index), then their sums in
+  // slice order: a loop unrolled over a run-time count would leave its tail
+  // as one load and wait per slice
   float acc = 0.0f;
-#pragma unroll 4
-  for (int sp = 0; sp < e.S; ++sp) acc += e.part[((int64_t)sp * e.M + m) * e.dtot + W.rbase + jc];
+  for (int s0 = 0; s0 < e.S; s0 += 8) {
+    float pv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      pv[u] = e.part[((int64_t)min(s0 + u, e.S - 1) * e.M + m) * e.dtot + W.rbase + jc];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < e.S) acc += pv[u];
+  }
   // H[m][t]: lane group grp adds partials p = grp, grp + ng, ... of rank t
   // (ng = 256 / rp groups), then rank t adds the groups in order
   {
     const int ng = 256 / rp, t = tid % rp, grp = tid / rp;
     if (grp < ng) {
       float ha = 0.0f;
-#pragma unroll 4
-      for (int p = grp; p < e.nhp; p += ng) ha += W.hpart[((int64_t)p * e.M + m) * rp + t];
+      for (int p0 = grp; p0 < e.nhp; p0 += 4 * ng) {   // four partials' loads, then their sums
+        float hv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          hv[u] = W.hpart[((int64_t)min(p0 + u * ng, e.nhp - 1) * e.M + m) * rp + t];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (p0 + u * ng < e.nhp) ha += hv[u];
+      }
       hp[grp][t] = ha;
     }
     __syncthreads();

@@ -287,8 +287,17 @@ __global__ __launch_bounds__(256) void reduce_gram_kernel(const float *__restric
     f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
     if (r0 + row < n) {
       v = ((const f32x4 *)part)[g];
-#pragma unroll 16
-      for (int s = 1; s < ns; ++s) v += ((const f32x4 *)part)[(int64_t)s * n4 + g];
+      // eight splits' loads in flight (clamped split index), then their sums
+      // in split order
+      for (int s0 = 1; s0 < ns; s0 += 8) {
+        f32x4 t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          t[u] = ((const f32x4 *)part)[(int64_t)min(s0 + u, ns - 1) * n4 + g];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < ns) v += t[u];
+      }
       ((f32x4 *)Y)[g] = v;
     }
 #pragma unroll
@@ -320,8 +329,15 @@ template <int P>
 QL_DEV void gram_sum(const double *__restrict__ gin, int nch, double (*Gs)[P]) {
   for (int e = threadIdx.x; e < P * P; e += 256) {
     double sum = 0.0;
-#pragma unroll 16
-    for (int b = 0; b < nch; ++b) sum += gin[(int64_t)b * P * P + e];
+    // eight partials' loads in flight (clamped index), then their sums in order
+    for (int b0 = 0; b0 < nch; b0 += 8) {
+      double t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = gin[(int64_t)min(b0 + u, nch - 1) * P * P + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b0 + u < nch) sum += t[u];
+    }
     Gs[e / P][e % P] = sum;
   }
 }
